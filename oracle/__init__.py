@@ -1,0 +1,8 @@
+"""fp64 CPU oracle of the KV/activation transform-and-quantize path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the benchmark's CPU
+baseline leg, never by the library.  It shares no code with the HIP path.
+"""
+from .kvq_oracle import (MODES, Quantized, Spec, dequantize, expand_scales, hadamard_matrix,  # noqa: F401
+                         inverse_rotate, pack_nibbles, qmax, quantize, reconstruction_errors,
+                         rotate, score_decode, unpack_nibbles)

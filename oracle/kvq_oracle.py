@@ -1,0 +1,234 @@
+"""fp64 CPU oracle for the transform-and-quantize path (KV cache / activations).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module.  It shares no code, table or constant with the HIP
+library and imports nothing from it; both sides only read the same seeded inputs.
+
+Every step is the plain definition, in float64, in the order the pages give it:
+
+  rotation   y = (1/sqrt(n)) H_n diag(sigma) x per n-channel block, H_n the Sylvester
+             Hadamard matrix in natural order, sigma in {-1,+1}           (C1)
+  norm sep.  nu = ||y||_2, u = y / nu (NSEP modes only)                    (C2)
+  scale      per token: max_d |u| / Q ; per channel: max over a block of B
+             tokens of |u_td| / Q ; Q = 2^(b-1) - 1                        (C3)
+  codes      c = clamp(rne(u / scale), -Q, Q)                              (C4)
+  packing    two's-complement nibbles, even channel in the low nibble      (C5)
+  dequant    y^ = c * S16 * N16, then the inverse rotation                 (C6)
+  score      s[q, t] = sum_d q_d * k^_td, query head hq reads KV head hq // G (C7)
+
+Sources (page title, section):
+  * norm-separation post ("nsep+pchan" for INT4/INT3 KV caches): "the fix", its four-line
+    PyTorch snippet (L2 norm, unit direction, absmax/7, round and clamp to +-7); "root
+    cause" (per-row absmax, outlier channels); the ".norm() pitfall" (an L2 norm, not
+    L_{-1}).
+  * Rotated Runtime Smooth analysis (ICLR): "problem definition" (alpha = max|X|/(2^(N-1)-1)),
+    "master equation" and "term-by-term" (R = (1/sqrt K)[+-1], R R^T = I, s_j = column max),
+    Figure 2 (Y = (XR)(R^-1 W^T) = X W^T), "experimental design" (RTN, group size 128).
+  * NSNQuant summary: "Hadamard transform" (randomized Hadamard), "implementation details"
+    (scores computed with the stored byproducts folded in, dequantization kernel).
+  * Activation-guided compensation abstract: random signs before the Hadamard rotation.
+
+Readings where the pages are silent or garbled (each also listed in the design doc):
+  R1 rotation is orthonormal (1/sqrt n); signs first, then H; natural Sylvester order;
+     one sign vector per head shared by all tokens; block k of a wide row uses
+     sigma[k n:(k+1) n].
+  R2 "per-channel" = max over the tokens of one B-token block of one sequence; the
+     snippet's amax over the last dim is the per-token NSEP mode.
+  R3 codes use the unrounded scale and norm; stored values are fp16(nu), fp16(scale).
+  R4 rounding is half-to-even; the rounding decision is taken on the fp32 value of the
+     quotient (the precision the kernels decide in): c = rne(fp32(u / scale)).
+  R5 nu = 0 or scale = 0 give codes 0 and stored 0.
+  R6 the decode score is the plain dot product q . k^ (no 1/sqrt d, no softmax), with
+     k^ the fp64 dequantized key before any output rounding.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+MODES = ("naive", "nsep", "pchan", "nsep_pchan")
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    """Shape and method parameters; x is [seqs * tokens, heads, head_dim]."""
+    seqs: int
+    tokens: int
+    heads: int
+    head_dim: int
+    bits: int
+    mode: str
+    block_tokens: int = 0     # per-channel token block B (pchan modes)
+    hadamard: int = 0         # 0 = no rotation, else the Hadamard block size n
+
+    @property
+    def nsep(self) -> bool:
+        return self.mode in ("nsep", "nsep_pchan")
+
+    @property
+    def per_channel(self) -> bool:
+        return self.mode in ("pchan", "nsep_pchan")
+
+
+def qmax(bits: int) -> int:
+    """Q = 2^(b-1) - 1: +-7 at INT4 (the snippet's clamp), +-3 at INT3, +-1 at 2 bits."""
+    return (1 << (bits - 1)) - 1
+
+
+# ----------------------------------------------------------------------------- rotation
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix in natural order: H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(n, dtype=np.int64)
+    a = i[:, None] & i[None, :]
+    parity = np.zeros_like(a)
+    while np.any(a):
+        parity ^= a & 1
+        a >>= 1
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def rotate(x: np.ndarray, signs: np.ndarray, n: int) -> np.ndarray:
+    """y = (1/sqrt n) H_n (sigma * x) on every n-channel block of every [.., heads, D] row.
+
+    x: float64 [N, heads, D]; signs: [heads, D] of +-1.
+    """
+    N, Hh, D = x.shape
+    xs = x * signs.astype(np.float64)[None, :, :]
+    blocks = xs.reshape(N, Hh, D // n, n)
+    y = blocks @ hadamard_matrix(n).T / np.sqrt(n)
+    return y.reshape(N, Hh, D)
+
+
+def inverse_rotate(y: np.ndarray, signs: np.ndarray, n: int) -> np.ndarray:
+    """x = sigma * (1/sqrt n) H_n^T y: the transpose of `rotate` (R^-1 = R^T)."""
+    N, Hh, D = y.shape
+    blocks = y.reshape(N, Hh, D // n, n)
+    x = (blocks @ hadamard_matrix(n) / np.sqrt(n)).reshape(N, Hh, D)
+    return x * signs.astype(np.float64)[None, :, :]
+
+
+# ----------------------------------------------------------------------------- quantize
+@dataclasses.dataclass
+class Quantized:
+    codes: np.ndarray      # int8 [N, heads, D] in [-Q, Q]
+    packed: np.ndarray     # uint8 [N, heads, D/2]
+    v: np.ndarray          # float64 quotient u / scale before rounding [N, heads, D]
+    nu: np.ndarray | None  # float64 norms [N, heads] (NSEP modes)
+    scale: np.ndarray      # float64 scales: [N, heads] or [seqs * T/B, heads, D]
+    norms16: np.ndarray | None   # float16 stored norms
+    scales16: np.ndarray         # float16 stored scales
+
+
+def quantize(x: np.ndarray, spec: Spec, signs: np.ndarray | None = None) -> Quantized:
+    """Quantize x ([N, heads, D], any float dtype, widened exactly to float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    N, Hh, D = x.shape
+    assert N == spec.seqs * spec.tokens and Hh == spec.heads and D == spec.head_dim
+    Q = qmax(spec.bits)
+
+    # C1: optional randomized Hadamard rotation
+    y = rotate(x, signs, spec.hadamard) if spec.hadamard else x.copy()
+
+    # C2: norm separation -> unit direction
+    nu = None
+    if spec.nsep:
+        nu = np.sqrt(np.sum(y * y, axis=-1))
+        safe = np.where(nu > 0.0, nu, 1.0)
+        u = np.where(nu[..., None] > 0.0, y / safe[..., None], 0.0)
+    else:
+        u = y
+
+    # C3: the scale, per token or per channel over a block of B tokens
+    if spec.per_channel:
+        B = spec.block_tokens
+        nb = spec.tokens // B
+        ub = np.abs(u).reshape(spec.seqs, nb, B, Hh, D)
+        scale = (ub.max(axis=2) / Q).reshape(spec.seqs * nb, Hh, D)
+        scale_full = np.repeat(scale.reshape(spec.seqs, nb, 1, Hh, D), B, axis=2).reshape(N, Hh, D)
+    else:
+        scale = np.abs(u).max(axis=-1) / Q
+        scale_full = np.broadcast_to(scale[..., None], u.shape)
+
+    # C4: quotient, rounding decision in fp32, half-to-even, clamp
+    safe = np.where(scale_full > 0.0, scale_full, 1.0)
+    v = np.where(scale_full > 0.0, u / safe, 0.0)
+    c = np.clip(np.rint(v.astype(np.float32)), -Q, Q).astype(np.int8)
+
+    return Quantized(codes=c, packed=pack_nibbles(c), v=v, nu=nu, scale=scale,
+                     norms16=None if nu is None else nu.astype(np.float16),
+                     scales16=scale.astype(np.float16))
+
+
+# ----------------------------------------------------------------------------- packing
+def pack_nibbles(c: np.ndarray) -> np.ndarray:
+    """Two 4-bit two's-complement codes per byte; channel 2i low nibble, 2i+1 high."""
+    c = c.astype(np.int16)
+    lo = c[..., 0::2] & 0xF
+    hi = c[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles; nibbles are sign-extended."""
+    b = b.astype(np.int16)
+    nib = np.stack([b & 0xF, b >> 4], axis=-1).reshape(*b.shape[:-1], b.shape[-1] * 2)
+    return np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+
+
+# ----------------------------------------------------------------------------- dequantize
+def expand_scales(scales16: np.ndarray, spec: Spec) -> np.ndarray:
+    """Stored scales broadcast to every element [N, heads, D] as float64."""
+    s = np.asarray(scales16).astype(np.float64)
+    N, Hh, D = spec.seqs * spec.tokens, spec.heads, spec.head_dim
+    if spec.per_channel:
+        B = spec.block_tokens
+        nb = spec.tokens // B
+        return np.repeat(s.reshape(spec.seqs, nb, 1, Hh, D), B, axis=2).reshape(N, Hh, D)
+    return np.broadcast_to(s.reshape(N, Hh, 1), (N, Hh, D))
+
+
+def dequantize(packed: np.ndarray, norms16, scales16, spec: Spec,
+               signs: np.ndarray | None = None) -> np.ndarray:
+    """x^ in float64: codes * scale (* norm), then the inverse rotation.
+
+    The inputs are the stored (fp16) norms and scales, exactly widened.
+    """
+    c = unpack_nibbles(np.asarray(packed)).astype(np.float64)
+    y = c * expand_scales(scales16, spec)
+    if spec.nsep:
+        y = y * np.asarray(norms16).astype(np.float64)[..., None]
+    return inverse_rotate(y, signs, spec.hadamard) if spec.hadamard else y
+
+
+# ----------------------------------------------------------------------------- decode score
+def score_decode(q: np.ndarray, k_hat: np.ndarray, spec: Spec) -> np.ndarray:
+    """scores[s, hq, t] = sum_d q[s, hq, d] * k^[s*T + t, hq // G, d] in float64.
+
+    q: [seqs, q_heads, D]; k_hat: dequantized keys [seqs*T, heads, D] (float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    S, Hq, D = q.shape
+    G = Hq // spec.heads
+    kh = k_hat.reshape(S, spec.tokens, spec.heads, D)
+    out = np.empty((S, Hq, spec.tokens))
+    for hq in range(Hq):
+        out[:, hq, :] = np.einsum("sd,std->st", q[:, hq, :], kh[:, :, hq // G, :])
+    return out
+
+
+# ----------------------------------------------------------------------------- error report
+def reconstruction_errors(x: np.ndarray, x_hat: np.ndarray, outlier_mask: np.ndarray) -> dict:
+    """Four relative-error measures of a reconstruction (for the mode ordering check).
+
+    outlier_mask: bool [heads, D], True on the generator's outlier channels.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    err = x_hat - x
+    fro = np.linalg.norm(err) / np.linalg.norm(x)
+    tok = np.mean(np.linalg.norm(err, axis=-1) / np.maximum(np.linalg.norm(x, axis=-1), 1e-300))
+    ch = np.mean(np.linalg.norm(err, axis=0) / np.maximum(np.linalg.norm(x, axis=0), 1e-300))
+    keep = ~outlier_mask[None, :, :]
+    keep = np.broadcast_to(keep, x.shape)
+    non = np.linalg.norm(err[keep]) / np.linalg.norm(x[keep])
+    return {"frobenius": fro, "per_token": tok, "per_channel": ch, "non_outlier": non}

@@ -1,0 +1,57 @@
+"""Inputs that lie exactly on the quantization grid (closed-form expected codes).
+
+Every (token, head) vector is y = 2^p * 2^-e * k with integer codes k, sum_d k_d^2 = 4^e and
+one entry equal to +-Q.  Then nu = 2^p, u = 2^-e k, scale = 2^-e, quotient = k, all exact in
+binary floating point, so quantize must return k and dequantize must return x bit for bit.
+With a rotation of size n in {16, 64} (1/sqrt n a power of two) the input is built as
+x = sigma * H_n y / sqrt(n) using scipy's Sylvester Hadamard matrix, so the rotated vector is
+exactly y again.  This module builds test inputs only; it does not call the oracle or the
+HIP library.
+"""
+import numpy as np
+import scipy.linalg
+
+from oracle import Spec  # only the parameter record
+
+# integer patterns with sum of squares 4^e and max |k| = Q
+PATTERNS = {4: (3, [7, 3, 2, 1, 1]), 3: (2, [3, 2, 1, 1, 1]), 2: (1, [1, 1, 1, 1])}
+
+
+def make(bits, mode, hadamard, head_dim=64, seqs=2, tokens=128, heads=2, seed=0):
+    """Returns (spec, x float64 [N, H, D], signs int8 [H, D] or None, codes int8 [N, H, D])."""
+    rng = np.random.default_rng(seed)
+    D = head_dim
+    B = D if "pchan" in mode else 0            # B tokens cover every channel with a +-Q
+    spec = Spec(seqs, tokens, heads, D, bits, mode, B, hadamard)
+    e, pat = PATTERNS[bits]
+    N = seqs * tokens
+    k = np.zeros((N, heads, D), dtype=np.int64)
+    expo = np.zeros((N, heads))
+    for r in range(N):
+        t = r % tokens
+        for h in range(heads):
+            lead = (t + 3 * h) % D
+            others = rng.choice(np.delete(np.arange(D), lead), size=len(pat) - 1, replace=False)
+            pos = np.concatenate([[lead], others])
+            k[r, h, pos] = np.array(pat) * rng.choice([-1, 1], size=len(pat))
+    if mode == "pchan":
+        # no norm separation: one exponent per (block, head) so each channel's max is Q 2^p
+        for blk in range(N // B):
+            expo[blk * B:(blk + 1) * B] = rng.integers(-3, 4, size=heads)
+    else:
+        expo[:] = rng.integers(-2, 4, size=(N, heads))
+    if mode in ("naive", "pchan"):
+        y = k * np.exp2(expo)[..., None]                    # scale = 2^p, quotient = k
+    else:
+        y = k * np.exp2(expo - e)[..., None]                # nu = 2^p, u = 2^-e k
+    signs = None
+    x = y
+    if hadamard:
+        n = hadamard
+        signs = rng.choice(np.array([-1, 1], dtype=np.int8), size=(heads, D))
+        H = scipy.linalg.hadamard(n).astype(np.float64)
+        blocks = y.reshape(N, heads, D // n, n) @ H.T / np.sqrt(n)   # H symmetric
+        x = blocks.reshape(N, heads, D) * signs[None]
+    assert np.all(np.abs(x) < 60000)
+    assert np.all(x.astype(np.float16).astype(np.float64) == x), "grid input not fp16-exact"
+    return spec, x, signs, k.astype(np.int8)
