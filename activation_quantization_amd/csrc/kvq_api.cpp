@@ -1,0 +1,240 @@
+// C ABI of libkvq: argument validation (before any HIP call), sizing and dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kvq_status ok() {
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+bool nsep_mode(int m) { return m == KVQ_NSEP || m == KVQ_NSEP_PCHAN; }
+bool pchan_mode(int m) { return m == KVQ_PCHAN || m == KVQ_NSEP_PCHAN; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kvq_status check_desc(const kvq_desc* d) {
+  if (!d) return fail(KVQ_ERR_NULL, "descriptor is NULL");
+  if (d->seqs < 0 || d->tokens_per_seq < 0)
+    return fail(KVQ_ERR_SHAPE, "seqs (%lld) and tokens_per_seq (%lld) must be >= 0",
+                (long long)d->seqs, (long long)d->tokens_per_seq);
+  if (d->heads <= 0 || d->head_dim <= 0)
+    return fail(KVQ_ERR_SHAPE, "heads (%lld) and head_dim (%lld) must be >= 1",
+                (long long)d->heads, (long long)d->head_dim);
+  if (d->head_dim & 1) return fail(KVQ_ERR_SHAPE, "head_dim %lld is odd", (long long)d->head_dim);
+  if (d->reserved != 0) return fail(KVQ_ERR_UNSUPPORTED, "reserved field must be 0");
+  if (d->bits < 2 || d->bits > 4) return fail(KVQ_ERR_UNSUPPORTED, "bits %d not in {2, 3, 4}", d->bits);
+  if (d->mode < KVQ_NAIVE || d->mode > KVQ_NSEP_PCHAN) return fail(KVQ_ERR_UNSUPPORTED, "unknown mode %d", d->mode);
+  if (d->dtype != KVQ_F16 && d->dtype != KVQ_BF16)
+    return fail(KVQ_ERR_UNSUPPORTED, "input dtype %d must be KVQ_F16 or KVQ_BF16", d->dtype);
+  const int64_t D = d->head_dim;
+  if (d->hadamard != 0) {
+    if (d->hadamard < 0 || !pow2(d->hadamard) || D % d->hadamard != 0)
+      return fail(KVQ_ERR_SHAPE, "hadamard %d must be a power of two dividing head_dim %lld", d->hadamard, (long long)D);
+    if (d->hadamard < 16 || d->hadamard > 128)
+      return fail(KVQ_ERR_UNSUPPORTED, "hadamard %d not in {16, 32, 64, 128}", d->hadamard);
+  }
+  if (pchan_mode(d->mode)) {
+    if (D != 64 && D != 128) return fail(KVQ_ERR_UNSUPPORTED, "per-channel modes need head_dim 64 or 128 (got %lld)", (long long)D);
+    if (d->block_tokens <= 0) return fail(KVQ_ERR_SHAPE, "block_tokens %d must be >= 1", d->block_tokens);
+    if (d->block_tokens != 64 && d->block_tokens != 128 && d->block_tokens != 256)
+      return fail(KVQ_ERR_UNSUPPORTED, "block_tokens %d not in {64, 128, 256}", d->block_tokens);
+    if (d->block_tokens == 256 && D == 128)
+      return fail(KVQ_ERR_UNSUPPORTED, "block_tokens 256 needs head_dim 64");
+    if (d->tokens_per_seq % d->block_tokens != 0)
+      return fail(KVQ_ERR_SHAPE, "block_tokens %d does not divide tokens_per_seq %lld", d->block_tokens,
+                  (long long)d->tokens_per_seq);
+  } else {
+    if (!pow2(D) || D < 64 || D > 8192)
+      return fail(KVQ_ERR_UNSUPPORTED, "per-token modes need head_dim a power of two in [64, 8192] (got %lld)", (long long)D);
+  }
+  // grid limits (one workgroup per tile; ids below 2^31)
+  const int64_t rows = d->seqs * d->tokens_per_seq;
+  if (rows > (int64_t(1) << 40) || d->heads > (int64_t(1) << 20))
+    return fail(KVQ_ERR_UNSUPPORTED, "tensor too large");
+  const int64_t tiles = pchan_mode(d->mode) ? rows / d->block_tokens * d->heads
+                                            : (rows * d->heads * (D / (D >= 128 ? 128 : 64)) + 63) / 64;
+  if (tiles >= (int64_t(1) << 31)) return fail(KVQ_ERR_UNSUPPORTED, "too many tiles (%lld)", (long long)tiles);
+  return KVQ_OK;
+}
+
+bool empty_work(const kvq_desc* d) { return d->seqs == 0 || d->tokens_per_seq == 0; }
+
+kvq_status device_ready() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(KVQ_ERR_HIP, "no HIP device available");
+  }
+  return KVQ_OK;
+}
+
+kvq_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+float qmax(int bits) { return float((1 << (bits - 1)) - 1); }
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_validate(const kvq_desc* d) {
+  const kvq_status s = check_desc(d);
+  return s == KVQ_OK ? ok() : s;
+}
+
+int64_t kvq_codes_bytes(const kvq_desc* d) {
+  if (check_desc(d) != KVQ_OK) return -1;
+  return d->seqs * d->tokens_per_seq * d->heads * d->head_dim / 2;
+}
+
+int64_t kvq_norms_count(const kvq_desc* d) {
+  if (check_desc(d) != KVQ_OK) return -1;
+  return nsep_mode(d->mode) ? d->seqs * d->tokens_per_seq * d->heads : 0;
+}
+
+int64_t kvq_scales_count(const kvq_desc* d) {
+  if (check_desc(d) != KVQ_OK) return -1;
+  const int64_t rows = d->seqs * d->tokens_per_seq;
+  return pchan_mode(d->mode) ? rows / d->block_tokens * d->heads * d->head_dim : rows * d->heads;
+}
+
+kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs, uint8_t* codes,
+                        uint16_t* norms, uint16_t* scales, void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (empty_work(d)) return ok();
+  if (!x || !codes || !scales) return fail(KVQ_ERR_NULL, "x, codes and scales are required");
+  if (nsep_mode(d->mode) != (norms != nullptr))
+    return fail(KVQ_ERR_NULL, nsep_mode(d->mode) ? "NSEP modes need a norms buffer" : "norms must be NULL without NSEP");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(x, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "x, codes and signs must be 16-byte aligned");
+  if (!aligned(scales, 2) || (norms && !aligned(norms, 2)))
+    return fail(KVQ_ERR_ALIGN, "norms and scales must be 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+
+  kvq::QuantArgs a{};
+  a.x = x; a.signs = signs; a.codes = codes; a.norms = norms; a.scales = scales;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.q = qmax(d->bits);
+  a.nsep = nsep_mode(d->mode);
+  a.dtype = d->dtype == KVQ_F16 ? kvq::DT_F16 : kvq::DT_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(pchan_mode(d->mode) ? kvq::launch_quantize_pchan(a, st) : kvq::launch_quantize_ptok(a, st),
+                  "quantize");
+}
+
+kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_t* norms,
+                          const uint16_t* scales, const int8_t* signs, void* y, int32_t y_dtype, void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (y_dtype != KVQ_F16 && y_dtype != KVQ_BF16 && y_dtype != KVQ_F32)
+    return fail(KVQ_ERR_UNSUPPORTED, "output dtype %d not in {F16, BF16, F32}", y_dtype);
+  if (empty_work(d)) return ok();
+  if (!codes || !scales || !y) return fail(KVQ_ERR_NULL, "codes, scales and y are required");
+  if (nsep_mode(d->mode) != (norms != nullptr))
+    return fail(KVQ_ERR_NULL, nsep_mode(d->mode) ? "NSEP modes need a norms buffer" : "norms must be NULL without NSEP");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(y, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "y, codes and signs must be 16-byte aligned");
+  if (!aligned(scales, 2) || (norms && !aligned(norms, 2)))
+    return fail(KVQ_ERR_ALIGN, "norms and scales must be 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+
+  kvq::DequantArgs a{};
+  a.codes = codes; a.norms = norms; a.scales = scales; a.signs = signs; a.y = y;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.nsep = nsep_mode(d->mode);
+  a.per_channel = pchan_mode(d->mode);
+  a.out_dtype = y_dtype == KVQ_F16 ? kvq::DT_F16 : y_dtype == KVQ_BF16 ? kvq::DT_BF16 : kvq::DT_F32;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(a.per_channel ? kvq::launch_dequantize_pchan(a, st) : kvq::launch_dequantize_ptok(a, st),
+                  "dequantize");
+}
+
+kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* codes,
+                            const uint16_t* norms, const uint16_t* scales, const int8_t* signs, float* scores,
+                            void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode score needs head_dim 64 or 128 (got %lld)", (long long)d->head_dim);
+  if (q_heads <= 0 || q_heads % d->heads != 0)
+    return fail(KVQ_ERR_SHAPE, "q_heads %lld must be a positive multiple of heads %lld", (long long)q_heads,
+                (long long)d->heads);
+  if (q_heads / d->heads > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (empty_work(d)) return ok();
+  if (!q || !codes || !scales || !scores) return fail(KVQ_ERR_NULL, "q, codes, scales and scores are required");
+  if (nsep_mode(d->mode) != (norms != nullptr))
+    return fail(KVQ_ERR_NULL, nsep_mode(d->mode) ? "NSEP modes need a norms buffer" : "norms must be NULL without NSEP");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(codes, 16)) return fail(KVQ_ERR_ALIGN, "codes must be 16-byte aligned");
+  if (!aligned(q, 2) || !aligned(scales, 2) || (norms && !aligned(norms, 2)) || !aligned(scores, 4))
+    return fail(KVQ_ERR_ALIGN, "q, norms, scales must be 2-byte and scores 4-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+
+  kvq::ScoreArgs a{};
+  a.q = q; a.codes = codes; a.norms = norms; a.scales = scales; a.signs = signs; a.scores = scores;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim; a.q_heads = q_heads;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.nsep = nsep_mode(d->mode);
+  a.per_channel = pchan_mode(d->mode);
+  return launched(kvq::launch_score_decode(a, static_cast<hipStream_t>(stream)), "score_decode");
+}
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_NULL: return "KVQ_ERR_NULL: missing or forbidden pointer";
+    case KVQ_ERR_ALIGN: return "KVQ_ERR_ALIGN: misaligned buffer";
+    case KVQ_ERR_SHAPE: return "KVQ_ERR_SHAPE: inconsistent sizes";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: parameters outside the built kernels";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: HIP runtime error";
+  }
+  return "unknown kvq_status";
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvq_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Device-side building blocks shared by the gfx950 kernels (HIP, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ conversions
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+// low / high 16-bit element of a packed pair -> fp32
+template <int DT> __device__ __forceinline__ float lo_f32(uint32_t w) {
+  if constexpr (DT == DT_F16) return f16_to_f32(w & 0xffffu);
+  else return __builtin_bit_cast(float, w << 16);
+}
+template <int DT> __device__ __forceinline__ float hi_f32(uint32_t w) {
+  if constexpr (DT == DT_F16) return f16_to_f32(w >> 16);
+  else return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+// fp32 -> fp16 bits, round to nearest even (hardware default rounding mode)
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+template <int DT> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == DT_F16) return f32_to_f16(a) | (f32_to_f16(b) << 16);
+  else return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+// ------------------------------------------------------------------ launch geometry
+// MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs (each with its
+// own L2).  Remap so that every XCD walks a contiguous range of tiles: neighbouring tiles
+// (which share cache lines of the codes, norms and scales outputs) then run on one L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
+  const int64_t x = bid & 7, k = bid >> 3;
+  const int64_t per = n >> 3, rem = n & 7;
+  return x * per + (x < rem ? x : rem) + k;
+}
+
+// 16-byte-chunk XOR swizzle for LDS tiles of `row_bytes` per row (power of two, >= 16):
+// consecutive rows land on different bank groups for both row-wise and chunk-wise access.
+__device__ __forceinline__ int swz_chunk(int row, int cc, int row_bytes) {
+  const int cpr = row_bytes >> 4;                         // chunks per row
+  const int rows_per_256 = row_bytes >= 256 ? 1 : 256 / row_bytes;
+  return cc ^ ((row / rows_per_256) & (cpr - 1));
+}
+
+// ------------------------------------------------------------------ wave helpers
+__device__ __forceinline__ void wave_lds_sync() {
+  // orders this wave's LDS accesses (LDS executes one wave's instructions in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float shfl_f(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+// ------------------------------------------------------------------ Walsh-Hadamard
+// In-register fast Walsh-Hadamard transform (unnormalized, natural Sylvester order) on
+// independent blocks of n = 2^lg consecutive elements of v[R]; lg is wave-uniform.
+// One butterfly stage per index bit: (a, b) -> (a + b, a - b).
+template <int R>
+__device__ __forceinline__ void fwht_blocks(float (&v)[R], int lg) {
+#pragma unroll
+  for (int s = 0; (1 << s) < R; ++s) {
+    if (s < lg) {
+      const int st = 1 << s;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if ((i & st) == 0) {
+          const float a = v[i], b = v[i + st];
+          v[i] = a + b;
+          v[i + st] = a - b;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace kvq

@@ -1,0 +1,63 @@
+// Host <-> kernel interface inside libkvq (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+
+struct QuantArgs {
+  const void* x;            // [rows, heads, D] f16/bf16
+  const int8_t* signs;      // [heads, D] or null
+  uint8_t* codes;           // [rows, heads, D/2]
+  uint16_t* norms;          // [rows, heads] or null
+  uint16_t* scales;         // per token [rows, heads] or per channel [rows/B, heads, D]
+  int64_t seqs, tokens, heads, dim;
+  int32_t block;            // B (per-channel modes)
+  int32_t lg_had;           // log2 n, 0 = no rotation
+  float inv_sqrt_n;         // 1/sqrt(n) (1 when no rotation)
+  float q;                  // Q = 2^(bits-1) - 1
+  int32_t nsep;             // norm separation on/off
+  int32_t dtype;            // DT_F16 / DT_BF16
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint16_t* norms;
+  const uint16_t* scales;
+  const int8_t* signs;
+  void* y;
+  int64_t seqs, tokens, heads, dim;
+  int32_t block;
+  int32_t lg_had;
+  float inv_sqrt_n;
+  int32_t nsep;
+  int32_t per_channel;
+  int32_t out_dtype;        // DT_F16 / DT_BF16 / DT_F32
+};
+
+struct ScoreArgs {
+  const uint16_t* q;        // [seqs, q_heads, D] fp16
+  const uint8_t* codes;
+  const uint16_t* norms;
+  const uint16_t* scales;
+  const int8_t* signs;
+  float* scores;            // [seqs, q_heads, tokens]
+  int64_t seqs, tokens, heads, dim, q_heads;
+  int32_t block;
+  int32_t lg_had;
+  float inv_sqrt_n;
+  int32_t nsep;
+  int32_t per_channel;
+};
+
+// Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
+hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t stream);
+
+}  // namespace kvq

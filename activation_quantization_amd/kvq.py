@@ -1,0 +1,186 @@
+"""Thin ctypes binding of libkvq (argument marshalling only; every step runs in HIP kernels).
+
+The names mirror the C ABI in include/kvq.h: quantize / dequantize / score_decode.  Tensors
+are torch tensors on the current HIP device (torch is used for device memory and streams);
+outputs are allocated with torch when not supplied.  There is no CPU fallback: if libkvq.so
+is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP = range(6)
+MODES = {"naive": 0, "nsep": 1, "pchan": 2, "nsep_pchan": 3}
+DTYPES = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
+DTYPE_NAMES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+class KvqDesc(ctypes.Structure):
+    _fields_ = [("seqs", ctypes.c_int64), ("tokens_per_seq", ctypes.c_int64),
+                ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("hadamard", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "kvq_validate": (ctypes.c_int, [ctypes.POINTER(KvqDesc)]),
+    "kvq_codes_bytes": (ctypes.c_int64, [ctypes.POINTER(KvqDesc)]),
+    "kvq_norms_count": (ctypes.c_int64, [ctypes.POINTER(KvqDesc)]),
+    "kvq_scales_count": (ctypes.c_int64, [ctypes.POINTER(KvqDesc)]),
+    "kvq_quantize": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, _P]),
+    "kvq_dequantize": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
+    "kvq_score_decode": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
+    "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvq_last_error": (ctypes.c_char_p, []),
+    "kvq_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so (built in-tree by activation_quantization_amd.build_lib)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m activation_quantization_amd.build_lib`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        L = lib()
+        super().__init__(f"{what}: {L.kvq_status_str(status).decode()} -- {L.kvq_last_error().decode()}")
+        self.status = status
+
+
+@dataclasses.dataclass(frozen=True)
+class Desc:
+    """Python mirror of kvq_desc; x is [seqs * tokens_per_seq, heads, head_dim]."""
+    seqs: int
+    tokens_per_seq: int
+    heads: int
+    head_dim: int
+    bits: int = 4
+    mode: str = "nsep_pchan"
+    block_tokens: int = 128
+    hadamard: int = 0
+    dtype: torch.dtype = torch.float16
+
+    def c(self) -> KvqDesc:
+        return KvqDesc(self.seqs, self.tokens_per_seq, self.heads, self.head_dim, self.bits,
+                       MODES[self.mode], self.block_tokens if "pchan" in self.mode else 0,
+                       self.hadamard, DTYPES[self.dtype], 0)
+
+    @property
+    def nsep(self) -> bool:
+        return self.mode in ("nsep", "nsep_pchan")
+
+    @property
+    def per_channel(self) -> bool:
+        return self.mode in ("pchan", "nsep_pchan")
+
+    @property
+    def rows(self) -> int:
+        return self.seqs * self.tokens_per_seq
+
+    def validate(self) -> int:
+        return lib().kvq_validate(ctypes.byref(self.c()))
+
+    def codes_bytes(self) -> int:
+        return lib().kvq_codes_bytes(ctypes.byref(self.c()))
+
+    def norms_count(self) -> int:
+        return lib().kvq_norms_count(ctypes.byref(self.c()))
+
+    def scales_count(self) -> int:
+        return lib().kvq_scales_count(ctypes.byref(self.c()))
+
+    def codes_shape(self):
+        return (self.rows, self.heads, self.head_dim // 2)
+
+    def scales_shape(self):
+        if self.per_channel:
+            return (self.rows // self.block_tokens, self.heads, self.head_dim)
+        return (self.rows, self.heads)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise KvqError(status, what)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the HIP device")
+
+
+def alloc_outputs(d: Desc, device):
+    codes = torch.empty(d.codes_shape(), dtype=torch.uint8, device=device)
+    norms = torch.empty((d.rows, d.heads), dtype=torch.float16, device=device) if d.nsep else None
+    scales = torch.empty(d.scales_shape(), dtype=torch.float16, device=device)
+    return codes, norms, scales
+
+
+def quantize(d: Desc, x: torch.Tensor, signs: torch.Tensor | None = None,
+             out=None, stream=None):
+    """kvq_quantize.  Returns (codes uint8, norms fp16 or None, scales fp16)."""
+    codes, norms, scales = out if out is not None else alloc_outputs(d, x.device)
+    _need_cuda(x, signs, codes, norms, scales)
+    st = lib().kvq_quantize(ctypes.byref(d.c()), _ptr(x), _ptr(signs), _ptr(codes), _ptr(norms),
+                            _ptr(scales), _stream(stream))
+    _check(st, "kvq_quantize")
+    return codes, norms, scales
+
+
+def dequantize(d: Desc, codes, norms, scales, signs=None, out_dtype=torch.float16,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_dequantize.  Returns y [rows, heads, head_dim] in out_dtype."""
+    if out is None:
+        out = torch.empty((d.rows, d.heads, d.head_dim), dtype=out_dtype, device=codes.device)
+    _need_cuda(codes, norms, scales, signs, out)
+    st = lib().kvq_dequantize(ctypes.byref(d.c()), _ptr(codes), _ptr(norms), _ptr(scales), _ptr(signs),
+                              _ptr(out), DTYPES[out.dtype], _stream(stream))
+    _check(st, "kvq_dequantize")
+    return out
+
+
+def score_decode(d: Desc, q: torch.Tensor, codes, norms, scales, signs=None,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_score_decode.  q fp16 [seqs, q_heads, head_dim] -> scores fp32 [seqs, q_heads, tokens]."""
+    if q.dtype != torch.float16:
+        raise ValueError("q must be fp16")
+    q_heads = q.shape[1]
+    if out is None:
+        out = torch.empty((d.seqs, q_heads, d.tokens_per_seq), dtype=torch.float32, device=codes.device)
+    _need_cuda(q, codes, norms, scales, signs, out)
+    st = lib().kvq_score_decode(ctypes.byref(d.c()), _ptr(q), q_heads, _ptr(codes), _ptr(norms),
+                                _ptr(scales), _ptr(signs), _ptr(out), _stream(stream))
+    _check(st, "kvq_score_decode")
+    return out

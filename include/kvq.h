@@ -1,0 +1,149 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) KV-cache / activation quantizer.
+ *
+ * The method (sources, by page title and section):
+ *   - "nsep+pchan" norm-separation post, "the fix": split each KV vector into an fp16 L2 norm
+ *     and a unit direction, then quantize the direction with per-channel scales; symmetric
+ *     round-to-nearest onto +-(2^(b-1)-1) (the snippet divides the absmax by 7 and clamps to
+ *     +-7 at INT4; INT3 is discussed under "INT3 > INT4").
+ *   - Rotated Runtime Smooth analysis, "problem definition" (alpha = max|X| / (2^(N-1)-1)) and
+ *     "term-by-term" (rotation R = (1/sqrt K)[+-1], R R^T = I; runtime scale s_j = max over
+ *     tokens of column j).
+ *   - NSNQuant summary, "Hadamard transform" (randomized Hadamard before quantization) and
+ *     "implementation details" (scores computed from the quantized cache with the stored
+ *     parameters folded into the kernel).
+ *   - Activation-guided compensation abstract: random +-1 signs before the Hadamard rotation.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor x is [rows, heads, head_dim], rows = seqs * tokens_per_seq, head_dim fastest,
+ *     contiguous.  For a wide activation row use heads = 1, head_dim = hidden.
+ *   - Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA tensor's storage)
+ *     on the current HIP device.  The caller allocates and owns every buffer; buffers must
+ *     stay alive until the work enqueued on `stream` has completed.  The library keeps no
+ *     pointer after a call returns and allocates nothing on these paths.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Every call only
+ *     enqueues kernels and returns without synchronizing; device faults surface at the
+ *     caller's next synchronization.
+ *   - All validation happens before anything is enqueued: on any error status nothing is
+ *     launched and no output is touched.  kvq_last_error() then describes the failure
+ *     (thread-local string).  No C++ exception crosses this interface.
+ *
+ * Storage formats
+ *   codes   uint8 [rows, heads, head_dim/2]: two 4-bit two's-complement codes per byte,
+ *           channel 2i in the low nibble, 2i+1 in the high nibble.  INT3 and 2-bit codes use
+ *           the same nibble layout.  Codes lie in [-Q, Q], Q = 2^(bits-1)-1.
+ *   norms   fp16 bits [rows, heads]: the L2 norm of each (rotated) vector; NSEP modes only.
+ *   scales  fp16 bits.  Per-token modes (NAIVE, NSEP): [rows, heads] = absmax / Q of the
+ *           (rotated, normalized) vector.  Per-channel modes (PCHAN, NSEP_PCHAN):
+ *           [seqs * tokens_per_seq / block_tokens, heads, head_dim] = max over the block's
+ *           tokens of |u| / Q, one per channel.
+ *   signs   int8 [heads, head_dim] of +-1 (any value < 0 counts as -1).  Block k of n
+ *           channels of head h uses signs[h, k*n : (k+1)*n].  NULL iff hadamard == 0.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,        /* a required pointer is NULL, or a forbidden one is non-NULL     */
+  KVQ_ERR_ALIGN = 2,       /* x, y, codes or signs not 16-byte aligned; norms, scales or q not
+                              2-byte aligned; scores not 4-byte aligned                      */
+  KVQ_ERR_SHAPE = 3,       /* negative seqs / tokens, heads or head_dim < 1, odd head_dim, n
+                              does not divide head_dim, block does not divide tokens_per_seq,
+                              q_heads not a positive multiple of heads                       */
+  KVQ_ERR_UNSUPPORTED = 4, /* bits, dtype, head_dim, block or n outside the built kernels     */
+  KVQ_ERR_HIP = 5          /* no HIP device, or the launch reported an error                 */
+} kvq_status;
+
+typedef enum {
+  KVQ_NAIVE = 0,      /* per-token absmax of x (after the optional rotation)                 */
+  KVQ_NSEP = 1,       /* norm separation, per-token absmax of the unit direction             */
+  KVQ_PCHAN = 2,      /* per-channel absmax over a block of tokens, no norm separation       */
+  KVQ_NSEP_PCHAN = 3  /* norm separation, then per-channel scales over the token block       */
+} kvq_mode;
+
+typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2 } kvq_dtype;
+
+/* Shape and method parameters (all fields plain integers for a stable layout: 56 bytes). */
+typedef struct {
+  int64_t seqs;           /* number of sequences (>= 0)                                       */
+  int64_t tokens_per_seq; /* tokens per sequence (>= 0); seqs or tokens_per_seq = 0 is an empty
+                             input: calls return KVQ_OK without launching or reading pointers */
+  int64_t heads;          /* KV heads (>= 1)                                                  */
+  int64_t head_dim;       /* channels per head: 64 or 128; per-token modes also 256..8192
+                             (powers of two)                                                  */
+  int32_t bits;           /* 2, 3 or 4                                                        */
+  int32_t mode;           /* kvq_mode                                                         */
+  int32_t block_tokens;   /* per-channel token block B: 64, 128 or 256 (B <= 128 when
+                             head_dim = 128); must divide tokens_per_seq; ignored (set 0) for
+                             per-token modes                                                  */
+  int32_t hadamard;       /* 0 = no rotation; else n in {16, 32, 64, 128}, n | head_dim       */
+  int32_t dtype;          /* kvq_dtype of x: KVQ_F16 or KVQ_BF16                              */
+  int32_t reserved;       /* must be 0                                                        */
+} kvq_desc;
+
+/* Checks a descriptor without touching the device.  KVQ_OK or the reason it is refused. */
+kvq_status kvq_validate(const kvq_desc* d);
+
+/* Buffer sizes for a valid descriptor (-1 if kvq_validate fails):
+ *   codes bytes = rows*heads*head_dim/2; norms = rows*heads for NSEP modes, else 0;
+ *   scales = rows*heads (per-token) or seqs*(tokens_per_seq/block_tokens)*heads*head_dim.  */
+int64_t kvq_codes_bytes(const kvq_desc* d);
+int64_t kvq_norms_count(const kvq_desc* d);
+int64_t kvq_scales_count(const kvq_desc* d);
+
+/*
+ * Quantize x [rows, heads, head_dim] (dtype d->dtype) into packed codes, fp16 norms (NSEP
+ * modes) and fp16 scales.  Steps per (token, head) vector: optional signs then orthonormal
+ * block Hadamard (1/sqrt n, natural Sylvester order); nu = ||y||_2 and u = y/nu (NSEP modes;
+ * nu = 0 gives u = 0); scale = absmax / Q per token or per channel over the token block;
+ * code = clamp(round_half_even(u / scale), -Q, Q) computed from the unrounded fp32 scale and
+ * norm (scale = 0 gives code 0).  Stored norms and scales are the fp16 (round-to-nearest-even)
+ * values of nu and scale.
+ *   norms must be NULL for NAIVE / PCHAN and non-NULL for NSEP modes.
+ */
+kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs,
+                        uint8_t* codes, uint16_t* norms, uint16_t* scales, void* stream);
+
+/*
+ * Dequantize: y^ = code * scale * (norm for NSEP modes), then the inverse rotation
+ * sigma * (1/sqrt n) H y^, written to y [rows, heads, head_dim] in y_dtype (F16, BF16 or
+ * F32, round-to-nearest-even).  Inputs are exactly the buffers kvq_quantize writes.
+ */
+kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_t* norms,
+                          const uint16_t* scales, const int8_t* signs, void* y, int32_t y_dtype,
+                          void* stream);
+
+/*
+ * Decode attention scores straight from the packed K cache described by d (head_dim 64 or
+ * 128):  scores[s, hq, t] = sum_d q[s, hq, d] * k^[s*T + t, hq / G, d], G = q_heads/heads
+ * (query heads grouped contiguously), k^ the dequantized key.  No 1/sqrt(d), no softmax.
+ * The kernel works in the rotated domain: it rotates each query once and folds the stored
+ * scales and norms into the contraction.
+ *   q: fp16 bits [seqs, q_heads, head_dim]; scores: fp32 [seqs, q_heads, tokens_per_seq].
+ */
+kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads,
+                            const uint8_t* codes, const uint16_t* norms, const uint16_t* scales,
+                            const int8_t* signs, float* scores, void* stream);
+
+/* Static description of a status code. */
+const char* kvq_status_str(kvq_status s);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* ABI version: 10000 * major + 100 * minor + patch. */
+int32_t kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,122 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol, lays out
+kvq_desc as the header says, and refuses bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_quantization_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"libkvq.so does not export {n}"
+    assert set(names) == set(kvq._SIGNATURES), "binding and header disagree"
+
+
+def test_desc_layout_matches_header():
+    assert "56 bytes" in open(HEADER).read()
+    assert ctypes.sizeof(kvq.KvqDesc) == 56
+    offs = [getattr(kvq.KvqDesc, f[0]).offset for f in kvq.KvqDesc._fields_]
+    assert offs == [0, 8, 16, 24, 32, 36, 40, 44, 48, 52]
+
+
+def test_version_and_status_strings():
+    L = kvq.lib()
+    assert L.kvq_version() >= 10000
+    for s in range(6):
+        assert L.kvq_status_str(s).startswith(b"KVQ_")
+
+
+GOOD = dict(seqs=2, tokens_per_seq=256, heads=4, head_dim=128, bits=4, mode="nsep_pchan",
+            block_tokens=128, hadamard=128)
+
+
+@pytest.mark.parametrize("change,want", [
+    ({}, kvq.OK),
+    ({"tokens_per_seq": 250}, kvq.ERR_SHAPE),             # block does not divide the sequence
+    ({"head_dim": 127, "mode": "naive"}, kvq.ERR_SHAPE),  # odd
+    ({"heads": 0}, kvq.ERR_SHAPE),
+    ({"seqs": -1}, kvq.ERR_SHAPE),
+    ({"hadamard": 48}, kvq.ERR_SHAPE),                    # not a power of two
+    ({"hadamard": 256, "mode": "naive", "head_dim": 512}, kvq.ERR_UNSUPPORTED),
+    ({"hadamard": 8}, kvq.ERR_UNSUPPORTED),
+    ({"bits": 5}, kvq.ERR_UNSUPPORTED),
+    ({"bits": 1}, kvq.ERR_UNSUPPORTED),
+    ({"head_dim": 256}, kvq.ERR_UNSUPPORTED),             # per-channel needs 64 / 128
+    ({"head_dim": 96, "mode": "naive", "hadamard": 0}, kvq.ERR_UNSUPPORTED),
+    ({"block_tokens": 32, "tokens_per_seq": 256}, kvq.ERR_UNSUPPORTED),
+    ({"block_tokens": 256}, kvq.ERR_UNSUPPORTED),         # 256 only with head_dim 64
+    ({"head_dim": 64, "block_tokens": 256, "hadamard": 64}, kvq.OK),
+    ({"head_dim": 4096, "mode": "naive", "block_tokens": 0}, kvq.OK),
+    ({"head_dim": 16384, "mode": "naive", "block_tokens": 0}, kvq.ERR_UNSUPPORTED),
+    ({"seqs": 0}, kvq.OK),                                # empty input is valid
+])
+def test_validation_matrix(change, want):
+    p = dict(GOOD)
+    p.update(change)
+    d = kvq.Desc(**p)
+    got = d.validate()
+    assert got == want, kvq.lib().kvq_last_error()
+    if want != kvq.OK:
+        assert kvq.lib().kvq_last_error()
+
+
+def test_size_queries():
+    d = kvq.Desc(**GOOD)
+    assert d.codes_bytes() == 2 * 256 * 4 * 64
+    assert d.norms_count() == 2 * 256 * 4
+    assert d.scales_count() == 2 * 2 * 4 * 128
+    n = kvq.Desc(1, 8192, 1, 4096, 4, "naive", 0, 128, kvq.torch.bfloat16)
+    assert n.codes_bytes() == 8192 * 2048 and n.norms_count() == 0 and n.scales_count() == 8192
+    assert kvq.Desc(**{**GOOD, "bits": 7}).codes_bytes() == -1
+
+
+FAKE = 1 << 20   # an aligned address that is never dereferenced: validation fails first
+
+
+def _q(d, x=FAKE, signs=FAKE, codes=FAKE, norms=FAKE, scales=FAKE):
+    return kvq.lib().kvq_quantize(ctypes.byref(d.c()), x, signs, codes, norms, scales, None)
+
+
+def test_pointer_checks_before_any_device_call():
+    d = kvq.Desc(**GOOD)
+    assert _q(d, x=None) == kvq.ERR_NULL
+    assert _q(d, norms=None) == kvq.ERR_NULL
+    assert _q(d, signs=None) == kvq.ERR_NULL
+    assert _q(kvq.Desc(**{**GOOD, "mode": "pchan"})) == kvq.ERR_NULL      # norms must be NULL
+    assert _q(kvq.Desc(**{**GOOD, "hadamard": 0})) == kvq.ERR_NULL        # signs must be NULL
+    assert _q(d, x=FAKE + 2) == kvq.ERR_ALIGN
+    assert _q(d, codes=FAKE + 8) == kvq.ERR_ALIGN
+    assert _q(d, scales=FAKE + 1) == kvq.ERR_ALIGN
+    L = kvq.lib()
+    assert L.kvq_dequantize(ctypes.byref(d.c()), FAKE, FAKE, FAKE, FAKE, FAKE, 7, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_score_decode(ctypes.byref(d.c()), FAKE, 6, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_SHAPE
+    assert L.kvq_score_decode(ctypes.byref(d.c()), FAKE, 4 * 17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+def test_no_device_maps_to_err_hip():
+    d = kvq.Desc(**GOOD)
+    assert _q(d) == kvq.ERR_HIP
+    assert b"no HIP device" in kvq.lib().kvq_last_error()
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "LIB_PATH", "/nonexistent/libkvq.so")
+    with pytest.raises(ImportError):
+        kvq.lib()
