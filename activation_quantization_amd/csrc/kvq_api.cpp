@@ -149,6 +149,7 @@ kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs, u
   a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
   a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
   a.q = qmax(d->bits);
+  a.scale_mul = float((d->hadamard ? 1.0 / std::sqrt(double(d->hadamard)) : 1.0) / double(qmax(d->bits)));
   a.nsep = nsep_mode(d->mode);
   a.dtype = d->dtype == KVQ_F16 ? kvq::DT_F16 : kvq::DT_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -53,7 +53,7 @@ __device__ __forceinline__ void stage_row(unsigned char* stage, int row, const f
 
 // ---------------------------------------------------------------------------------------
 // Per-channel modes: one workgroup of B threads per (sequence, token block, head) tile.
-template <int ODT, int R>
+template <int ODT, int R, int LG>
 __global__ void __launch_bounds__(256) dequant_pchan_kernel(DequantArgs a, int64_t ntiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int CRB = R / 2, CCR = CRB / 16;
@@ -99,8 +99,8 @@ __global__ void __launch_bounds__(256) dequant_pchan_kernel(DequantArgs a, int64
 #pragma unroll
     for (int i = 0; i < R; ++i) y[i] *= nrm;
   }
-  if (a.lg_had) {
-    fwht_blocks<R>(y, a.lg_had);
+  if (LG) {
+    fwht_blocks<R>(y, LG);
 #pragma unroll
     for (int i = 0; i < R; ++i) y[i] *= a.inv_sqrt_n;
     unsign<R>(y, a.signs + h * R);
@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(256) dequant_pchan_kernel(DequantArgs a, int64
 
 // ---------------------------------------------------------------------------------------
 // Per-token modes: one wave per 64 consecutive row segments of R channels.
-template <int ODT, int R>
+template <int ODT, int R, int LG>
 __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t nseg, int64_t ntiles, int lgL) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int CRB = R / 2, CCR = CRB / 16;
@@ -163,8 +163,8 @@ __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[8 * i + e] = nib_f(cw[i], e) * f;
   }
-  if (a.lg_had) {
-    fwht_blocks<R>(y, a.lg_had);
+  if (LG) {
+    fwht_blocks<R>(y, LG);
 #pragma unroll
     for (int i = 0; i < R; ++i) y[i] *= a.inv_sqrt_n;
     unsign<R>(y, a.signs + h * a.dim + part * R);
@@ -185,48 +185,56 @@ __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t
 }
 
 // ---------------------------------------------------------------------------------------
-template <int ODT>
-static hipError_t launch_dq_pchan_odt(const DequantArgs& a, hipStream_t st) {
+template <int ODT, int R, int LG>
+static void dq_pchan_k(const DequantArgs& a, hipStream_t st) {
   constexpr int OB = ODT == DT_F32 ? 4 : 2;
   const int64_t ntiles = a.seqs * (a.tokens / a.block) * a.heads;
-  const size_t lds = (size_t)a.block * a.dim * OB;     // >= the code tile
-  if (a.dim == 128)
-    hipLaunchKernelGGL((dequant_pchan_kernel<ODT, 128>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
-  else
-    hipLaunchKernelGGL((dequant_pchan_kernel<ODT, 64>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
-  return hipGetLastError();
+  const size_t lds = (size_t)a.block * R * OB;     // >= the code tile
+  hipLaunchKernelGGL((dequant_pchan_kernel<ODT, R, LG>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
 }
 
-hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t st) {
-  switch (a.out_dtype) {
-    case DT_F16: return launch_dq_pchan_odt<DT_F16>(a, st);
-    case DT_BF16: return launch_dq_pchan_odt<DT_BF16>(a, st);
-    default: return launch_dq_pchan_odt<DT_F32>(a, st);
-  }
-}
-
-template <int ODT>
-static hipError_t launch_dq_ptok_odt(const DequantArgs& a, hipStream_t st) {
+template <int ODT, int R, int LG>
+static void dq_ptok_k(const DequantArgs& a, hipStream_t st) {
   constexpr int OB = ODT == DT_F32 ? 4 : 2;
-  const int R = a.dim >= 128 ? 128 : 64;
   int lgL = 0;
   while ((R << lgL) < a.dim) ++lgL;
   const int64_t nseg = a.seqs * a.tokens * a.heads * (a.dim / R);
   const int64_t ntiles = (nseg + 63) / 64;
-  const size_t lds = (size_t)64 * R * OB;
-  if (R == 128)
-    hipLaunchKernelGGL((dequant_ptok_kernel<ODT, 128>), dim3((unsigned)ntiles), dim3(64), lds, st, a, nseg, ntiles, lgL);
-  else
-    hipLaunchKernelGGL((dequant_ptok_kernel<ODT, 64>), dim3((unsigned)ntiles), dim3(64), lds, st, a, nseg, ntiles, lgL);
+  hipLaunchKernelGGL((dequant_ptok_kernel<ODT, R, LG>), dim3((unsigned)ntiles), dim3(64), (size_t)64 * R * OB, st, a,
+                     nseg, ntiles, lgL);
+}
+
+// compile-time Hadamard size: LG = log2(n) in {0 (none), 4, 5, 6, 7}
+template <int ODT, int R, bool PCHAN>
+static void dq_by_lg(const DequantArgs& a, hipStream_t st) {
+#define KVQ_DQ(LGV) (PCHAN ? dq_pchan_k<ODT, R, LGV>(a, st) : dq_ptok_k<ODT, R, LGV>(a, st))
+  switch (a.lg_had) {
+    case 0: KVQ_DQ(0); break;
+    case 4: KVQ_DQ(4); break;
+    case 5: KVQ_DQ(5); break;
+    case 6: KVQ_DQ(6); break;
+    default: if constexpr (R >= 128) KVQ_DQ(7); break;
+  }
+#undef KVQ_DQ
+}
+
+template <int ODT, bool PCHAN>
+static void dq_odt(const DequantArgs& a, hipStream_t st) {
+  const bool wide = PCHAN ? a.dim == 128 : a.dim >= 128;
+  if (wide) dq_by_lg<ODT, 128, PCHAN>(a, st); else dq_by_lg<ODT, 64, PCHAN>(a, st);
+}
+
+template <bool PCHAN>
+static hipError_t dq_launch(const DequantArgs& a, hipStream_t st) {
+  switch (a.out_dtype) {
+    case DT_F16: dq_odt<DT_F16, PCHAN>(a, st); break;
+    case DT_BF16: dq_odt<DT_BF16, PCHAN>(a, st); break;
+    default: dq_odt<DT_F32, PCHAN>(a, st); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t st) {
-  switch (a.out_dtype) {
-    case DT_F16: return launch_dq_ptok_odt<DT_F16>(a, st);
-    case DT_BF16: return launch_dq_ptok_odt<DT_BF16>(a, st);
-    default: return launch_dq_ptok_odt<DT_F32>(a, st);
-  }
-}
+hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t st) { return dq_launch<true>(a, st); }
+hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t st) { return dq_launch<false>(a, st); }
 
 }  // namespace kvq

@@ -19,6 +19,7 @@ struct QuantArgs {
   int32_t lg_had;           // log2 n, 0 = no rotation
   float inv_sqrt_n;         // 1/sqrt(n) (1 when no rotation)
   float q;                  // Q = 2^(bits-1) - 1
+  float scale_mul;          // 1 / (sqrt(n) Q): stored scale = max of the unnormalized |u| * scale_mul
   int32_t nsep;             // norm separation on/off
   int32_t dtype;            // DT_F16 / DT_BF16
 };

@@ -7,59 +7,197 @@
 // "term-by-term" (R = (1/sqrt K)[+-1]; runtime scale s_j = max over tokens of column j);
 // NSNQuant summary "Hadamard transform" (randomized Hadamard before quantization).
 //
-// Layout in registers: one thread owns one row of R = min(head_dim, 128) channels of one
-// (token, head) and keeps it in VGPRs from load to store, so the 128-point transform needs
-// no cross-lane traffic.  Tiles are loaded with coalesced 16-byte loads into LDS and read
-// back row-wise through an XOR swizzle; codes leave the same way.
+// Layout: one thread owns one row of R = min(head_dim, 128) channels of one (token, head) and
+// keeps it in VGPRs from load to store, so the transform needs no cross-lane traffic.  Tiles
+// come in with coalesced 16-byte loads through an XOR-swizzled LDS tile and leave the same way.
+//
+// Arithmetic (all equal to the plain definition up to rounding):
+//   * signs + first butterfly stage + fp16/bf16 -> fp32 widening in one v_dot2 per output:
+//     (s0 x0 + s1 x1, s0 x0 - s1 x1) with the sign pair as a packed +-1 operand.
+//   * the transform is left unnormalized (Y = H diag(s) x); 1/sqrt(n) cancels in every
+//     quotient and only enters the stored scale.  ||y|| = ||x|| (orthonormal rotation), so the
+//     norm is taken from the input with v_dot2 (exact squares).  For per-token scales the norm
+//     cancels too: v = Q Y_c / max_c |Y_c|.
+//   * one fma per code: b = bits(u * (Q/m) + 192.5) rounds v = u Q / m onto a 2^-16 grid; bits
+//     16..19 of b are the code's nibble (round half up) and b & 0xffff == 0 flags a near-tie
+//     (|v - (k + 1/2)| <= 2^-17).  The clamp to [-Q, Q] is implied: |u| <= m.
+//   * near-ties (a few per 10^5 codes) are re-decided exactly: the affected channel (per-
+//     channel scales) or vector (per-token scales) is recomputed in fp64 from the input and
+//     the code is rne(fp32(v)), the rounding decision taken on the fp32 value of the quotient.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 
-// y[i] <- -y[i] where the sign byte is negative
-template <int R>
-__device__ __forceinline__ void apply_signs(float (&y)[R], const int8_t* __restrict__ sg) {
+constexpr float MAGIC = 192.5f;   // [128, 256): ulp 2^-16; + 0.5 turns truncation into rounding
+
+// packed +-1 pair (s0, s1) for v_dot2; s* given as the sign bits (bit 15 and 31 positions)
+template <int DT> __device__ __forceinline__ uint32_t one_pair() {
+  return DT == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
+}
+template <int DT> __device__ __forceinline__ float dot2(uint32_t x, uint32_t c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, c), 0.f, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, c), 0.f, false);
+}
+template <int DT> __device__ __forceinline__ float dot2acc(uint32_t x, float acc) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, x), acc, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, x), acc, false);
+}
+
+// Row of packed 16-bit inputs -> fp32 after signs and the first butterfly stage (or plain
+// widening without rotation).  sg: this row's R sign bytes (16-byte aligned).
+template <int DT, int R>
+__device__ __forceinline__ void widen_stage1(float (&y)[R], const uint32_t (&w)[R / 2], const int8_t* __restrict__ sg,
+                                             bool rotate) {
+  if (rotate) {
 #pragma unroll
-  for (int c = 0; c < R / 16; ++c) {
-    const u32x4 sv = *(const u32x4*)(sg + 16 * c);
-    const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w};
+    for (int c = 0; c < R / 16; ++c) {
+      const u32x4 sv = *(const u32x4*)(sg + 16 * c);
+      const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t neg = (s4[j >> 2] >> (8 * (j & 3) + 7)) & 1u;
-      y[16 * c + j] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y[16 * c + j]) ^ (neg << 31));
+      for (int k = 0; k < 8; ++k) {           // pair k of this 16-channel group
+        const uint32_t sw = s4[k >> 1];
+        const uint32_t sb = (k & 1) ? (((sw >> 8) & 0x8000u) | (sw & 0x80000000u))
+                                    : (((sw << 8) & 0x8000u) | ((sw << 16) & 0x80000000u));
+        const uint32_t cp = one_pair<DT>() | sb;
+        const int i = 8 * c + k;
+        y[2 * i] = dot2<DT>(w[i], cp);
+        y[2 * i + 1] = dot2<DT>(w[i], cp ^ 0x80000000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R / 2; ++i) {
+      y[2 * i] = lo_f32<DT>(w[i]);
+      y[2 * i + 1] = hi_f32<DT>(w[i]);
     }
   }
 }
 
-template <int R>
-__device__ __forceinline__ float sum_squares(const float (&y)[R]) {
-  float p[8];
+// in-register butterfly stages 1 .. LG-1 on blocks of 2^LG (stage 0 is done by widen_stage1)
+template <int R, int LG>
+__device__ __forceinline__ void fwht_rest(float (&v)[R]) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) p[k] = y[k] * y[k];
+  for (int s = 1; s < LG; ++s) {
+    const int st = 1 << s;
 #pragma unroll
-  for (int i = 8; i < R; ++i) p[i & 7] = fmaf(y[i], y[i], p[i & 7]);
-  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    for (int i = 0; i < R; ++i) {
+      if ((i & st) == 0) {
+        const float a = v[i], b = v[i + st];
+        v[i] = a + b;
+        v[i + st] = a - b;
+      }
+    }
+  }
 }
 
-template <int R>
-__device__ __forceinline__ float abs_max(const float (&y)[R]) {
-  float m[4] = {0.f, 0.f, 0.f, 0.f};
+template <int DT, int R>
+__device__ __forceinline__ float sum_squares_in(const uint32_t (&w)[R / 2]) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < R; ++i) m[i & 3] = fmaxf(m[i & 3], fabsf(y[i]));
-  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  for (int i = 0; i < R / 2; ++i) p[i & 3] = dot2acc<DT>(w[i], p[i & 3]);
+  return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
-// code = clamp(rne(u * inv_scale), -q, q) as a two's-complement nibble
-__device__ __forceinline__ uint32_t code_nibble(float u, float inv_scale, float q) {
-  float v = __builtin_rintf(u * inv_scale);
-  v = fminf(fmaxf(v, -q), q);
-  return (uint32_t)(int)v & 0xfu;
+// Codes of R values with per-element inverse scale.  cw[i] holds codes 8i..8i+7 (channel
+// 8i + e in nibble e).  Near-ties are reported two ways: the return value is true in lanes
+// holding one, and chm (wave-uniform, R/32 words) gets bit c when any lane of the wave holds
+// a near-tie in channel c (the ballot of the compare itself, reduced on the scalar unit).
+template <int R, bool CHANNEL_FLAGS, typename InvF>
+__device__ __forceinline__ bool quantize_row(const float (&u)[R], InvF inv, uint32_t (&cw)[R / 8], uint32_t (&chm)[R / 32]) {
+  bool f = false;
+#pragma unroll
+  for (int g = 0; g < R / 32; ++g) chm[g] = 0u;
+#pragma unroll
+  for (int i = 0; i < R / 8; ++i) {
+    uint32_t p[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 8 * i + 2 * k;
+      const uint32_t be = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[c], inv(c), MAGIC));
+      const uint32_t bo = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[c + 1], inv(c + 1), MAGIC));
+      const bool fe = (be & 0xffffu) == 0u, fo = (bo & 0xffffu) == 0u;
+      if constexpr (CHANNEL_FLAGS) {
+        if (__ballot(fe)) chm[c >> 5] |= 1u << (c & 31);
+        if (__ballot(fo)) chm[c >> 5] |= 2u << (c & 31);
+      } else {
+        f = f | fe | fo;
+      }
+      p[k] = (be & 0x000F0000u) | ((bo << 4) & 0x00F00000u);   // byte 2 = code pair
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0C0C0602u);
+    const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x06020C0Cu);
+    cw[i] = lo | hi;
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------------- exact
+// fp64 value of channel c of the unnormalized rotation of one input row (R values at `row`):
+// Y_c = sum over c's n-block of (-1)^popcount(c & j) s_j x_j.  Exact for fp16 inputs (the sum
+// of 128 fp16 values fits in 53 bits).
+template <int DT>
+__device__ double exact_rot64(const unsigned char* __restrict__ row, const int8_t* __restrict__ sg, int c, int lg) {
+  if (lg == 0) {
+    const uint32_t h = *(const uint16_t*)(row + 2 * c);
+    return (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
+  }
+  const int n = 1 << lg, base = (c >> lg) << lg;
+  double acc = 0.0;
+  for (int j0 = base; j0 < base + n; j0 += 8) {
+    const u32x4 v = *(const u32x4*)(row + 2 * j0);
+    const u32x2 s8 = *(const u32x2*)(sg + j0);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e;
+      const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
+      const double x = (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
+      const uint32_t sneg = ((e < 4 ? s8.x : s8.y) >> (8 * (e & 3) + 7)) & 1u;
+      const uint32_t hneg = (uint32_t)__builtin_popcount((uint32_t)(c & j & (n - 1))) & 1u;
+      acc += (sneg ^ hneg) ? -x : x;
+    }
+  }
+  return acc;
+}
+
+template <int DT, int R>
+__device__ double exact_sumsq64(const unsigned char* __restrict__ row) {
+  double acc = 0.0;
+  for (int j0 = 0; j0 < R; j0 += 8) {
+    const u32x4 v = *(const u32x4*)(row + 2 * j0);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
+      const double x = (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
+      acc = __builtin_fma(x, x, acc);
+    }
+  }
+  return acc;
+}
+
+// the exact rounding decision: rne of the fp32 value of the fp64 quotient
+__device__ __forceinline__ uint32_t exact_code(double v) {
+  return (uint32_t)(int)__builtin_rintf((float)v) & 0xfu;
+}
+
+// replace the nibble of channel c in row `row` of a staged code tile
+__device__ __forceinline__ void patch_nibble(unsigned char* stage, int row, int crb, int c, uint32_t nib) {
+  const int byte = c >> 1;
+  unsigned char* p = stage + row * crb + swz_chunk(row, byte >> 4, crb) * 16 + (byte & 15);
+  const uint32_t sh = (c & 1) * 4;
+  *p = (unsigned char)((*p & ~(0xFu << sh)) | (nib << sh));
 }
 
 // ---------------------------------------------------------------------------------------
 // Per-channel modes (PCHAN, NSEP_PCHAN): one workgroup of B threads per (sequence, token
 // block, head) tile; thread t owns token t of the block.
-template <int DT, int R>
+template <int DT, int R, int LG>
 __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t ntiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int ROWB = R * 2;        // input row bytes
@@ -71,6 +209,8 @@ __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t n
   unsigned char* stage = smem;                                  // B * ROWB
   float* colmax = (float*)(smem + (size_t)B * ROWB);           // nw * R
   float* invs = colmax + nw * R;                                // R
+  uint32_t* fmask = (uint32_t*)(invs + R);                      // R / 32 flagged-channel bits
+  unsigned long long* m64 = (unsigned long long*)(fmask + 4);   // exact channel max (bits)
 
   const int64_t tile = xcd_tile(blockIdx.x, ntiles);
   const int64_t nb = a.tokens / B;
@@ -80,8 +220,9 @@ __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t n
   const int64_t row0 = s * a.tokens + blk * B;
   const int64_t tok_stride = a.heads * ROWB;                    // bytes between tokens
   const unsigned char* xb = (const unsigned char*)a.x + (row0 * a.heads + h) * ROWB;
+  const int8_t* sg = a.signs ? a.signs + h * R : nullptr;
 
-  // 1. coalesced tile load -> LDS
+  // 1. coalesced tile load -> LDS -> one row per thread
 #pragma unroll
   for (int k = 0; k < CPR; ++k) {
     const int q = tid + k * B;
@@ -90,37 +231,30 @@ __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t n
     *(u32x4*)(stage + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = v;
   }
   __syncthreads();
-  float y[R];
+  uint32_t wv[R / 2];
 #pragma unroll
   for (int cc = 0; cc < CPR; ++cc) {
     const u32x4 v = *(const u32x4*)(stage + tid * ROWB + swz_chunk(tid, cc, ROWB) * 16);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      y[8 * cc + 2 * j] = lo_f32<DT>(wv[j]);
-      y[8 * cc + 2 * j + 1] = hi_f32<DT>(wv[j]);
-    }
+    wv[4 * cc] = v.x; wv[4 * cc + 1] = v.y; wv[4 * cc + 2] = v.z; wv[4 * cc + 3] = v.w;
   }
   __syncthreads();   // the staging buffer is free from here on
 
-  // 2. randomized Hadamard rotation (orthonormal)
-  if (a.lg_had) {
-    apply_signs<R>(y, a.signs + h * R);
-    fwht_blocks<R>(y, a.lg_had);
-#pragma unroll
-    for (int i = 0; i < R; ++i) y[i] *= a.inv_sqrt_n;
-  }
-
-  // 3. norm separation
+  // 2. norm of the input (= norm of the rotated vector), then the unnormalized rotation
+  float inv_nu = 1.f, nu = 0.f;
   if (a.nsep) {
-    const float nu = sqrtf(sum_squares<R>(y));
-    const float inv_nu = nu > 0.f ? 1.f / nu : 0.f;
+    nu = sqrtf(sum_squares_in<DT, R>(wv));
+    inv_nu = nu > 0.f ? 1.f / nu : 0.f;
     a.norms[(row0 + tid) * a.heads + h] = (uint16_t)f32_to_f16(nu);
+  }
+  float y[R];
+  widen_stage1<DT, R>(y, wv, sg, LG != 0);
+  fwht_rest<R, LG>(y);
+  if (a.nsep) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) y[i] *= inv_nu;
+    for (int i = 0; i < R; ++i) y[i] *= inv_nu;                // u, up to the common 1/sqrt(n)
   }
 
-  // 4. per-channel absmax over the B tokens: each wave transposes 16 channels at a time
+  // 3. per-channel absmax over the B tokens: each wave transposes 16 channels at a time
   //    through a 4 KiB LDS scratch (64 tokens x 16 fp32), reduces 16 tokens per lane and
   //    finishes across the 4 lane groups with two lane shuffles.
   float* scr = (float*)(stage + w * 4096);
@@ -149,25 +283,49 @@ __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t n
     float m = colmax[c];
     for (int ww = 1; ww < nw; ++ww) m = fmaxf(m, colmax[ww * R + c]);
     invs[c] = m > 0.f ? a.q / m : 0.f;
-    a.scales[(sb * a.heads + h) * R + c] = (uint16_t)f32_to_f16(m / a.q);
+    a.scales[(sb * a.heads + h) * R + c] = (uint16_t)f32_to_f16(m * a.scale_mul);
   }
+  if (tid < R / 32) fmask[tid] = 0u;
   __syncthreads();
 
-  // 5. codes, staged through LDS for coalesced 16-byte stores
-  uint32_t cw[R / 8];
-#pragma unroll
-  for (int i = 0; i < R / 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) word |= code_nibble(y[8 * i + e], invs[8 * i + e], a.q) << (4 * e);
-    cw[i] = word;
-  }
+  // 4. codes (+ near-tie flags), staged through LDS for coalesced 16-byte stores
+  uint32_t cw[R / 8], chm[R / 32];
+  quantize_row<R, true>(y, [&](int c) { return invs[c]; }, cw, chm);
 #pragma unroll
   for (int cc = 0; cc < CCR; ++cc) {
     const u32x4 v = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
     *(u32x4*)(stage + tid * CRB + swz_chunk(tid, cc, CRB) * 16) = v;
   }
+  uint32_t anych = 0u;
+#pragma unroll
+  for (int g = 0; g < R / 32; ++g) {
+    anych |= chm[g];
+    if (lane == 0 && chm[g]) atomicOr(&fmask[g], chm[g]);
+  }
+
+  // 5. rare path: re-decide the codes of channels holding a near-tie exactly, in fp64
+  if (__syncthreads_or(anych != 0u)) {
+    __syncthreads();
+    const unsigned char* xrow = xb + tid * tok_stride;
+    const double nu64 = a.nsep ? sqrt(exact_sumsq64<DT, R>(xrow)) : 1.0;
+    for (int g = 0; g < R / 32; ++g) {
+      uint32_t bits = fmask[g];
+      while (bits) {
+        const int c = 32 * g + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        const double wv64 = nu64 > 0.0 ? exact_rot64<DT>(xrow, sg, c, LG) / nu64 : 0.0;
+        if (tid == 0) *m64 = 0ull;
+        __syncthreads();
+        atomicMax(m64, __builtin_bit_cast(unsigned long long, fabs(wv64)));
+        __syncthreads();
+        const double mm = __builtin_bit_cast(double, *m64);
+        patch_nibble(stage, tid, CRB, c, mm > 0.0 ? exact_code((double)a.q * wv64 / mm) : 0u);
+        __syncthreads();
+      }
+    }
+  }
   __syncthreads();
+
   unsigned char* cb = a.codes + (row0 * a.heads + h) * CRB;
 #pragma unroll
   for (int k = 0; k < CCR; ++k) {
@@ -181,10 +339,11 @@ __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t n
 // ---------------------------------------------------------------------------------------
 // Per-token modes (NAIVE, NSEP): one wave per 64 consecutive row segments of R channels.
 // A (token, head) vector of D = L * R channels spans L = 2^lgL neighbouring lanes.
-template <int DT, int R>
+template <int DT, int R, int LG>
 __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nseg, int64_t ntiles, int lgL) {
   constexpr int ROWB = R * 2, CPR = ROWB / 16, CRB = R / 2, CCR = CRB / 16;
   __shared__ __attribute__((aligned(16))) unsigned char stage[64 * ROWB];
+  __shared__ double F[R];                                       // exact re-decision workspace
   const int lane = threadIdx.x;
   const int64_t seg0 = xcd_tile(blockIdx.x, ntiles) * 64;
   const int nvalid = (int)(nseg - seg0 < 64 ? nseg - seg0 : 64);
@@ -199,55 +358,90 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     *(u32x4*)(stage + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = v;
   }
   wave_lds_sync();
-  float y[R];
+  uint32_t wv[R / 2];
 #pragma unroll
   for (int cc = 0; cc < CPR; ++cc) {
     const u32x4 v = *(const u32x4*)(stage + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      y[8 * cc + 2 * j] = lo_f32<DT>(wv[j]);
-      y[8 * cc + 2 * j + 1] = hi_f32<DT>(wv[j]);
-    }
+    wv[4 * cc] = v.x; wv[4 * cc + 1] = v.y; wv[4 * cc + 2] = v.z; wv[4 * cc + 3] = v.w;
   }
   const int L = 1 << lgL;
   const int64_t seg = seg0 + lane;
   const int64_t vec = seg >> lgL;
   const int part = (int)(seg & (L - 1));
   const int64_t h = vec % a.heads;
+  const int8_t* sg = a.signs ? a.signs + h * a.dim + part * R : nullptr;
 
-  if (a.lg_had) {
-    apply_signs<R>(y, a.signs + h * a.dim + part * R);
-    fwht_blocks<R>(y, a.lg_had);
-#pragma unroll
-    for (int i = 0; i < R; ++i) y[i] *= a.inv_sqrt_n;
-  }
-  float nu = 0.f;
+  float ss = 0.f;
   if (a.nsep) {
-    float ss = sum_squares<R>(y);
+    ss = sum_squares_in<DT, R>(wv);
     for (int o = 1; o < L; o <<= 1) ss += shfl_xor_f(ss, o);
-    nu = sqrtf(ss);
-    const float inv_nu = nu > 0.f ? 1.f / nu : 0.f;
-#pragma unroll
-    for (int i = 0; i < R; ++i) y[i] *= inv_nu;
   }
-  float m = abs_max<R>(y);
+  float y[R];
+  widen_stage1<DT, R>(y, wv, sg, LG != 0);
+  fwht_rest<R, LG>(y);
+  float m = 0.f;
+  {
+    float mm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < R; ++i) mm[i & 3] = fmaxf(mm[i & 3], fabsf(y[i]));
+    m = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
+  }
   for (int o = 1; o < L; o <<= 1) m = fmaxf(m, shfl_xor_f(m, o));
   const float inv_scale = m > 0.f ? a.q / m : 0.f;
 
-  uint32_t cw[R / 8];
-#pragma unroll
-  for (int i = 0; i < R / 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) word |= code_nibble(y[8 * i + e], inv_scale, a.q) << (4 * e);
-    cw[i] = word;
-  }
+  uint32_t cw[R / 8], chm_unused[R / 32];
+  const bool flagged = quantize_row<R, false>(y, [&](int) { return inv_scale; }, cw, chm_unused);
   wave_lds_sync();   // every lane has read its input row
 #pragma unroll
   for (int cc = 0; cc < CCR; ++cc) {
     const u32x4 v = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
     *(u32x4*)(stage + lane * CRB + swz_chunk(lane, cc, CRB) * 16) = v;
+  }
+
+  // rare path: recompute every code of a vector holding a near-tie, exactly (fp64 transform
+  // in LDS, shared by the wave); v = Q Y_c / max |Y| for both per-token modes.
+  uint64_t ball = __ballot(lane < nvalid && flagged);
+  while (ball) {
+    const int l0 = __builtin_ctzll(ball);
+    const int64_t v0 = (seg0 + l0) >> lgL;
+    const int lane0 = (int)((v0 << lgL) - seg0);
+    ball &= ~((L == 64 ? ~0ull : ((1ull << L) - 1ull)) << lane0);
+    const int64_t hv = v0 % a.heads;
+    double mx = 0.0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int p = 0; p < L; ++p) {
+        const unsigned char* xr = xb + (lane0 + p) * ROWB;
+        const int8_t* sgp = a.signs ? a.signs + hv * a.dim + p * R : nullptr;
+        wave_lds_sync();
+        for (int i = lane; i < R; i += 64) {
+          const uint32_t hb = *(const uint16_t*)(xr + 2 * i);
+          double x = (double)(DT == DT_F16 ? f16_to_f32(hb) : bf16_to_f32(hb));
+          if (sgp && sgp[i] < 0) x = -x;
+          F[i] = x;
+        }
+        for (int st = 0; st < LG; ++st) {
+          wave_lds_sync();
+          for (int pp = lane; pp < R / 2; pp += 64) {
+            const int i = ((pp >> st) << (st + 1)) | (pp & ((1 << st) - 1));
+            const double u = F[i], v = F[i + (1 << st)];
+            F[i] = u + v;
+            F[i + (1 << st)] = u - v;
+          }
+        }
+        wave_lds_sync();
+        if (pass == 0) {
+          for (int i = lane; i < R; i += 64) mx = fmax(mx, fabs(F[i]));
+        } else if (lane < R / 2) {
+          const uint32_t lo = mx > 0.0 ? exact_code((double)a.q * F[2 * lane] / mx) : 0u;
+          const uint32_t hi = mx > 0.0 ? exact_code((double)a.q * F[2 * lane + 1] / mx) : 0u;
+          const int row = lane0 + p;
+          stage[row * CRB + swz_chunk(row, lane >> 4, CRB) * 16 + (lane & 15)] = (unsigned char)(lo | (hi << 4));
+        }
+      }
+      if (pass == 0) {
+        for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+      }
+    }
   }
   wave_lds_sync();
   unsigned char* cb = a.codes + seg0 * CRB;
@@ -261,46 +455,70 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     }
   }
   if (part == 0 && lane < nvalid) {
+    const float nu = sqrtf(ss);
     if (a.nsep) a.norms[vec] = (uint16_t)f32_to_f16(nu);
-    a.scales[vec] = (uint16_t)f32_to_f16(m / a.q);
+    const float scale = a.nsep ? (nu > 0.f ? m * a.scale_mul / nu : 0.f) : m * a.scale_mul;
+    a.scales[vec] = (uint16_t)f32_to_f16(scale);
   }
 }
 
 // ---------------------------------------------------------------------------------------
-template <int DT>
-static hipError_t launch_pchan_dt(const QuantArgs& a, hipStream_t st) {
+template <int DT, int R, int LG>
+static void launch_pchan_k(const QuantArgs& a, hipStream_t st) {
   const int64_t ntiles = a.seqs * (a.tokens / a.block) * a.heads;
   const int nw = a.block / 64;
-  if (a.dim == 128) {
-    const size_t lds = (size_t)a.block * 256 + (size_t)nw * 128 * 4 + 128 * 4;
-    hipLaunchKernelGGL((quant_pchan_kernel<DT, 128>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
-  } else {
-    const size_t lds = (size_t)a.block * 128 + (size_t)nw * 64 * 4 + 64 * 4;
-    hipLaunchKernelGGL((quant_pchan_kernel<DT, 64>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
+  const size_t lds = (size_t)a.block * R * 2 + (size_t)nw * R * 4 + R * 4 + 16 + 8;
+  hipLaunchKernelGGL((quant_pchan_kernel<DT, R, LG>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
+}
+
+template <int DT, int R, int LG>
+static void launch_ptok_k(const QuantArgs& a, hipStream_t st, int64_t nseg, int lgL) {
+  const int64_t ntiles = (nseg + 63) / 64;
+  hipLaunchKernelGGL((quant_ptok_kernel<DT, R, LG>), dim3((unsigned)ntiles), dim3(64), 0, st, a, nseg, ntiles, lgL);
+}
+
+// compile-time Hadamard size: LG = log2(n) in {0 (none), 4, 5, 6, 7}
+template <int DT, int R, template <int, int, int> class K, typename... Args>
+static void by_lg(int lg, Args&&... args) {
+  switch (lg) {
+    case 0: K<DT, R, 0>::run(args...); break;
+    case 4: K<DT, R, 4>::run(args...); break;
+    case 5: K<DT, R, 5>::run(args...); break;
+    case 6: K<DT, R, 6>::run(args...); break;
+    default: if constexpr (R >= 128) K<DT, R, 7>::run(args...); break;
   }
-  return hipGetLastError();
+}
+template <int DT, int R, int LG> struct PchanK {
+  static void run(const QuantArgs& a, hipStream_t st) { launch_pchan_k<DT, R, LG>(a, st); }
+};
+template <int DT, int R, int LG> struct PtokK {
+  static void run(const QuantArgs& a, hipStream_t st, int64_t nseg, int lgL) { launch_ptok_k<DT, R, LG>(a, st, nseg, lgL); }
+};
+
+template <int DT>
+static void pchan_dt(const QuantArgs& a, hipStream_t st) {
+  if (a.dim == 128) by_lg<DT, 128, PchanK>(a.lg_had, a, st);
+  else by_lg<DT, 64, PchanK>(a.lg_had, a, st);
 }
 
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t st) {
-  return a.dtype == DT_F16 ? launch_pchan_dt<DT_F16>(a, st) : launch_pchan_dt<DT_BF16>(a, st);
+  if (a.dtype == DT_F16) pchan_dt<DT_F16>(a, st); else pchan_dt<DT_BF16>(a, st);
+  return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t launch_ptok_dt(const QuantArgs& a, hipStream_t st) {
+static void ptok_dt(const QuantArgs& a, hipStream_t st) {
   const int R = a.dim >= 128 ? 128 : 64;
   int lgL = 0;
   while ((R << lgL) < a.dim) ++lgL;
   const int64_t nseg = a.seqs * a.tokens * a.heads * (a.dim / R);
-  const int64_t ntiles = (nseg + 63) / 64;
-  if (R == 128)
-    hipLaunchKernelGGL((quant_ptok_kernel<DT, 128>), dim3((unsigned)ntiles), dim3(64), 0, st, a, nseg, ntiles, lgL);
-  else
-    hipLaunchKernelGGL((quant_ptok_kernel<DT, 64>), dim3((unsigned)ntiles), dim3(64), 0, st, a, nseg, ntiles, lgL);
-  return hipGetLastError();
+  if (R == 128) by_lg<DT, 128, PtokK>(a.lg_had, a, st, nseg, lgL);
+  else by_lg<DT, 64, PtokK>(a.lg_had, a, st, nseg, lgL);
 }
 
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t st) {
-  return a.dtype == DT_F16 ? launch_ptok_dt<DT_F16>(a, st) : launch_ptok_dt<DT_BF16>(a, st);
+  if (a.dtype == DT_F16) ptok_dt<DT_F16>(a, st); else ptok_dt<DT_BF16>(a, st);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -55,3 +55,28 @@ def make(bits, mode, hadamard, head_dim=64, seqs=2, tokens=128, heads=2, seed=0)
     assert np.all(np.abs(x) < 60000)
     assert np.all(x.astype(np.float16).astype(np.float64) == x), "grid input not fp16-exact"
     return spec, x, signs, k.astype(np.int8)
+
+
+def all_ties(had, seed=0, T=128, H=2, D=64):
+    """Every quotient an exact half-integer (or +-7): tokens are signed permutations of one
+    multiset {7, half-integers} with the 7 in channel (t mod D), so all norms are equal and every
+    per-token and per-channel max is 7 * 2^p.  With a rotation of size 16 the input is
+    sigma * H y / 4 of such a y (exact in fp16)."""
+    rng = np.random.default_rng(seed)
+    halves = rng.choice(np.arange(0.5, 7.0, 1.0), size=D - 1)
+    y = np.zeros((T, H, D))
+    for t in range(T):
+        for h in range(H):
+            vals = np.concatenate([[7.0], rng.permutation(halves)]) * rng.choice([-1, 1], size=D)
+            pos = np.concatenate([[t % D], rng.permutation(np.delete(np.arange(D), t % D))])
+            y[t, h, pos] = vals
+    y *= 2.0 ** -2
+    want = np.vectorize(lambda v: round(v))(y * 4.0).astype(np.int8)   # half-even, independent
+    signs = None
+    x = y
+    if had:
+        signs = rng.choice(np.array([-1, 1], np.int8), size=(H, D))
+        Hm = scipy.linalg.hadamard(had).astype(np.float64)
+        x = (y.reshape(T, H, D // had, had) @ Hm.T / np.sqrt(had)).reshape(T, H, D) * signs[None]
+    assert np.all(x.astype(np.float16).astype(np.float64) == x)
+    return x, signs, want

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from activation_quantization_amd import kvq, synth
-from tests import parity
+from tests import grid, parity
 from tests.test_gpu_parity import DEV, run_full
 
 pytestmark = pytest.mark.gpu
@@ -115,3 +115,18 @@ def test_tie_flip_rate_report():
     stats, _ = run_full(d, synth.make_x(w), synth.make_signs(w), deq=False)
     print("tie flips", stats, "rate", stats["tie_flips"] / stats["codes"])
     assert stats["tie_flips"] <= parity.tie_budget(stats["codes"])
+
+
+@pytest.mark.parametrize("had", [0, 16])
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_exact_ties_are_rounded_half_even(mode, had):
+    x64, signs, want = grid.all_ties(had)
+    d = kvq.Desc(1, 128, 2, 64, 4, mode, 64 if "pchan" in mode else 0, had, torch.float16)
+    sg = None if signs is None else torch.from_numpy(signs).to(DEV)
+    codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).half().to(DEV), sg)
+    torch.cuda.synchronize()
+    got = oracle.unpack_nibbles(codes.cpu().numpy())
+    np.testing.assert_array_equal(got, want)
+    # and the oracle agrees (its own decision in fp32 of the fp64 quotient)
+    sp = oracle.Spec(1, 128, 2, 64, 4, mode, d.block_tokens if "pchan" in mode else 0, had)
+    np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)

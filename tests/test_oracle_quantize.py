@@ -134,3 +134,12 @@ def test_dequant_error_within_half_step(mode):
     stored = oracle.expand_scales(q.scales16, sp) * (q.norms16.astype(np.float64)[..., None] if sp.nsep else 1.0)
     bound = 0.5 * step + np.abs(q.codes) * np.abs(stored - step) + 1e-12
     assert np.all(np.abs(yh - y) <= bound)
+
+
+@pytest.mark.parametrize("had", [0, 16])
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_all_ties_round_half_even(mode, had):
+    # every quotient an exact half-integer: codes must be Python's half-even round() of it
+    x, signs, want = grid.all_ties(had)
+    sp = Spec(1, 128, 2, 64, 4, mode, 64 if "pchan" in mode else 0, had)
+    np.testing.assert_array_equal(oracle.quantize(x, sp, signs).codes, want)
