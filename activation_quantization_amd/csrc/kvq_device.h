@@ -65,11 +65,21 @@ __device__ __forceinline__ int swz_chunk(int row, int cc, int row_bytes) {
 }
 
 // ------------------------------------------------------------------ wave helpers
+// Orders this wave's LDS accesses.  LDS executes one wave's instructions in order, so only
+// the compiler must be kept from reordering; no memory fence (a fence would also wait for
+// every global access in flight, the asynchronous tile prefetch included).
 __device__ __forceinline__ void wave_lds_sync() {
-  // orders this wave's LDS accesses (LDS executes one wave's instructions in order)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations, then s_barrier.
+// Global loads in flight (the prefetch into a different LDS array) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ float shfl_xor_f(float v, int m) {
   const int lane = __lane_id();

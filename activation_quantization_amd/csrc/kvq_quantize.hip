@@ -35,11 +35,19 @@ constexpr float MAGIC = 192.5f;   // [128, 256): ulp 2^-16; + 0.5 turns truncati
 template <int DT> __device__ __forceinline__ uint32_t one_pair() {
   return DT == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
 }
-template <int DT> __device__ __forceinline__ float dot2(uint32_t x, uint32_t c) {
-  if constexpr (DT == DT_F16)
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, c), 0.f, false);
-  else
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, c), 0.f, false);
+// x.lo * c.lo + x.hi * c.hi in fp32 (NEG_HI: x.lo * c.lo - x.hi * c.hi).  VOP3 form with a
+// literal zero accumulator: the builtin selects the accumulate-in-place encoding, which needs
+// an extra register clear per use.
+template <int DT, bool NEG_HI = false> __device__ __forceinline__ float dot2(uint32_t x, uint32_t c) {
+  float r;
+  if constexpr (DT == DT_F16) {
+    if constexpr (NEG_HI) asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(c));
+    else asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(c));
+  } else {
+    if constexpr (NEG_HI) asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(c));
+    else asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(c));
+  }
+  return r;
 }
 template <int DT> __device__ __forceinline__ float dot2acc(uint32_t x, float acc) {
   if constexpr (DT == DT_F16)
@@ -56,7 +64,9 @@ __device__ __forceinline__ void widen_stage1(float (&y)[R], const uint32_t (&w)[
   if (rotate) {
 #pragma unroll
     for (int c = 0; c < R / 16; ++c) {
-      const u32x4 sv = *(const u32x4*)(sg + 16 * c);
+      // wave-uniform: read through the constant address space so it becomes a scalar load
+      // (lgkmcnt), which does not wait behind the tile prefetch in flight on vmcnt
+      const u32x4 sv = *(const __attribute__((address_space(4))) u32x4*)(sg + 16 * c);
       const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {           // pair k of this 16-channel group
@@ -66,7 +76,7 @@ __device__ __forceinline__ void widen_stage1(float (&y)[R], const uint32_t (&w)[
         const uint32_t cp = one_pair<DT>() | sb;
         const int i = 8 * c + k;
         y[2 * i] = dot2<DT>(w[i], cp);
-        y[2 * i + 1] = dot2<DT>(w[i], cp ^ 0x80000000u);
+        y[2 * i + 1] = dot2<DT, true>(w[i], cp);
       }
     }
   } else {
@@ -75,6 +85,32 @@ __device__ __forceinline__ void widen_stage1(float (&y)[R], const uint32_t (&w)[
       y[2 * i] = lo_f32<DT>(w[i]);
       y[2 * i + 1] = hi_f32<DT>(w[i]);
     }
+  }
+}
+
+// Per-lane signs (per-token kernel): flip the sign bits of the packed inputs right after
+// they are loaded (v_perm moves sign byte k's bit 7 to bit 15 / 31 of its pair).
+template <int R>
+__device__ __forceinline__ void apply_signs_packed(uint32_t (&w)[R / 2], const int8_t* __restrict__ sg) {
+#pragma unroll
+  for (int c = 0; c < R / 16; ++c) {
+    const u32x4 sv = *(const u32x4*)(sg + 16 * c);
+    const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t sw = s4[k >> 1];
+      const uint32_t m = __builtin_amdgcn_perm(0u, sw, (k & 1) ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u;
+      w[8 * c + k] ^= m;
+    }
+  }
+}
+
+template <int DT, int R>
+__device__ __forceinline__ void stage1_unsigned(float (&y)[R], const uint32_t (&w)[R / 2]) {
+#pragma unroll
+  for (int i = 0; i < R / 2; ++i) {
+    y[2 * i] = dot2<DT>(w[i], one_pair<DT>());
+    y[2 * i + 1] = dot2<DT, true>(w[i], one_pair<DT>());
   }
 }
 
@@ -127,7 +163,7 @@ __device__ __forceinline__ bool quantize_row(const float (&u)[R], InvF inv, uint
       } else {
         f = f | fe | fo;
       }
-      p[k] = (be & 0x000F0000u) | ((bo << 4) & 0x00F00000u);   // byte 2 = code pair
+      p[k] = (be & 0x000F0000u) | ((bo << 4) & ~0x000F0000u);   // byte 2 = code pair (v_bfi)
     }
     const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0C0C0602u);
     const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x06020C0Cu);
@@ -141,13 +177,14 @@ __device__ __forceinline__ bool quantize_row(const float (&u)[R], InvF inv, uint
 // Y_c = sum over c's n-block of (-1)^popcount(c & j) s_j x_j.  Exact for fp16 inputs (the sum
 // of 128 fp16 values fits in 53 bits).
 template <int DT>
-__device__ double exact_rot64(const unsigned char* __restrict__ row, const int8_t* __restrict__ sg, int c, int lg) {
+__device__ __attribute__((noinline)) double exact_rot64(const unsigned char* __restrict__ row, const int8_t* __restrict__ sg, int c, int lg) {
   if (lg == 0) {
     const uint32_t h = *(const uint16_t*)(row + 2 * c);
     return (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
   }
   const int n = 1 << lg, base = (c >> lg) << lg;
   double acc = 0.0;
+#pragma unroll 1
   for (int j0 = base; j0 < base + n; j0 += 8) {
     const u32x4 v = *(const u32x4*)(row + 2 * j0);
     const u32x2 s8 = *(const u32x2*)(sg + j0);
@@ -166,8 +203,9 @@ __device__ double exact_rot64(const unsigned char* __restrict__ row, const int8_
 }
 
 template <int DT, int R>
-__device__ double exact_sumsq64(const unsigned char* __restrict__ row) {
+__device__ __attribute__((noinline)) double exact_sumsq64(const unsigned char* __restrict__ row) {
   double acc = 0.0;
+#pragma unroll 1
   for (int j0 = 0; j0 < R; j0 += 8) {
     const u32x4 v = *(const u32x4*)(row + 2 * j0);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -195,212 +233,204 @@ __device__ __forceinline__ void patch_nibble(unsigned char* stage, int row, int 
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-channel modes (PCHAN, NSEP_PCHAN): one workgroup of B threads per (sequence, token
-// block, head) tile; thread t owns token t of the block.
-template <int DT, int R, int LG>
+// Asynchronous tile load straight into LDS (global_load_lds_dwordx4: no VGPRs, completes in
+// the background).  One wave instruction fills 1 KiB of LDS, lane i at +16 i; lane i fetches
+// the global chunk that the XOR swizzle places there.  `rows` rows of ROWB bytes, row r at
+// src + r * stride; the calling wave handles instructions w, w + nw, ...
+template <int ROWB>
+__device__ __forceinline__ void load_tile_lds(unsigned char* lds, const unsigned char* src, int64_t stride, int rows,
+                                              int w, int nw, int lane) {
+  constexpr int CPR = ROWB / 16;
+  const int ninst = rows * CPR / 64;
+  for (int k = w; k < ninst; k += nw) {
+    const int p = k * 64 + lane;
+    const int row = p / CPR, ccp = p % CPR;
+    const int cc = swz_chunk(row, ccp, ROWB);   // the XOR swizzle is an involution
+    __builtin_amdgcn_global_load_lds((const void*)(src + row * stride + cc * 16),
+                                     (__attribute__((address_space(3))) void*)(lds + k * 1024), 16, 0, 0);
+  }
+}
+
+// Per-channel modes (PCHAN, NSEP_PCHAN): persistent workgroups of B = 64 NW threads; each
+// tile is one (sequence, token block, head) and thread t owns token t of the block.  Pipeline
+// per iteration: wait for this tile's input (prefetched into LDS) -> rows to registers ->
+// store the previous tile's codes -> prefetch the next tile -> compute.  All barriers are
+// LDS-only, so nothing waits on the prefetch until the next iteration needs it.
+template <int DT, int R, int LG, int NW>
 __global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t ntiles) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int B = 64 * NW;
   constexpr int ROWB = R * 2;        // input row bytes
   constexpr int CPR = ROWB / 16;     // input 16-byte chunks per row
   constexpr int CRB = R / 2;         // code row bytes
   constexpr int CCR = CRB / 16;      // code chunks per row
-  const int B = a.block;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = B >> 6;
-  unsigned char* stage = smem;                                  // B * ROWB
-  float* colmax = (float*)(smem + (size_t)B * ROWB);           // nw * R
-  float* invs = colmax + nw * R;                                // R
-  uint32_t* fmask = (uint32_t*)(invs + R);                      // R / 32 flagged-channel bits
-  unsigned long long* m64 = (unsigned long long*)(fmask + 4);   // exact channel max (bits)
+  __shared__ __attribute__((aligned(16))) unsigned char stage_in[B * ROWB];
+  __shared__ __attribute__((aligned(16))) float scr_all[NW * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_codes[B * CRB];
+  __shared__ float colmax[NW * R];
+  __shared__ float invs[R];
+  __shared__ uint32_t fmask[R / 32];
+  __shared__ uint32_t wave_any[NW];
+  __shared__ unsigned long long m64;
 
-  const int64_t tile = xcd_tile(blockIdx.x, ntiles);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t nb = a.tokens / B;
-  const int64_t h = tile % a.heads;
-  const int64_t sb = tile / a.heads;                            // seq * nb + block
-  const int64_t s = sb / nb, blk = sb - s * nb;
-  const int64_t row0 = s * a.tokens + blk * B;
   const int64_t tok_stride = a.heads * ROWB;                    // bytes between tokens
-  const unsigned char* xb = (const unsigned char*)a.x + (row0 * a.heads + h) * ROWB;
-  const int8_t* sg = a.signs ? a.signs + h * R : nullptr;
-
-  // 1. coalesced tile load -> LDS -> one row per thread
+  const int64_t G = gridDim.x;
+  auto tile_of = [&](int64_t v, int64_t& h, int64_t& sb, int64_t& row0) {
+    const int64_t tile = xcd_tile(v, ntiles);
+    h = tile % a.heads;
+    sb = tile / a.heads;                                        // seq * nb + block
+    const int64_t s = sb / nb, blk = sb - s * nb;
+    row0 = s * a.tokens + blk * B;
+  };
+  auto store_codes = [&](int64_t h, int64_t row0) {
+    unsigned char* cb = a.codes + (row0 * a.heads + h) * CRB;
 #pragma unroll
-  for (int k = 0; k < CPR; ++k) {
-    const int q = tid + k * B;
-    const int row = q / CPR, cc = q % CPR;
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(xb + row * tok_stride + cc * 16));
-    *(u32x4*)(stage + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = v;
-  }
-  __syncthreads();
-  uint32_t wv[R / 2];
-#pragma unroll
-  for (int cc = 0; cc < CPR; ++cc) {
-    const u32x4 v = *(const u32x4*)(stage + tid * ROWB + swz_chunk(tid, cc, ROWB) * 16);
-    wv[4 * cc] = v.x; wv[4 * cc + 1] = v.y; wv[4 * cc + 2] = v.z; wv[4 * cc + 3] = v.w;
-  }
-  __syncthreads();   // the staging buffer is free from here on
-
-  // 2. norm of the input (= norm of the rotated vector), then the unnormalized rotation
-  float inv_nu = 1.f, nu = 0.f;
-  if (a.nsep) {
-    nu = sqrtf(sum_squares_in<DT, R>(wv));
-    inv_nu = nu > 0.f ? 1.f / nu : 0.f;
-    a.norms[(row0 + tid) * a.heads + h] = (uint16_t)f32_to_f16(nu);
-  }
-  float y[R];
-  widen_stage1<DT, R>(y, wv, sg, LG != 0);
-  fwht_rest<R, LG>(y);
-  if (a.nsep) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) y[i] *= inv_nu;                // u, up to the common 1/sqrt(n)
-  }
-
-  // 3. per-channel absmax over the B tokens: each wave transposes 16 channels at a time
-  //    through a 4 KiB LDS scratch (64 tokens x 16 fp32), reduces 16 tokens per lane and
-  //    finishes across the 4 lane groups with two lane shuffles.
-  float* scr = (float*)(stage + w * 4096);
-  const int ch = lane & 15, grp = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < R / 16; ++j) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const f32x4 v = {y[16 * j + 4 * jj], y[16 * j + 4 * jj + 1], y[16 * j + 4 * jj + 2], y[16 * j + 4 * jj + 3]};
-      *(f32x4*)(scr + lane * 16 + 4 * (jj ^ ((lane >> 2) & 3))) = v;
+    for (int k = 0; k < CCR; ++k) {
+      const int q = tid + k * B;
+      const int row = q / CCR, cc = q % CCR;
+      const u32x4 cv = *(const u32x4*)(stage_codes + row * CRB + swz_chunk(row, cc, CRB) * 16);
+      __builtin_nontemporal_store(cv, (u32x4*)(cb + (int64_t)row * a.heads * CRB + cc * 16));
     }
-    wave_lds_sync();
-    float m = 0.f;
+  };
+
+  int64_t v = blockIdx.x;
+  int64_t ph = -1, prow0 = 0;                                   // previous tile (codes staged)
+  if (v < ntiles) {
+    int64_t h, sb, row0;
+    tile_of(v, h, sb, row0);
+    load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + (row0 * a.heads + h) * ROWB, tok_stride, B, w, NW, lane);
+  }
+  for (; v < ntiles; v += G) {
+    int64_t h, sb, row0;
+    tile_of(v, h, sb, row0);
+    const unsigned char* xb = (const unsigned char*)a.x + (row0 * a.heads + h) * ROWB;
+    const int8_t* sg = a.signs ? a.signs + h * R : nullptr;
+
+    // 1. this tile's rows -> registers; previous tile's codes -> HBM; prefetch the next tile
+    __builtin_amdgcn_s_waitcnt(0x0070);                         // vmcnt(0): the prefetch landed
+    lds_barrier();
+    uint32_t wv[R / 2];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int t = 4 * k + grp;   // (t >> 2) & 3 == k & 3
-      m = fmaxf(m, fabsf(scr[t * 16 + 4 * ((ch >> 2) ^ (k & 3)) + (ch & 3)]));
+    for (int cc = 0; cc < CPR; ++cc) {
+      const u32x4 q = *(const u32x4*)(stage_in + tid * ROWB + swz_chunk(tid, cc, ROWB) * 16);
+      wv[4 * cc] = q.x; wv[4 * cc + 1] = q.y; wv[4 * cc + 2] = q.z; wv[4 * cc + 3] = q.w;
     }
-    m = fmaxf(m, shfl_xor_f(m, 16));
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    if (lane < 16) colmax[w * R + 16 * j + lane] = m;
-    wave_lds_sync();
-  }
-  __syncthreads();
-  for (int c = tid; c < R; c += B) {
-    float m = colmax[c];
-    for (int ww = 1; ww < nw; ++ww) m = fmaxf(m, colmax[ww * R + c]);
-    invs[c] = m > 0.f ? a.q / m : 0.f;
-    a.scales[(sb * a.heads + h) * R + c] = (uint16_t)f32_to_f16(m * a.scale_mul);
-  }
-  if (tid < R / 32) fmask[tid] = 0u;
-  __syncthreads();
+    lds_barrier();
+    if (ph >= 0) store_codes(ph, prow0);
+    if (v + G < ntiles) {
+      int64_t h2, sb2, r2;
+      tile_of(v + G, h2, sb2, r2);
+      load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + (r2 * a.heads + h2) * ROWB, tok_stride, B, w, NW, lane);
+    }
 
-  // 4. codes (+ near-tie flags), staged through LDS for coalesced 16-byte stores
-  uint32_t cw[R / 8], chm[R / 32];
-  quantize_row<R, true>(y, [&](int c) { return invs[c]; }, cw, chm);
+    // 2. norm of the input (= norm of the rotated vector), then the unnormalized rotation
+    float inv_nu = 1.f;
+    if (a.nsep) {
+      const float nu = sqrtf(sum_squares_in<DT, R>(wv));
+      inv_nu = nu > 0.f ? 1.f / nu : 0.f;
+      a.norms[(row0 + tid) * a.heads + h] = (uint16_t)f32_to_f16(nu);
+    }
+    float y[R];
+    widen_stage1<DT, R>(y, wv, sg, LG != 0);
+    fwht_rest<R, LG>(y);
+    if (a.nsep) {
 #pragma unroll
-  for (int cc = 0; cc < CCR; ++cc) {
-    const u32x4 v = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
-    *(u32x4*)(stage + tid * CRB + swz_chunk(tid, cc, CRB) * 16) = v;
-  }
-  uint32_t anych = 0u;
-#pragma unroll
-  for (int g = 0; g < R / 32; ++g) {
-    anych |= chm[g];
-    if (lane == 0 && chm[g]) atomicOr(&fmask[g], chm[g]);
-  }
+      for (int i = 0; i < R; ++i) y[i] *= inv_nu;              // u, up to the common 1/sqrt(n)
+    }
 
-  // 5. rare path: re-decide the codes of channels holding a near-tie exactly, in fp64
-  if (__syncthreads_or(anych != 0u)) {
-    __syncthreads();
-    const unsigned char* xrow = xb + tid * tok_stride;
-    const double nu64 = a.nsep ? sqrt(exact_sumsq64<DT, R>(xrow)) : 1.0;
+    // 3. per-channel absmax over the B tokens: each wave transposes 16 channels at a time
+    //    through a 4 KiB LDS scratch (64 tokens x 16 fp32), reduces 16 tokens per lane and
+    //    finishes across the 4 lane groups with two lane shuffles.
+    float* scr = scr_all + w * 1024;
+    const int ch = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < R / 16; ++j) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 q = {y[16 * j + 4 * jj], y[16 * j + 4 * jj + 1], y[16 * j + 4 * jj + 2], y[16 * j + 4 * jj + 3]};
+        *(f32x4*)(scr + lane * 16 + 4 * (jj ^ ((lane >> 2) & 3))) = q;
+      }
+      wave_lds_sync();
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int t = 4 * k + grp;   // (t >> 2) & 3 == k & 3
+        m = fmaxf(m, fabsf(scr[t * 16 + 4 * ((ch >> 2) ^ (k & 3)) + (ch & 3)]));
+      }
+      m = fmaxf(m, shfl_xor_f(m, 16));
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      if (lane < 16) colmax[w * R + 16 * j + lane] = m;
+      wave_lds_sync();
+    }
+    lds_barrier();
+    for (int c = tid; c < R; c += B) {
+      float m = colmax[c];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) m = fmaxf(m, colmax[ww * R + c]);
+      invs[c] = m > 0.f ? a.q / m : 0.f;
+      a.scales[(sb * a.heads + h) * R + c] = (uint16_t)f32_to_f16(m * a.scale_mul);
+    }
+    if (tid < R / 32) fmask[tid] = 0u;
+    lds_barrier();
+
+    // 4. codes (+ near-tie flags), staged in LDS; stored at the start of the next iteration
+    uint32_t cw[R / 8], chm[R / 32];
+    quantize_row<R, true>(y, [&](int c) { return invs[c]; }, cw, chm);
+#pragma unroll
+    for (int cc = 0; cc < CCR; ++cc) {
+      const u32x4 q = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
+      *(u32x4*)(stage_codes + tid * CRB + swz_chunk(tid, cc, CRB) * 16) = q;
+    }
+    uint32_t anych = 0u;
+#pragma unroll
     for (int g = 0; g < R / 32; ++g) {
-      uint32_t bits = fmask[g];
-      while (bits) {
-        const int c = 32 * g + __builtin_ctz(bits);
-        bits &= bits - 1u;
-        const double wv64 = nu64 > 0.0 ? exact_rot64<DT>(xrow, sg, c, LG) / nu64 : 0.0;
-        if (tid == 0) *m64 = 0ull;
-        __syncthreads();
-        atomicMax(m64, __builtin_bit_cast(unsigned long long, fabs(wv64)));
-        __syncthreads();
-        const double mm = __builtin_bit_cast(double, *m64);
-        patch_nibble(stage, tid, CRB, c, mm > 0.0 ? exact_code((double)a.q * wv64 / mm) : 0u);
-        __syncthreads();
+      anych |= chm[g];
+      if (lane == 0 && chm[g]) atomicOr(&fmask[g], chm[g]);
+    }
+    if (lane == 0) wave_any[w] = anych;
+    lds_barrier();
+    uint32_t any = 0u;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) any |= wave_any[ww];
+
+    // 5. rare path: re-decide the codes of channels holding a near-tie exactly, in fp64
+    if (any) {
+      const unsigned char* xrow = xb + tid * tok_stride;
+      const double nu64 = a.nsep ? sqrt(exact_sumsq64<DT, R>(xrow)) : 1.0;
+      for (int g = 0; g < R / 32; ++g) {
+        uint32_t bits = fmask[g];
+        while (bits) {
+          const int c = 32 * g + __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const double wv64 = nu64 > 0.0 ? exact_rot64<DT>(xrow, sg, c, LG) / nu64 : 0.0;
+          if (tid == 0) m64 = 0ull;
+          lds_barrier();
+          atomicMax(&m64, __builtin_bit_cast(unsigned long long, fabs(wv64)));
+          lds_barrier();
+          const double mm = __builtin_bit_cast(double, m64);
+          patch_nibble(stage_codes, tid, CRB, c, mm > 0.0 ? exact_code((double)a.q * wv64 / mm) : 0u);
+          lds_barrier();
+        }
       }
     }
+    ph = h;
+    prow0 = row0;
   }
-  __syncthreads();
-
-  unsigned char* cb = a.codes + (row0 * a.heads + h) * CRB;
-#pragma unroll
-  for (int k = 0; k < CCR; ++k) {
-    const int q = tid + k * B;
-    const int row = q / CCR, cc = q % CCR;
-    const u32x4 v = *(const u32x4*)(stage + row * CRB + swz_chunk(row, cc, CRB) * 16);
-    __builtin_nontemporal_store(v, (u32x4*)(cb + (int64_t)row * a.heads * CRB + cc * 16));
+  if (ph >= 0) {
+    lds_barrier();
+    store_codes(ph, prow0);
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// Per-token modes (NAIVE, NSEP): one wave per 64 consecutive row segments of R channels.
-// A (token, head) vector of D = L * R channels spans L = 2^lgL neighbouring lanes.
+// Per-token rare path: every code of each vector holding a near-tie is recomputed exactly
+// (fp64 transform in LDS, shared by the wave); v = Q Y_c / max |Y| for both per-token modes.
 template <int DT, int R, int LG>
-__global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nseg, int64_t ntiles, int lgL) {
-  constexpr int ROWB = R * 2, CPR = ROWB / 16, CRB = R / 2, CCR = CRB / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char stage[64 * ROWB];
-  __shared__ double F[R];                                       // exact re-decision workspace
+__device__ __forceinline__ void ptok_exact(const QuantArgs& a, uint64_t ball, int64_t seg0, int lgL,
+                                                     const unsigned char* xb, unsigned char* stage_codes, double* F) {
+  constexpr int ROWB = R * 2, CRB = R / 2;
   const int lane = threadIdx.x;
-  const int64_t seg0 = xcd_tile(blockIdx.x, ntiles) * 64;
-  const int nvalid = (int)(nseg - seg0 < 64 ? nseg - seg0 : 64);
-  const unsigned char* xb = (const unsigned char*)a.x + seg0 * ROWB;
-
-#pragma unroll
-  for (int k = 0; k < CPR; ++k) {
-    const int q = lane + k * 64;
-    const int row = q / CPR, cc = q % CPR;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < nvalid) v = __builtin_nontemporal_load((const u32x4*)(xb + row * ROWB + cc * 16));
-    *(u32x4*)(stage + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = v;
-  }
-  wave_lds_sync();
-  uint32_t wv[R / 2];
-#pragma unroll
-  for (int cc = 0; cc < CPR; ++cc) {
-    const u32x4 v = *(const u32x4*)(stage + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16);
-    wv[4 * cc] = v.x; wv[4 * cc + 1] = v.y; wv[4 * cc + 2] = v.z; wv[4 * cc + 3] = v.w;
-  }
   const int L = 1 << lgL;
-  const int64_t seg = seg0 + lane;
-  const int64_t vec = seg >> lgL;
-  const int part = (int)(seg & (L - 1));
-  const int64_t h = vec % a.heads;
-  const int8_t* sg = a.signs ? a.signs + h * a.dim + part * R : nullptr;
-
-  float ss = 0.f;
-  if (a.nsep) {
-    ss = sum_squares_in<DT, R>(wv);
-    for (int o = 1; o < L; o <<= 1) ss += shfl_xor_f(ss, o);
-  }
-  float y[R];
-  widen_stage1<DT, R>(y, wv, sg, LG != 0);
-  fwht_rest<R, LG>(y);
-  float m = 0.f;
-  {
-    float mm[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < R; ++i) mm[i & 3] = fmaxf(mm[i & 3], fabsf(y[i]));
-    m = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
-  }
-  for (int o = 1; o < L; o <<= 1) m = fmaxf(m, shfl_xor_f(m, o));
-  const float inv_scale = m > 0.f ? a.q / m : 0.f;
-
-  uint32_t cw[R / 8], chm_unused[R / 32];
-  const bool flagged = quantize_row<R, false>(y, [&](int) { return inv_scale; }, cw, chm_unused);
-  wave_lds_sync();   // every lane has read its input row
-#pragma unroll
-  for (int cc = 0; cc < CCR; ++cc) {
-    const u32x4 v = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
-    *(u32x4*)(stage + lane * CRB + swz_chunk(lane, cc, CRB) * 16) = v;
-  }
-
-  // rare path: recompute every code of a vector holding a near-tie, exactly (fp64 transform
-  // in LDS, shared by the wave); v = Q Y_c / max |Y| for both per-token modes.
-  uint64_t ball = __ballot(lane < nvalid && flagged);
   while (ball) {
     const int l0 = __builtin_ctzll(ball);
     const int64_t v0 = (seg0 + l0) >> lgL;
@@ -423,9 +453,9 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
           wave_lds_sync();
           for (int pp = lane; pp < R / 2; pp += 64) {
             const int i = ((pp >> st) << (st + 1)) | (pp & ((1 << st) - 1));
-            const double u = F[i], v = F[i + (1 << st)];
-            F[i] = u + v;
-            F[i + (1 << st)] = u - v;
+            const double u = F[i], w2 = F[i + (1 << st)];
+            F[i] = u + w2;
+            F[i + (1 << st)] = u - w2;
           }
         }
         wave_lds_sync();
@@ -435,7 +465,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
           const uint32_t lo = mx > 0.0 ? exact_code((double)a.q * F[2 * lane] / mx) : 0u;
           const uint32_t hi = mx > 0.0 ? exact_code((double)a.q * F[2 * lane + 1] / mx) : 0u;
           const int row = lane0 + p;
-          stage[row * CRB + swz_chunk(row, lane >> 4, CRB) * 16 + (lane & 15)] = (unsigned char)(lo | (hi << 4));
+          stage_codes[row * CRB + swz_chunk(row, lane >> 4, CRB) * 16 + (lane & 15)] = (unsigned char)(lo | (hi << 4));
         }
       }
       if (pass == 0) {
@@ -443,38 +473,172 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
       }
     }
   }
-  wave_lds_sync();
-  unsigned char* cb = a.codes + seg0 * CRB;
-#pragma unroll
-  for (int k = 0; k < CCR; ++k) {
-    const int q = lane + k * 64;
-    const int row = q / CCR, cc = q % CCR;
-    if (row < nvalid) {
-      const u32x4 v = *(const u32x4*)(stage + row * CRB + swz_chunk(row, cc, CRB) * 16);
-      __builtin_nontemporal_store(v, (u32x4*)(cb + row * CRB + cc * 16));
-    }
-  }
-  if (part == 0 && lane < nvalid) {
-    const float nu = sqrtf(ss);
-    if (a.nsep) a.norms[vec] = (uint16_t)f32_to_f16(nu);
-    const float scale = a.nsep ? (nu > 0.f ? m * a.scale_mul / nu : 0.f) : m * a.scale_mul;
-    a.scales[vec] = (uint16_t)f32_to_f16(scale);
-  }
 }
 
 // ---------------------------------------------------------------------------------------
+// Per-token modes (NAIVE, NSEP): persistent single-wave workgroups; a tile is 64 consecutive
+// row segments of R channels (16 KiB for R = 128), prefetched into LDS one tile ahead.  A
+// (token, head) vector of D = L * R channels spans L = 2^lgL neighbouring lanes.
+template <int DT, int R, int LG>
+__global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nseg, int64_t ntiles, int lgL) {
+  constexpr int ROWB = R * 2, CPR = ROWB / 16, CRB = R / 2, CCR = CRB / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char stage_in[64 * ROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_codes[64 * CRB];
+  __shared__ double F[R];                                       // exact re-decision workspace
+  const int lane = threadIdx.x;
+  const int L = 1 << lgL;
+  const int64_t G = gridDim.x;
+  const int64_t full_tiles = nseg / 64;                         // tiles without a ragged tail
+  auto store_codes = [&](int64_t seg0, int nvalid) {
+    unsigned char* cb = a.codes + seg0 * CRB;
+#pragma unroll
+    for (int k = 0; k < CCR; ++k) {
+      const int q = lane + k * 64;
+      const int row = q / CCR, cc = q % CCR;
+      if (row < nvalid) {
+        const u32x4 t = *(const u32x4*)(stage_codes + row * CRB + swz_chunk(row, cc, CRB) * 16);
+        __builtin_nontemporal_store(t, (u32x4*)(cb + row * CRB + cc * 16));
+      }
+    }
+  };
+
+  // only full tiles are prefetched; the tile order is remapped per XCD, so test the tile
+  // index itself (the ragged last tile is loaded with guarded loads when its turn comes)
+  int64_t v = blockIdx.x;
+  int64_t pseg0 = -1;
+  int pvalid = 0;
+  if (v < ntiles && xcd_tile(v, ntiles) < full_tiles)
+    load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + xcd_tile(v, ntiles) * 64 * ROWB, ROWB, 64, 0, 1, lane);
+  for (; v < ntiles; v += G) {
+    const int64_t seg0 = xcd_tile(v, ntiles) * 64;
+    const int nvalid = (int)(nseg - seg0 < 64 ? nseg - seg0 : 64);
+    const unsigned char* xb = (const unsigned char*)a.x + seg0 * ROWB;
+    if (nvalid < 64) {
+      // ragged last tile: plain guarded loads (no prefetch was issued for it)
+#pragma unroll
+      for (int k = 0; k < CPR; ++k) {
+        const int q = lane + k * 64;
+        const int row = q / CPR, cc = q % CPR;
+        u32x4 t = {0u, 0u, 0u, 0u};
+        if (row < nvalid) t = __builtin_nontemporal_load((const u32x4*)(xb + row * ROWB + cc * 16));
+        *(u32x4*)(stage_in + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = t;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the prefetch landed
+    wave_lds_sync();
+    uint32_t wv[R / 2];
+#pragma unroll
+    for (int cc = 0; cc < CPR; ++cc) {
+      const u32x4 t = *(const u32x4*)(stage_in + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16);
+      wv[4 * cc] = t.x; wv[4 * cc + 1] = t.y; wv[4 * cc + 2] = t.z; wv[4 * cc + 3] = t.w;
+    }
+    wave_lds_sync();
+    const int64_t seg = seg0 + lane;
+    const int64_t vec = seg >> lgL;
+    const int part = (int)(seg & (L - 1));
+    const int64_t h = vec % a.heads;
+    const int8_t* sg = a.signs ? a.signs + h * a.dim + part * R : nullptr;
+    // per-lane signs are vector loads: apply them before the next prefetch is in flight, so
+    // their wait does not include it; then store the previous tile's codes and prefetch
+    if constexpr (LG != 0) apply_signs_packed<R>(wv, sg);
+    if (pseg0 >= 0) store_codes(pseg0, pvalid);
+    if (v + G < ntiles && xcd_tile(v + G, ntiles) < full_tiles)
+      load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + xcd_tile(v + G, ntiles) * 64 * ROWB, ROWB, 64, 0, 1, lane);
+
+    float ss = 0.f;
+    if (a.nsep) {
+      ss = sum_squares_in<DT, R>(wv);
+      for (int o = 1; o < L; o <<= 1) ss += shfl_xor_f(ss, o);
+    }
+    float y[R];
+    if constexpr (LG != 0) {
+      stage1_unsigned<DT, R>(y, wv);
+    } else {
+      widen_stage1<DT, R>(y, wv, nullptr, false);
+    }
+    fwht_rest<R, LG>(y);
+    float m = 0.f;
+    {
+      float mm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < R; ++i) mm[i & 3] = fmaxf(mm[i & 3], fabsf(y[i]));
+      m = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
+    }
+    for (int o = 1; o < L; o <<= 1) m = fmaxf(m, shfl_xor_f(m, o));
+    const float inv_scale = m > 0.f ? a.q / m : 0.f;
+
+    uint32_t cw[R / 8], chm_unused[R / 32];
+    const bool flagged = quantize_row<R, false>(y, [&](int) { return inv_scale; }, cw, chm_unused);
+    wave_lds_sync();   // the previous tile's codes have been read out of stage_codes
+#pragma unroll
+    for (int cc = 0; cc < CCR; ++cc) {
+      const u32x4 t = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
+      *(u32x4*)(stage_codes + lane * CRB + swz_chunk(lane, cc, CRB) * 16) = t;
+    }
+
+    // rare path: recompute every code of a vector holding a near-tie, exactly
+    const uint64_t ball = __ballot(lane < nvalid && flagged);
+    if (ball) ptok_exact<DT, R, LG>(a, ball, seg0, lgL, xb, stage_codes, F);
+    if (part == 0 && lane < nvalid) {
+      const float nu = sqrtf(ss);
+      if (a.nsep) a.norms[vec] = (uint16_t)f32_to_f16(nu);
+      const float scale = a.nsep ? (nu > 0.f ? m * a.scale_mul / nu : 0.f) : m * a.scale_mul;
+      a.scales[vec] = (uint16_t)f32_to_f16(scale);
+    }
+    wave_lds_sync();
+    pseg0 = seg0;
+    pvalid = nvalid;
+  }
+  if (pseg0 >= 0) store_codes(pseg0, pvalid);
+}
+
+}  // namespace kvq
+#include <mutex>
+#include <unordered_map>
+namespace kvq {
+template <typename K>
+static int64_t persistent_grid(K kernel, int threads, int64_t ntiles) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, int64_t> cache;     // (device, kernel) -> resident workgroups
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t key = ((uint64_t)(uintptr_t)(const void*)kernel << 8) ^ (uint64_t)dev;
+  int64_t g;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it == cache.end()) {
+      int cus = 0, per_cu = 0;
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+      if (cus < 8) cus = 8;
+      g = (int64_t)per_cu * cus;
+      g -= g % 8;
+      cache.emplace(key, g);
+    } else {
+      g = it->second;
+    }
+  }
+  return ntiles < g ? ntiles : g;
+}
+
 template <int DT, int R, int LG>
 static void launch_pchan_k(const QuantArgs& a, hipStream_t st) {
   const int64_t ntiles = a.seqs * (a.tokens / a.block) * a.heads;
-  const int nw = a.block / 64;
-  const size_t lds = (size_t)a.block * R * 2 + (size_t)nw * R * 4 + R * 4 + 16 + 8;
-  hipLaunchKernelGGL((quant_pchan_kernel<DT, R, LG>), dim3((unsigned)ntiles), dim3(a.block), lds, st, a, ntiles);
+  auto go = [&](auto kernel) {
+    const int64_t grid = persistent_grid(kernel, a.block, ntiles);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(a.block), 0, st, a, ntiles);
+  };
+  if (a.block == 64) go(quant_pchan_kernel<DT, R, LG, 1>);
+  else if (a.block == 128) go(quant_pchan_kernel<DT, R, LG, 2>);
+  else if constexpr (R == 64) go(quant_pchan_kernel<DT, R, LG, 4>);
 }
 
 template <int DT, int R, int LG>
 static void launch_ptok_k(const QuantArgs& a, hipStream_t st, int64_t nseg, int lgL) {
   const int64_t ntiles = (nseg + 63) / 64;
-  hipLaunchKernelGGL((quant_ptok_kernel<DT, R, LG>), dim3((unsigned)ntiles), dim3(64), 0, st, a, nseg, ntiles, lgL);
+  const int64_t grid = persistent_grid(quant_ptok_kernel<DT, R, LG>, 64, ntiles);
+  hipLaunchKernelGGL((quant_ptok_kernel<DT, R, LG>), dim3((unsigned)grid), dim3(64), 0, st, a, nseg, ntiles, lgL);
 }
 
 // compile-time Hadamard size: LG = log2(n) in {0 (none), 4, 5, 6, 7}
