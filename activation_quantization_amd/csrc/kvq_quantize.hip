@@ -251,178 +251,6 @@ __device__ __forceinline__ void load_tile_lds(unsigned char* lds, const unsigned
   }
 }
 
-// Per-channel modes (PCHAN, NSEP_PCHAN): persistent workgroups of B = 64 NW threads; each
-// tile is one (sequence, token block, head) and thread t owns token t of the block.  Pipeline
-// per iteration: wait for this tile's input (prefetched into LDS) -> rows to registers ->
-// store the previous tile's codes -> prefetch the next tile -> compute.  All barriers are
-// LDS-only, so nothing waits on the prefetch until the next iteration needs it.
-template <int DT, int R, int LG, int NW>
-__global__ void __launch_bounds__(256) quant_pchan_kernel(QuantArgs a, int64_t ntiles) {
-  constexpr int B = 64 * NW;
-  constexpr int ROWB = R * 2;        // input row bytes
-  constexpr int CPR = ROWB / 16;     // input 16-byte chunks per row
-  constexpr int CRB = R / 2;         // code row bytes
-  constexpr int CCR = CRB / 16;      // code chunks per row
-  __shared__ __attribute__((aligned(16))) unsigned char stage_in[B * ROWB];
-  __shared__ __attribute__((aligned(16))) float scr_all[NW * 1024];
-  __shared__ __attribute__((aligned(16))) unsigned char stage_codes[B * CRB];
-  __shared__ float colmax[NW * R];
-  __shared__ float invs[R];
-  __shared__ uint32_t fmask[R / 32];
-  __shared__ uint32_t wave_any[NW];
-  __shared__ unsigned long long m64;
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t nb = a.tokens / B;
-  const int64_t tok_stride = a.heads * ROWB;                    // bytes between tokens
-  const int64_t G = gridDim.x;
-  auto tile_of = [&](int64_t v, int64_t& h, int64_t& sb, int64_t& row0) {
-    const int64_t tile = xcd_tile(v, ntiles);
-    h = tile % a.heads;
-    sb = tile / a.heads;                                        // seq * nb + block
-    const int64_t s = sb / nb, blk = sb - s * nb;
-    row0 = s * a.tokens + blk * B;
-  };
-  auto store_codes = [&](int64_t h, int64_t row0) {
-    unsigned char* cb = a.codes + (row0 * a.heads + h) * CRB;
-#pragma unroll
-    for (int k = 0; k < CCR; ++k) {
-      const int q = tid + k * B;
-      const int row = q / CCR, cc = q % CCR;
-      const u32x4 cv = *(const u32x4*)(stage_codes + row * CRB + swz_chunk(row, cc, CRB) * 16);
-      __builtin_nontemporal_store(cv, (u32x4*)(cb + (int64_t)row * a.heads * CRB + cc * 16));
-    }
-  };
-
-  int64_t v = blockIdx.x;
-  int64_t ph = -1, prow0 = 0;                                   // previous tile (codes staged)
-  if (v < ntiles) {
-    int64_t h, sb, row0;
-    tile_of(v, h, sb, row0);
-    load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + (row0 * a.heads + h) * ROWB, tok_stride, B, w, NW, lane);
-  }
-  for (; v < ntiles; v += G) {
-    int64_t h, sb, row0;
-    tile_of(v, h, sb, row0);
-    const unsigned char* xb = (const unsigned char*)a.x + (row0 * a.heads + h) * ROWB;
-    const int8_t* sg = a.signs ? a.signs + h * R : nullptr;
-
-    // 1. this tile's rows -> registers; previous tile's codes -> HBM; prefetch the next tile
-    __builtin_amdgcn_s_waitcnt(0x0070);                         // vmcnt(0): the prefetch landed
-    lds_barrier();
-    uint32_t wv[R / 2];
-#pragma unroll
-    for (int cc = 0; cc < CPR; ++cc) {
-      const u32x4 q = *(const u32x4*)(stage_in + tid * ROWB + swz_chunk(tid, cc, ROWB) * 16);
-      wv[4 * cc] = q.x; wv[4 * cc + 1] = q.y; wv[4 * cc + 2] = q.z; wv[4 * cc + 3] = q.w;
-    }
-    lds_barrier();
-    if (ph >= 0) store_codes(ph, prow0);
-    if (v + G < ntiles) {
-      int64_t h2, sb2, r2;
-      tile_of(v + G, h2, sb2, r2);
-      load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + (r2 * a.heads + h2) * ROWB, tok_stride, B, w, NW, lane);
-    }
-
-    // 2. norm of the input (= norm of the rotated vector), then the unnormalized rotation
-    float inv_nu = 1.f;
-    if (a.nsep) {
-      const float nu = sqrtf(sum_squares_in<DT, R>(wv));
-      inv_nu = nu > 0.f ? 1.f / nu : 0.f;
-      a.norms[(row0 + tid) * a.heads + h] = (uint16_t)f32_to_f16(nu);
-    }
-    float y[R];
-    widen_stage1<DT, R>(y, wv, sg, LG != 0);
-    fwht_rest<R, LG>(y);
-    if (a.nsep) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) y[i] *= inv_nu;              // u, up to the common 1/sqrt(n)
-    }
-
-    // 3. per-channel absmax over the B tokens: each wave transposes 16 channels at a time
-    //    through a 4 KiB LDS scratch (64 tokens x 16 fp32), reduces 16 tokens per lane and
-    //    finishes across the 4 lane groups with two lane shuffles.
-    float* scr = scr_all + w * 1024;
-    const int ch = lane & 15, grp = lane >> 4;
-#pragma unroll
-    for (int j = 0; j < R / 16; ++j) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 q = {y[16 * j + 4 * jj], y[16 * j + 4 * jj + 1], y[16 * j + 4 * jj + 2], y[16 * j + 4 * jj + 3]};
-        *(f32x4*)(scr + lane * 16 + 4 * (jj ^ ((lane >> 2) & 3))) = q;
-      }
-      wave_lds_sync();
-      float m = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int t = 4 * k + grp;   // (t >> 2) & 3 == k & 3
-        m = fmaxf(m, fabsf(scr[t * 16 + 4 * ((ch >> 2) ^ (k & 3)) + (ch & 3)]));
-      }
-      m = fmaxf(m, shfl_xor_f(m, 16));
-      m = fmaxf(m, shfl_xor_f(m, 32));
-      if (lane < 16) colmax[w * R + 16 * j + lane] = m;
-      wave_lds_sync();
-    }
-    lds_barrier();
-    for (int c = tid; c < R; c += B) {
-      float m = colmax[c];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) m = fmaxf(m, colmax[ww * R + c]);
-      invs[c] = m > 0.f ? a.q / m : 0.f;
-      a.scales[(sb * a.heads + h) * R + c] = (uint16_t)f32_to_f16(m * a.scale_mul);
-    }
-    if (tid < R / 32) fmask[tid] = 0u;
-    lds_barrier();
-
-    // 4. codes (+ near-tie flags), staged in LDS; stored at the start of the next iteration
-    uint32_t cw[R / 8], chm[R / 32];
-    quantize_row<R, true>(y, [&](int c) { return invs[c]; }, cw, chm);
-#pragma unroll
-    for (int cc = 0; cc < CCR; ++cc) {
-      const u32x4 q = {cw[4 * cc], cw[4 * cc + 1], cw[4 * cc + 2], cw[4 * cc + 3]};
-      *(u32x4*)(stage_codes + tid * CRB + swz_chunk(tid, cc, CRB) * 16) = q;
-    }
-    uint32_t anych = 0u;
-#pragma unroll
-    for (int g = 0; g < R / 32; ++g) {
-      anych |= chm[g];
-      if (lane == 0 && chm[g]) atomicOr(&fmask[g], chm[g]);
-    }
-    if (lane == 0) wave_any[w] = anych;
-    lds_barrier();
-    uint32_t any = 0u;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) any |= wave_any[ww];
-
-    // 5. rare path: re-decide the codes of channels holding a near-tie exactly, in fp64
-    if (any) {
-      const unsigned char* xrow = xb + tid * tok_stride;
-      const double nu64 = a.nsep ? sqrt(exact_sumsq64<DT, R>(xrow)) : 1.0;
-      for (int g = 0; g < R / 32; ++g) {
-        uint32_t bits = fmask[g];
-        while (bits) {
-          const int c = 32 * g + __builtin_ctz(bits);
-          bits &= bits - 1u;
-          const double wv64 = nu64 > 0.0 ? exact_rot64<DT>(xrow, sg, c, LG) / nu64 : 0.0;
-          if (tid == 0) m64 = 0ull;
-          lds_barrier();
-          atomicMax(&m64, __builtin_bit_cast(unsigned long long, fabs(wv64)));
-          lds_barrier();
-          const double mm = __builtin_bit_cast(double, m64);
-          patch_nibble(stage_codes, tid, CRB, c, mm > 0.0 ? exact_code((double)a.q * wv64 / mm) : 0u);
-          lds_barrier();
-        }
-      }
-    }
-    ph = h;
-    prow0 = row0;
-  }
-  if (ph >= 0) {
-    lds_barrier();
-    store_codes(ph, prow0);
-  }
-}
-
 // Per-token rare path: every code of each vector holding a near-tie is recomputed exactly
 // (fp64 transform in LDS, shared by the wave); v = Q Y_c / max |Y| for both per-token modes.
 template <int DT, int R, int LG>
@@ -623,18 +451,6 @@ static int64_t persistent_grid(K kernel, int threads, int64_t ntiles) {
 }
 
 template <int DT, int R, int LG>
-static void launch_pchan_k(const QuantArgs& a, hipStream_t st) {
-  const int64_t ntiles = a.seqs * (a.tokens / a.block) * a.heads;
-  auto go = [&](auto kernel) {
-    const int64_t grid = persistent_grid(kernel, a.block, ntiles);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(a.block), 0, st, a, ntiles);
-  };
-  if (a.block == 64) go(quant_pchan_kernel<DT, R, LG, 1>);
-  else if (a.block == 128) go(quant_pchan_kernel<DT, R, LG, 2>);
-  else if constexpr (R == 64) go(quant_pchan_kernel<DT, R, LG, 4>);
-}
-
-template <int DT, int R, int LG>
 static void launch_ptok_k(const QuantArgs& a, hipStream_t st, int64_t nseg, int lgL) {
   const int64_t ntiles = (nseg + 63) / 64;
   const int64_t grid = persistent_grid(quant_ptok_kernel<DT, R, LG>, 64, ntiles);
@@ -652,23 +468,9 @@ static void by_lg(int lg, Args&&... args) {
     default: if constexpr (R >= 128) K<DT, R, 7>::run(args...); break;
   }
 }
-template <int DT, int R, int LG> struct PchanK {
-  static void run(const QuantArgs& a, hipStream_t st) { launch_pchan_k<DT, R, LG>(a, st); }
-};
 template <int DT, int R, int LG> struct PtokK {
   static void run(const QuantArgs& a, hipStream_t st, int64_t nseg, int lgL) { launch_ptok_k<DT, R, LG>(a, st, nseg, lgL); }
 };
-
-template <int DT>
-static void pchan_dt(const QuantArgs& a, hipStream_t st) {
-  if (a.dim == 128) by_lg<DT, 128, PchanK>(a.lg_had, a, st);
-  else by_lg<DT, 64, PchanK>(a.lg_had, a, st);
-}
-
-hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t st) {
-  if (a.dtype == DT_F16) pchan_dt<DT_F16>(a, st); else pchan_dt<DT_BF16>(a, st);
-  return hipGetLastError();
-}
 
 template <int DT>
 static void ptok_dt(const QuantArgs& a, hipStream_t st) {
