@@ -6,27 +6,33 @@
 // (R = (1/sqrt K)[+-1]; runtime scale s_j = max over the tokens of column j); NSNQuant summary
 // "Hadamard transform" (random signs, then the Hadamard matrix).
 //
-// Work split: one workgroup per tile = (sequence, block of B tokens, head), B / 32 waves; wave
-// w takes tokens [32 w, 32 w + 32) of the block as two sub-tiles of 16 tokens.  In a sub-tile,
-// lane l = 16 g + j holds token j and the R/4 channels [g R/4, (g + 1) R/4): it loads them as
-// its part of the MFMA B operand and gets back the rotated values of the same channels from
-// the MFMA D layout, so norms, codes and their packing never leave the lane.
+// Work split: a tile is (sequence, block of B tokens, head).  Persistent workgroups of four
+// waves walk the tiles of their XCD's range; the rows of the next tile stream into a second
+// LDS buffer (global_load_lds, 1 KiB per wave instruction) while the current tile is
+// computed.  Wave w owns the output channels [w R/4, (w + 1) R/4) of every token of the tile,
+// so the per-channel max over the block, the scales and the exact re-decision of near-ties
+// are all wave-local.  Two workgroup barriers per tile: one publishes the token norms, one
+// hands the assembled code rows over, which the next iteration stores whole.
 //
-// Rotation: Y^T = blockdiag(H_n) diag(sigma) X^T per sub-tile with v_mfma_f32_16x16x32 (f16 or
-// bf16 operands, fp32 accumulation; the +-1 products are exact).  Output rows are channels
-// c = (R/4)(i >> 2) + 4 I + (i & 3) of I-block I, the contraction index of K step K is
-// c' = (R/4) g + 8 K + e.  With this numbering every 16 x 32 block of the n x n matrix is
-// beta(I, K) * F_{I mod 2}: two fixed +-1/0 fragments and a sign or zero that depends only on
-// (I, K) and is known at compile time, so four fragment registers hold the whole transform.
-// The random signs flip the sign bits of the B operand.  The transform is left unnormalized:
-// 1/sqrt(n) cancels in every quotient and only enters the stored scale.
+// Rotation: Y^T = blockdiag(H_n) diag(sigma) X^T in 16-token sub-tiles with
+// v_mfma_f32_16x16x32 (fp16 or bf16 operands, fp32 accumulation; the +-1 products are exact).
+// In a sub-tile, lane l = 16 g + j holds token j; the B operand of K step K is channels
+// 32 K + 8 g + e, and MFMA row i of the wave's local I-block I is channel
+// c = (R/4) w + 8 (i >> 2) + 4 I + (i & 3) (R = 128; R = 64 uses one I-block), so lane l
+// receives channels (R/4) w + 8 g + [0, 8) of token j.  Every 16 x 32 block of the n x n matrix
+// factors bit by bit into beta(w, K), from the bits of c and c' that are set by w and K alone
+// (a sign, or zero outside the diagonal blocks), times a fragment F_{w,I} over the remaining
+// bits, so two fragment registers per wave hold the transform.  The random signs and beta flip
+// the sign bits of the B operand.  The transform is left unnormalized: 1/sqrt(n) cancels
+// in every quotient and only enters the stored scale.
 //
-// Scales: u = y / ||y|| (||y|| = ||x||, taken from the input with exact fp16/bf16 squares);
-// the per-channel max over the block goes through LDS once per tile.  Codes: one fma per value,
-// b = bits(u * (Q / m) + 136.5): byte 2 of b is code + 8 (round half up on a 2^-16 grid) and
-// b & 0xffff == 0 marks a near-tie, |v - (k + 1/2)| <= 2^-17.  Near-ties are re-decided
-// exactly: the channel's max is recomputed in fp64 from the tokens whose fp32 value is within
-// 2^-12 of it, the flagged values in fp64 too, and the code is rne(fp32(v)).
+// Scales: u = y / ||y|| (||y|| = ||x||, from the input with exact fp16/bf16 squares).  Codes:
+// one fma per value, b = bits(u * (Q / m) + 136.5): byte 2 of b is code + 8 (round half up on a
+// 2^-16 grid) and b & 0xffff == 0 marks a near-tie, |v - (k + 1/2)| <= 2^-17.  Near-ties are
+// re-decided exactly: the channel's max is recomputed in fp64 from the tokens whose fp32
+// value is within 2^-12 of it, the flagged values in fp64 too, and the code is rne(fp32(v)).
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -43,55 +49,6 @@ template <int DT> __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
                                                    0);
-}
-
-// Sign / zero of block (I, K) relative to F_{I mod 2}: bits 3.. of the output channel come
-// from I >> 1 and bits 3.. of the input channel from K.
-template <int LG> __device__ __forceinline__ constexpr int frag_beta(int I, int K) {
-  const int n = 1 << LG, a = (I >> 1) << 3, k = K << 3;
-  if ((a & ~(n - 1)) != (k & ~(n - 1))) return 0;
-  return (__builtin_popcount(a & k & (n - 1)) & 1) ? -1 : 1;
-}
-
-// This lane's part of F_p (A operand: row i = lane & 15, inputs 8 (lane >> 4) + e): entry
-// (c, c') of blockdiag(H_n) for I = p, K = 0.
-template <int DT, int R, int LG> __device__ __forceinline__ u32x4 hadamard_fragment(int p, int lane) {
-  const int i = lane & 15, gk = lane >> 4;
-  const int c = (R / 4) * (i >> 2) + 4 * p + (i & 3);
-  const uint32_t one = DT == DT_F16 ? 0x3C00u : 0x3F80u;
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t pair = 0u;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int cp = (R / 4) * gk + 2 * q + hh;
-      uint32_t v = 0u;
-      if ((c >> LG) == (cp >> LG)) v = one | ((uint32_t)(__builtin_popcount(c & cp & ((1 << LG) - 1)) & 1) << 15);
-      pair |= v << (16 * hh);
-    }
-    w[q] = pair;
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// Sign-bit masks of the 8 random signs of K step K in this lane (0x8000 per negated half).
-template <int R> __device__ __forceinline__ u32x4 sign_masks(const int8_t* __restrict__ sg, int g, int K) {
-  const u32x2 s8 = *(const u32x2*)(sg + (R / 4) * g + 8 * K);
-  uint32_t m[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t sw = q < 2 ? s8.x : s8.y;
-    m[q] = __builtin_amdgcn_perm(0u, sw, (q & 1) ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u;
-  }
-  return u32x4{m[0], m[1], m[2], m[3]};
-}
-
-template <int DT> __device__ __forceinline__ float sumsq2(uint32_t x, float acc) {
-  if constexpr (DT == DT_F16)
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, x), acc, false);
-  else
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, x), acc, false);
 }
 
 __device__ __forceinline__ uint32_t min3_u16(uint32_t a, uint32_t b, uint32_t c) {
@@ -111,318 +68,400 @@ template <int DT> __device__ __forceinline__ double widen64(uint32_t h) {
   return (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
 }
 
-// Exact (fp64) parts of one token for the rare path: over this lane's R/4 input channels,
-// the unnormalized rotated value of channel c (sum of +-x, exact) and the sum of squares.
-struct ExactParts {
-  double y, ss;
-};
-template <int DT, int R, int LG>
-__device__ __noinline__ ExactParts exact_parts(const unsigned char* __restrict__ xrow, const int8_t* __restrict__ sgl,
-                                               int c0, int c) {
-  constexpr int n = 1 << LG;
-  double y = 0.0, ss = 0.0;
-#pragma unroll 1
-  for (int q = 0; q < R / 32; ++q) {
-    const u32x4 v = *(const u32x4*)(xrow + 16 * q);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = c0 + 8 * q + e;
-      const double x = widen64<DT>((e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu));
-      ss = __builtin_fma(x, x, ss);
-      if constexpr (LG == 0) {
-        if (k == c) y = x;
-      } else if ((k >> LG) == (c >> LG)) {
-        const bool neg = ((__builtin_popcount(k & c & (n - 1)) & 1) != 0) != (sgl[k] < 0);
-        y += neg ? -x : x;
-      }
-    }
-  }
-  return ExactParts{y, ss};
-}
-
 __device__ __forceinline__ uint32_t exact_nibble(double v) {
   return (uint32_t)(int)__builtin_rintf((float)v) & 0xfu;
 }
 
-template <int DT, int R, int LG, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) quant_pchan_mfma(QuantArgs a, int64_t ntiles) {
-  constexpr int B = 32 * NW;
-  constexpr int NK = R / 32;            // K steps per sub-tile
-  constexpr int NI = R / 16;            // output blocks of 16 channels
-  constexpr int CL = R / 4;             // channels per lane
-  constexpr int NP = R / 32;            // packed code words per lane and sub-tile
-  // per wave: its 32 input rows (staged by global_load_lds), later reused for its lane maxima
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max over the 16 lanes of each row (lanes 16 g .. 16 g + 15) with DPP row rotations
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));   // row_ror:2
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));   // row_ror:1
+  return v;
+}
+
+__device__ __forceinline__ uint32_t row_or16(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// entry (c, c') of blockdiag(H_n), n = 2^LG: zero unless c and c' share their n-block
+template <int LG> __device__ __forceinline__ constexpr int hval(int c, int cp) {
+  if ((c >> LG) != (cp >> LG)) return 0;
+  return (__builtin_popcount(c & cp & ((1 << LG) - 1)) & 1) ? -1 : 1;
+}
+
+template <int R> __device__ __forceinline__ constexpr int out_channel(int w, int I, int i) {
+  return R == 128 ? 32 * w + 8 * (i >> 2) + 4 * I + (i & 3) : 16 * w + 4 * (i >> 2) + (i & 3);
+}
+// bits of the channel numbers that are set by the wave index (c) and by the K step (c')
+template <int R> constexpr int UMASK = R == 128 ? 0x60 : 0x20;
+
+// F_{w,I}: this lane's 8 A-operand entries (row i = lane & 15, inputs 8 (lane >> 4) + e of K
+// step 0) over the bits of c and c' that are not both uniform
+template <int DT, int R, int LG> __device__ __forceinline__ u32x4 hadamard_fragment(int w, int I, int lane) {
+  const int c = out_channel<R>(w, I, lane & 15) & ~UMASK<R>;
+  const uint32_t one = DT == DT_F16 ? 0x3C00u : 0x3F80u;
+  uint32_t q4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t pair = 0u;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int cp = (8 * (lane >> 4) + 2 * q + hh) & ~UMASK<R>;
+      const int v = hval<LG>(c, cp);
+      pair |= (v == 0 ? 0u : (one | (v < 0 ? 0x8000u : 0u))) << (16 * hh);
+    }
+    q4[q] = pair;
+  }
+  return u32x4{q4[0], q4[1], q4[2], q4[3]};
+}
+// beta(w, K): the factor from the uniform bits
+template <int R, int LG> __device__ __forceinline__ constexpr int frag_beta(int w, int K) {
+  return hval<LG>(out_channel<R>(w, 0, 0) & UMASK<R>, (32 * K) & UMASK<R>);
+}
+
+template <int DT, int R, int LG, int B>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+quant_pchan_tile(QuantArgs a, int64_t ntiles) {
+  constexpr int NK = R / 32;            // K steps of the contraction
+  constexpr int NIW = R / 64;           // output I-blocks per wave
+  constexpr int LCH = 4 * NIW;          // channels per lane and token
+  constexpr int ST = B / 16;            // sub-tiles per tile
+  constexpr int OWN = B / 64;           // sub-tiles whose norms this wave computes
   constexpr int ROWB = 2 * R;           // input row bytes
   constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
-  constexpr int WSTAGE = 32 * ROWB;     // bytes per wave (= (R/4) quads x 16 slots x 16 B)
-  __shared__ __attribute__((aligned(16))) unsigned char stage[NW * WSTAGE];
-  __shared__ __attribute__((aligned(16))) float invs[R];
-  __shared__ unsigned long long m64[R];
-  __shared__ uint32_t chmask[R / 32];
-  __shared__ uint32_t wflag[NW];
+  constexpr int TSTAGE = B * ROWB;      // bytes of the staged tile
+  constexpr int WSTAGE = TSTAGE / 4;    // bytes each wave loads (B / 4 rows)
+  constexpr int NLD = WSTAGE / 1024;    // load instructions per wave
+  constexpr int RB = R / 2;             // code row bytes
+  static_assert(ST % 4 == 0 && NLD >= 1, "tile shape");
+  // the tile's input rows; once every wave is done with them, the packed code rows
+  // [token][R/2 bytes] (wave w fills bytes [(R/8) w, (R/8)(w + 1)) of every row)
+  __shared__ __attribute__((aligned(16))) unsigned char stage[TSTAGE];
+  __shared__ __attribute__((aligned(16))) int8_t sg[R];                 // the head's random signs
+  __shared__ __attribute__((aligned(16))) float ninv[16 * ST];         // [j][s]: 1 / norm of token 16 s + j
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int j = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
   const int64_t tile = xcd_tile(blockIdx.x, ntiles);
-  const int64_t h = tile % a.heads, sb = tile / a.heads;
+  const int64_t h = tile % a.heads, sb = tile / a.heads;   // sb = sequence * (tokens / B) + block
   const int64_t nb = a.tokens / B;
   const int64_t seq = sb / nb;
-  const int64_t row0 = seq * a.tokens + (sb - seq * nb) * B + 32 * w;   // first token of this wave
+  const int64_t row0 = seq * a.tokens + (sb - seq * nb) * B;   // first token of the tile
 
-  // 1. signs and fragments (issued first: sub-tile 0 must not wait for them behind its input),
-  //    then the input of both sub-tiles, 4 x 16 B per lane and sub-tile (R = 128)
-  const int8_t* sgh = a.signs ? a.signs + h * R : nullptr;
-  u32x4 fr[4], sm[NK];
-  if constexpr (LG != 0) {
-    fr[0] = hadamard_fragment<DT, R, LG>(0, lane);
-    fr[1] = hadamard_fragment<DT, R, LG>(1, lane);
-    fr[2] = fr[0] ^ 0x80008000u;
-    fr[3] = fr[1] ^ 0x80008000u;
+  // 1. this wave's B / 4 rows into LDS (instruction k moves 1 KiB; the chunk that lane p fetches
+  //    is XOR-swizzled with its row, so slot cc of row r holds chunk cc ^ (r % CPR) and the
+  //    MFMA-layout reads below are free of bank conflicts); wave 0 also fetches the signs
+  {
+    const unsigned char* xw = (const unsigned char*)a.x + ((row0 + (B / 4) * w) * a.heads + h) * ROWB;
+    const uint32_t tok_bytes = (uint32_t)(a.heads * ROWB);
 #pragma unroll
-    for (int K = 0; K < NK; ++K) sm[K] = sign_masks<R>(sgh, g, K);
-  }
-  // the wave's 32 rows: instruction k moves 1 KiB (64 lanes x 16 B) into LDS; the chunk that
-  // lane p fetches is XOR-swizzled with its row so that the MFMA-layout reads below are free
-  // of bank conflicts (slot cc of row r holds chunk cc ^ (r mod CPR))
-  unsigned char* wst = stage + w * WSTAGE;
-  const unsigned char* xw = (const unsigned char*)a.x + ((row0 * a.heads + h) * R) * 2;
-  const int64_t tok_bytes = a.heads * ROWB;
-#pragma unroll
-  for (int k = 0; k < WSTAGE / 1024; ++k) {
-    const int p = 64 * k + lane, row = p / CPR, cc = p % CPR;
-    __builtin_amdgcn_global_load_lds((const void*)(xw + row * tok_bytes + 16 * (cc ^ (row % CPR))),
-                                     (__attribute__((address_space(3))) void*)(wst + k * 1024), 16, 0, 0);
-  }
-  if (tid < R) m64[tid] = 0ull;
-  if (tid < R / 32) chmask[tid] = 0u;
-  if (tid < NW) wflag[tid] = 0u;
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the staged rows (and the signs) have landed
-  asm volatile("" ::: "memory");
-  u32x4 xin[2][NK];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int row = 16 * s + j;
-#pragma unroll
-    for (int K = 0; K < NK; ++K)
-      xin[s][K] = *(const u32x4*)(wst + row * ROWB + 16 * (((R / 32) * g + K) ^ (row % CPR)));
-  }
-
-  // 2. norms and the rotation, sub-tile by sub-tile
-  f32x4 u[2][NI];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float inv_nu = 1.f;
-    if (a.nsep) {
-      float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-      for (int K = 0; K < NK; ++K) {
-        p0 = sumsq2<DT>(xin[s][K].x, p0);
-        p1 = sumsq2<DT>(xin[s][K].y, p1);
-        p0 = sumsq2<DT>(xin[s][K].z, p0);
-        p1 = sumsq2<DT>(xin[s][K].w, p1);
-      }
-      float ss = p0 + p1;
-      ss += shfl_xor_f(ss, 16);
-      ss += shfl_xor_f(ss, 32);
-      inv_nu = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
-      if (g == 0) a.norms[(row0 + 16 * s + j) * a.heads + h] = (uint16_t)f32_to_f16(ss * inv_nu);
+    for (int k = 0; k < NLD; ++k) {
+      const int p = 64 * k + lane, row = p / CPR, cc = p % CPR;
+      const uint32_t off = (uint32_t)row * tok_bytes + 16u * (uint32_t)(cc ^ ((row + (B / 4) * w) % CPR));
+      __builtin_amdgcn_global_load_lds((const void*)(xw + off),
+                                       (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, 0);
     }
-    if constexpr (LG == 0) {
+    if constexpr (LG != 0) {
+      if (w == 0 && lane < R / 16)
+        __builtin_amdgcn_global_load_lds((const void*)(a.signs + h * R + 16 * lane),
+                                         (__attribute__((address_space(3))) void*)sg, 16, 0, 0);
+    }
+  }
+  // this wave's base fragments F_I (the random signs and the block signs beta(w, K) are folded
+  // in once the signs have landed), built while the rows are in flight
+  u32x4 fb0[NIW];
+  if constexpr (LG != 0) {
+#pragma unroll
+    for (int I = 0; I < NIW; ++I) fb0[I] = hadamard_fragment<DT, R, LG>(w, I, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's rows (and the signs) have landed
+  asm volatile("" ::: "memory");
+  lds_barrier();
+
+  // the NK operand chunks of tile row 16 s + j: channels 32 K + 8 g + [0, 8) (the swizzle
+  // (16 s + j) % CPR = j % CPR does not depend on s)
+  auto read_x = [&](int s, int K) {
+    return *(const u32x4*)(stage + 16 * s * ROWB + (j * ROWB + 16 * ((4 * K + g) ^ (j % CPR))));
+  };
+  // squared norm of token 16 s + j from the Gram matrix X X^T of the sub-tile (A = B = the same
+  // registers; exact products, fp32 sums).  Token t's diagonal entry sits in lane 16 (t / 4) + t,
+  // register t % 4: every lane selects register j % 4 and reads lane j + 16 (j / 4).
+  auto gram_ssq = [&](const u32x4 (&x)[NK]) {
+    f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = 0; K < NK; ++K) gm = mfma16<DT>(x[K], x[K], gm);
+    const float d01 = (j & 1) ? gm.y : gm.x, d23 = (j & 1) ? gm.w : gm.z;
+    const float dg = (j & 2) ? d23 : d01;
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((j + 16 * (j >> 2)) << 2, __builtin_bit_cast(int, dg)));
+  };
+
+  // 2. norms of this wave's own sub-tiles -> LDS (and the stored fp16 norms)
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int s = OWN * w + o;
+    u32x4 x[NK];
+#pragma unroll
+    for (int K = 0; K < NK; ++K) x[K] = read_x(s, K);
+    const float ssq = gram_ssq(x);
+    const float rq = __builtin_amdgcn_rsqf(ssq);            // +inf for a zero vector
+    const float rinv = ssq > 0.f ? rq : 0.f;
+    if (g == 0) {
+      ninv[j * ST + s] = a.nsep ? rinv : 1.f;
+      if (a.nsep) a.norms[(row0 + 16 * s + j) * a.heads + h] = (uint16_t)f32_to_f16(ssq * rinv);   // sqrt(ssq)
+    }
+  }
+
+  // 3. the rotation of this wave's channels, sub-tile by sub-tile (unnormalized)
+  f32x4 u[ST][NIW];
+  auto rotate = [&](auto wc, int only_s, f32x4 (&ur)[NIW]) {
+    constexpr int W = decltype(wc)::value;
+    // fragments of the nonzero blocks of this wave, signed for the head
+    u32x4 fk[NK][NIW];
+    if constexpr (LG != 0) {
 #pragma unroll
       for (int K = 0; K < NK; ++K) {
-        const uint32_t q[4] = {xin[s][K].x, xin[s][K].y, xin[s][K].z, xin[s][K].w};
+        const int bt = frag_beta<R, LG>(W, K);
+        if (bt == 0) continue;
+        const u32x2 s8 = *(const u32x2*)(sg + 32 * K + 8 * g);
+        uint32_t m[4];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          u[s][2 * K + hh] = f32x4{lo_f32<DT>(q[2 * hh]), hi_f32<DT>(q[2 * hh]), lo_f32<DT>(q[2 * hh + 1]),
-                                   hi_f32<DT>(q[2 * hh + 1])};
+        for (int q = 0; q < 4; ++q)
+          m[q] = (__builtin_amdgcn_perm(0u, q < 2 ? s8.x : s8.y, (q & 1) ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u) ^
+                 (bt < 0 ? 0x80008000u : 0u);
+#pragma unroll
+        for (int I = 0; I < NIW; ++I) fk[K][I] = fb0[I] ^ u32x4{m[0], m[1], m[2], m[3]};
       }
-    } else {
-      u32x4 xs[NK];
+    }
+    auto one = [&](int s, f32x4 (&us)[NIW]) {
+      u32x4 x[NK];
 #pragma unroll
-      for (int K = 0; K < NK; ++K) xs[K] = xin[s][K] ^ sm[K];
+      for (int K = 0; K < NK; ++K) x[K] = read_x(s, K);
+      if constexpr (LG == 0) {
+        const int c0 = (R / 4) * W + LCH * g;               // no rotation: the lane's own channels
+        const uint32_t e0 = (uint32_t)((c0 & 7) >> 1);
+        const u32x4 xr = R == 128 ? x[W] : *(const u32x4*)(stage + 16 * s * ROWB + (j * ROWB + 16 * ((c0 >> 3) ^ (j % CPR))));
+        const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
-      for (int I = 0; I < NI; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int I = 0; I < NIW; ++I) {
+          const uint32_t w0 = xw[(e0 + 2 * I) & 3], w1 = xw[(e0 + 2 * I + 1) & 3];
+          us[I] = f32x4{lo_f32<DT>(w0), hi_f32<DT>(w0), lo_f32<DT>(w1), hi_f32<DT>(w1)};
+        }
+      } else {
+#pragma unroll
+        for (int I = 0; I < NIW; ++I) us[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int K = 0; K < NK; ++K) {
-          const int bt = frag_beta<LG>(I, K);
-          if (bt != 0) acc = mfma16<DT>(fr[(I & 1) + (bt < 0 ? 2 : 0)], xs[K], acc);
+          if (frag_beta<R, LG>(W, K) == 0) continue;
+#pragma unroll
+          for (int I = 0; I < NIW; ++I) us[I] = mfma16<DT>(fk[K][I], x[K], us[I]);
         }
-        u[s][I] = acc;
       }
-    }
-    if (a.nsep) {
+    };
+    if (only_s >= 0) {                                      // one sub-tile, for the rare path
 #pragma unroll
-      for (int I = 0; I < NI; ++I) u[s][I] *= inv_nu;
+      for (int s = 0; s < ST; ++s)
+        if (s == only_s) one(s, ur);
+      return;
     }
-  }
-
-  // 3. per-channel max over the block: lane maxima of the two tokens -> LDS (over the wave's own
-  //    staged rows, which it has finished reading); TPQ threads then
-  //    reduce channels 4 cq .. 4 cq + 3, each over R/16 of the 16 NW token slots, and finish
-  //    with lane shuffles inside their aligned group
 #pragma unroll
-  for (int I = 0; I < NI; ++I) {
-    const f32x4 m = {fmaxf(fabsf(u[0][I].x), fabsf(u[1][I].x)), fmaxf(fabsf(u[0][I].y), fabsf(u[1][I].y)),
-                     fmaxf(fabsf(u[0][I].z), fabsf(u[1][I].z)), fmaxf(fabsf(u[0][I].w), fabsf(u[1][I].w))};
-    ((f32x4*)wst)[(NI * g + I) * 16 + j] = m;   // slot (quad NI g + I, token j) of this wave
-  }
-  lds_barrier();
+    for (int s = 0; s < ST; ++s) {
+      one(s, u[s]);
+      // keeps the scheduler from hoisting every sub-tile's operand reads (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto run = [&](int only_s, f32x4 (&ur)[NIW]) {
+    switch (w) {
+      case 0: rotate(std::integral_constant<int, 0>{}, only_s, ur); break;
+      case 1: rotate(std::integral_constant<int, 1>{}, only_s, ur); break;
+      case 2: rotate(std::integral_constant<int, 2>{}, only_s, ur); break;
+      default: rotate(std::integral_constant<int, 3>{}, only_s, ur); break;
+    }
+  };
   {
-    constexpr int TPQ = NW * 256 / R;     // threads per channel quad
-    constexpr int SPT = R / 16;           // token slots per thread
-    const int cq = tid / TPQ, part = tid % TPQ;
-    const int slot0 = part * SPT;                     // of the 16 NW (wave, token) slots
-    const f32x4* rp = (const f32x4*)(stage + (slot0 / 16) * WSTAGE) + cq * 16 + slot0 % 16;
-    f32x4 mx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-      const f32x4 v = rp[(k + tid) % SPT];
-      mx = f32x4{fmaxf(mx.x, v.x), fmaxf(mx.y, v.y), fmaxf(mx.z, v.z), fmaxf(mx.w, v.w)};
-    }
-#pragma unroll
-    for (int o = 1; o < TPQ; o <<= 1) {
-      mx.x = fmaxf(mx.x, shfl_xor_f(mx.x, o));
-      mx.y = fmaxf(mx.y, shfl_xor_f(mx.y, o));
-      mx.z = fmaxf(mx.z, shfl_xor_f(mx.z, o));
-      mx.w = fmaxf(mx.w, shfl_xor_f(mx.w, o));
-    }
-    if (part == 0) {
-      const float mm[4] = {mx.x, mx.y, mx.z, mx.w};
-      f32x4 iv;
-      uint16_t* sp = a.scales + (sb * a.heads + h) * R + 4 * cq;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        iv[r] = mm[r] > 0.f ? a.q / mm[r] : 0.f;
-        sp[r] = (uint16_t)f32_to_f16(mm[r] * a.scale_mul);
-      }
-      *(f32x4*)(invs + 4 * cq) = iv;
-    }
+    f32x4 unused[NIW];
+    run(-1, unused);
   }
-  lds_barrier();
 
-  // 4. codes and near-tie flags
-  f32x4 iv[NI];
+  // 4. every wave's norms are published: u = y / norm, the per-channel maxima over the tile
+  lds_barrier();
+  float rn[ST];
 #pragma unroll
-  for (int I = 0; I < NI; ++I) iv[I] = *(const f32x4*)(invs + CL * g + 4 * I);
-  uint32_t pk[2][NP];
+  for (int s4 = 0; s4 < ST / 4; ++s4) {
+    const f32x4 v = *(const f32x4*)(ninv + j * ST + 4 * s4);
+    rn[4 * s4] = v.x; rn[4 * s4 + 1] = v.y; rn[4 * s4 + 2] = v.z; rn[4 * s4 + 3] = v.w;
+  }
+  float mxf[LCH];
+#pragma unroll
+  for (int q = 0; q < LCH; ++q) mxf[q] = 0.f;
+#pragma unroll
+  for (int s = 0; s < ST; ++s)
+#pragma unroll
+    for (int I = 0; I < NIW; ++I) {
+      u[s][I] *= rn[s];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mxf[4 * I + r] = fmaxf(mxf[4 * I + r], fabsf(u[s][I][r]));
+    }
+  uint32_t mx[LCH];
+#pragma unroll
+  for (int q = 0; q < LCH; ++q) mx[q] = row_max16(__builtin_bit_cast(uint32_t, mxf[q]));   // values >= 0
+
+  // 5. scales (lane j < LCH stores channel (R/4) w + LCH g + j) and inverse scales
+  float iv[LCH];
+  uint32_t s16 = 0u;
+#pragma unroll
+  for (int q = 0; q < LCH; ++q) {
+    const float m = __builtin_bit_cast(float, mx[q]);
+    iv[q] = m > 0.f ? a.q * __builtin_amdgcn_rcpf(m) : 0.f;
+    if (q == j) s16 = f32_to_f16(m * a.scale_mul);
+  }
+  if (j < LCH) a.scales[(sb * a.heads + h) * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
+
+  // 6. codes and near-tie flags
+  uint32_t pk[ST];
   uint32_t fl = 0xffffffffu;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < ST; ++s) {
+    uint32_t b[8];
 #pragma unroll
-    for (int d = 0; d < NP; ++d) {
-      uint32_t b[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        b[r] = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s][2 * d][r], iv[2 * d][r], CODE_MAGIC));
-        b[4 + r] = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s][2 * d + 1][r], iv[2 * d + 1][r], CODE_MAGIC));
-      }
+    for (int q = 0; q < LCH; ++q) b[q] = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s][q >> 2][q & 3], iv[q], CODE_MAGIC));
+    if constexpr (LCH == 8) {
       fl = min3_u16(fl, b[0], b[1]);
       fl = min3_u16(fl, b[2], b[3]);
       fl = min3_u16(fl, b[4], b[5]);
       fl = min3_u16(fl, b[6], b[7]);
-      pk[s][d] = pack8(b);
+    } else {
+      fl = min3_u16(fl, b[0], b[1]);
+      fl = min3_u16(fl, b[2], b[3]);
+      b[4] = b[5] = b[6] = b[7] = 0x00080000u;              // code 0 padding (dropped on store)
     }
+    pk[s] = pack8(b);
   }
-  if (__ballot((fl & 0xffffu) == 0u) != 0ull && lane == 0) wflag[w] = 1u;
-  lds_barrier();
-  uint32_t any = 0u;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) any |= wflag[ww];
 
-  // 5. rare path: exact re-decision of the near-ties (whole workgroup, uniform control flow)
-  if (any) {
-    uint32_t cm[2] = {0u, 0u};
+  // 7. rare path, wave-local: exact re-decision of this wave's near-ties.  u is recomputed
+  //    from the staged rows with the same instructions (bit-identical), so the main path need
+  //    not keep it alive.
+  if (__ballot((fl & 0xffffu) == 0u) != 0ull) {
+    uint64_t fbm = 0ull, cbm = 0ull;                        // bit LCH s + q: near-tie / near-max
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < ST; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 us[NIW];
+      run(s, us);
 #pragma unroll
-      for (int I = 0; I < NI; ++I)
+      for (int q = 0; q < LCH; ++q) {
+        const float uq = us[q >> 2][q & 3] * rn[s];
+        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_fmaf(uq, iv[q], CODE_MAGIC));
+        if ((bb & 0xffffu) == 0u) fbm |= 1ull << (LCH * s + q);
+        if (fabsf(uq) * iv[q] >= a.q * (1.f - 0x1p-12f)) cbm |= 1ull << (LCH * s + q);
+      }
+    }
+    uint32_t cm = 0u;                                       // bit q: channel (R/4) w + LCH g + q
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s][I][r], iv[I][r], CODE_MAGIC));
-          if ((bb & 0xffffu) == 0u) cm[s] |= 1u << (4 * I + r);
-        }
-    const uint32_t cml = cm[0] | cm[1];
-    if (cml) atomicOr(&chmask[(CL * g) >> 5], cml << ((CL * g) & 31));
-    lds_barrier();
+    for (int s = 0; s < ST; ++s) cm |= (uint32_t)(fbm >> (LCH * s)) & ((1u << LCH) - 1u);
+    // OR over the 16 lanes of each row, then the four rows side by side
+    cm = row_or16(cm);
+    uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)cm, 0) |
+                    ((uint32_t)__builtin_amdgcn_readlane((int)cm, 16) << LCH) |
+                    ((uint32_t)__builtin_amdgcn_readlane((int)cm, 32) << (2 * LCH)) |
+                    ((uint32_t)__builtin_amdgcn_readlane((int)cm, 48) << (3 * LCH));
     const double qd = (double)a.q;
-    // pass 0: exact maxima of the flagged channels (from the tokens near the fp32 max);
-    // pass 1: exact codes of the flagged values
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int wd = 0; wd < R / 32; ++wd) {
-        uint32_t bits = chmask[wd];
-        while (bits) {
-          const int c = 32 * wd + __builtin_ctz(bits);
-          bits &= bits - 1u;
-          const int gc = c / CL, k = c % CL;
-          const float ivc = invs[c];
+    // exact u of tile row r for channel c: lane l takes inputs l, l + 64, ...
+    auto exact_u = [&](int r, int c) {
+      double y = 0.0, ss = 0.0;
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            bool need = false;
-            if (g == gc) {
-              float uv = 0.f;   // u[s][k / 4][k % 4] (k is uniform: selects, no indexed registers)
+      for (int e = 0; e < R / 64; ++e) {
+        const int p = lane + 64 * e;
+        const uint32_t hw = *(const uint16_t*)(stage + r * ROWB + 16 * ((p >> 3) ^ (r % CPR)) + 2 * (p & 7));
+        const double x = widen64<DT>(hw);
+        ss = __builtin_fma(x, x, ss);
+        const int hv = LG == 0 ? (p == c ? 1 : 0) : hval<LG>(c, p);
+        if (hv != 0) y += ((hv < 0) != (LG != 0 && sg[p] < 0)) ? -x : x;
+      }
+      y = wave_sum64(y);
+      ss = wave_sum64(ss);
+      const double nu = sqrt(ss);
+      return a.nsep ? (nu > 0.0 ? y / nu : 0.0) : y;
+    };
+    while (bits) {
+      const int cl = __builtin_ctz(bits);                   // channel (R/4) w + cl
+      bits &= bits - 1u;
+      const int gc = cl / LCH, q = cl % LCH;
+      const int c = (R / 4) * w + cl;
+      // pass 0: exact max over the candidate tokens; pass 1: exact codes of flagged values
+      double mm = 0.0;
+#pragma unroll 1
+      for (int pass = 0; pass < 2; ++pass) {
+        const uint64_t src = pass == 0 ? cbm : fbm;
 #pragma unroll
-              for (int I = 0; I < NI; ++I)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (4 * I + r == k) uv = u[s][I][r];
-              need = pass == 0 ? fabsf(uv) * ivc >= a.q * (1.f - 0x1p-12f) : ((cm[s] >> k) & 1u) != 0u;
-            }
-            need = __shfl(need ? 1 : 0, j + 16 * gc) != 0;
-            double y = 0.0, ss = 0.0;
-            if (need) {
-              const unsigned char* xr =
-                  (const unsigned char*)a.x + (((row0 + 16 * s + j) * a.heads + h) * R + CL * g) * 2;
-              const ExactParts ep = exact_parts<DT, R, LG>(xr, sgh, CL * g, c);
-              y = ep.y;
-              ss = ep.ss;
-            }
-            y += __shfl_xor(y, 16);
-            y += __shfl_xor(y, 32);
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            if (need && g == gc) {
-              const double nu = sqrt(ss);
-              const double uv = a.nsep ? (nu > 0.0 ? y / nu : 0.0) : y;
-              if (pass == 0) {
-                atomicMax(&m64[c], __builtin_bit_cast(unsigned long long, fabs(uv)));
-              } else {
-                const double mm = __builtin_bit_cast(double, m64[c]);
-                const uint32_t nib = mm > 0.0 ? exact_nibble(qd * uv / mm) : 0u;
-                const int sh = 4 * (k & 7);
-#pragma unroll
-                for (int d = 0; d < NP; ++d)
-                  if (d == (k >> 3)) pk[s][d] = (pk[s][d] & ~(0xFu << sh)) | (nib << sh);
-              }
+        for (int s = 0; s < ST; ++s) {
+          const bool need = g == gc && ((src >> (LCH * s + q)) & 1ull) != 0ull;
+          uint64_t tok = (__ballot(need) >> (16 * gc)) & 0xffffull;
+          while (tok) {
+            const int jt = __builtin_ctzll(tok);
+            tok &= tok - 1ull;
+            const double uex = exact_u(16 * s + jt, c);
+            if (pass == 0) {
+              mm = fmax(mm, fabs(uex));
+            } else if (lane == 16 * gc + jt) {
+              const uint32_t nib = mm > 0.0 ? exact_nibble(qd * uex / mm) : 0u;
+              const int sh = 4 * q;
+              pk[s] = (pk[s] & ~(0xFu << sh)) | (nib << sh);
             }
           }
         }
       }
-      lds_barrier();
     }
   }
 
-  // 6. codes: 16 bytes per lane and sub-tile (R = 128)
+  // 8. codes -> LDS rows (every wave is done with the staged input), then whole rows out:
+  //    wave w stores tokens [w B/4, (w + 1) B/4), one 64-byte (R = 128) row per 4 lanes
+  lds_barrier();
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    unsigned char* cp = a.codes + ((row0 + 16 * s + j) * a.heads + h) * (R / 2) + (R / 8) * g;
-    if constexpr (NP == 4)
-      __builtin_nontemporal_store(u32x4{pk[s][0], pk[s][1], pk[s][2], pk[s][3]}, (u32x4*)cp);
+  for (int s = 0; s < ST; ++s) {
+    unsigned char* cp = stage + (16 * s + j) * RB + (R / 8) * w + (LCH / 2) * g;
+    if constexpr (R == 128)
+      *(uint32_t*)cp = pk[s];
     else
-      __builtin_nontemporal_store(u32x2{pk[s][0], pk[s][1]}, (u32x2*)cp);
+      *(uint16_t*)cp = (uint16_t)pk[s];
+  }
+  lds_barrier();
+  constexpr int PPR = RB / 16;                              // 16-byte pieces per code row
+  constexpr int PIECES = (B / 4) * PPR;                     // per wave
+  unsigned char* cb = a.codes + ((row0 + (B / 4) * w) * a.heads + h) * RB;
+  const uint32_t code_row = (uint32_t)(a.heads * RB);
+#pragma unroll
+  for (int k = 0; k < (PIECES + 63) / 64; ++k) {
+    const int pc = 64 * k + lane;
+    if (PIECES % 64 == 0 || pc < PIECES) {
+      const int t = pc / PPR, o = 16 * (pc % PPR);
+      const u32x4 cv = *(const u32x4*)(stage + ((B / 4) * w + t) * RB + o);
+      *(u32x4*)(cb + (uint32_t)t * code_row + o) = cv;
+    }
   }
 }
 
 template <int DT, int R, int LG>
 void launch_r(const QuantArgs& a, hipStream_t st) {
   const int64_t ntiles = a.seqs * (a.tokens / a.block) * a.heads;
-  if (a.block == 64)
-    hipLaunchKernelGGL((quant_pchan_mfma<DT, R, LG, 2>), dim3((unsigned)ntiles), dim3(128), 0, st, a, ntiles);
-  else if (a.block == 128)
-    hipLaunchKernelGGL((quant_pchan_mfma<DT, R, LG, 4>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles);
-  else if constexpr (R == 64)
-    hipLaunchKernelGGL((quant_pchan_mfma<DT, R, LG, 8>), dim3((unsigned)ntiles), dim3(512), 0, st, a, ntiles);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles); };
+  if (a.block == 64) go(quant_pchan_tile<DT, R, LG, 64>);
+  else if (a.block == 128) go(quant_pchan_tile<DT, R, LG, 128>);
+  else if constexpr (R == 64) go(quant_pchan_tile<DT, R, LG, 256>);
 }
 
 template <int DT, int R>

@@ -76,6 +76,11 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle baseline sample (0 = skip)")
     ap.add_argument("--traffic", type=str, default=None,
                     help="JSON file with rocprofv3-derived HBM bytes per quantize launch")
+    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode"), default=None,
+                    help="run just this kernel in each step (for profiler runs; no cpu baseline)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain device-to-device copy of the fp16 input (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the quantize / dequantize / decode-score path has no "
@@ -102,15 +107,39 @@ def main():
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        del y
+        y = torch.empty_like(x)
+        for _ in range(args.warmup):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            y.copy_(x)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        nbytes = x.numel() * x.element_size()
+        print(json.dumps({"calibrate_copy": {"bytes_read": nbytes, "bytes_written": nbytes, "us": round(us, 2),
+                                             "GB/s": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}}), flush=True)
+        return
     names = ("quantize", "dequantize", "score_decode")
+    run = {n: args.only in (None, n) for n in names}
+
+    if args.only not in (None, "quantize"):
+        kvq.quantize(d, x, signs, out=(codes, norms, scales), stream=stream)   # the cache it reads
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        kvq.quantize(d, x, signs, out=(codes, norms, scales), stream=stream)
+        if run["quantize"]:
+            kvq.quantize(d, x, signs, out=(codes, norms, scales), stream=stream)
         if ev: ev[1].record(stream)
-        kvq.dequantize(d, codes, norms, scales, signs, out=y, stream=stream)
+        if run["dequantize"]:
+            kvq.dequantize(d, codes, norms, scales, signs, out=y, stream=stream)
         if ev: ev[2].record(stream)
-        kvq.score_decode(d, q, codes, norms, scales, signs, out=scores, stream=stream)
+        if run["score_decode"]:
+            kvq.score_decode(d, q, codes, norms, scales, signs, out=scores, stream=stream)
         if ev: ev[3].record(stream)
 
     for _ in range(args.warmup):
@@ -127,15 +156,20 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     b = algorithmic_bytes(w, w.q_heads)
-    step_bytes = b["quantize"] + b["dequantize"] + b["score_decode"]
+    step_bytes = sum(b[n] for n in names if run[n])
     kernels = {}
     for n in names:
+        if not run[n]:
+            continue
         gbs = b[n] / (per_kernel_ms[n] * 1e-3) / 1e9
         kernels[n] = {"us": round(per_kernel_ms[n] * 1e3, 2), "bytes": b[n], "GB/s": round(gbs, 1),
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         traffic = json.load(open(args.traffic)).get("quantize_bytes_per_launch")
+    if args.only:
+        print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
+        return
     qa = kernels["quantize"]["GB/s"]
     out = {
         "metric": "quantize/dequant/decode-score GB/s and % of HBM peak, 1x MI355X",
