@@ -41,6 +41,25 @@ def algorithmic_bytes(w, q_heads):
             "elements": n}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "long_context_hbm_traffic.md")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    or None when there is none or the kernel source has changed since it was taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) == 5 and f[0] == "traffic" and f[1] == kernel:
+            kv = dict(x.split("=", 1) for x in f[2:])
+            src = os.path.join(ROOT, kv["source"])
+            if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == kv["sha256"]:
+                return int(kv["bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(w, n_seqs: int):
     """The fp64 oracle (as it stands) on the first n_seqs sequences, one at a time."""
     import threadpoolctl
@@ -74,8 +93,6 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle baseline sample (0 = skip)")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with rocprofv3-derived HBM bytes per quantize launch")
     ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode"), default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -164,9 +181,7 @@ def main():
         gbs = b[n] / (per_kernel_ms[n] * 1e-3) / 1e9
         kernels[n] = {"us": round(per_kernel_ms[n] * 1e3, 2), "bytes": b[n], "GB/s": round(gbs, 1),
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("quantize_bytes_per_launch")
+    traffic = measured_traffic("quantize")
     if args.only:
         print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
         return
