@@ -63,22 +63,23 @@ __global__ void __launch_bounds__(256) dequant_pchan_kernel(DequantArgs a, int64
   const int tid = threadIdx.x;
   unsigned char* stage = smem;
 
+  // tiles numbered along the head-major streams (block fastest)
   const int64_t tile = xcd_tile(blockIdx.x, ntiles);
   const int64_t nb = a.tokens / B;
-  const int64_t h = tile % a.heads;
-  const int64_t sb = tile / a.heads;
-  const int64_t s = sb / nb, blk = sb - s * nb;
+  const int64_t hs = tile / nb, blk = tile - hs * nb;   // hs = s * heads + h
+  const int64_t s = hs / a.heads, h = hs - s * a.heads;
   const int64_t row0 = s * a.tokens + blk * B;
+  const int64_t tok0 = hs * a.tokens + blk * B;
 
-  const unsigned char* cbase = a.codes + (row0 * a.heads + h) * CRB;
+  const unsigned char* cbase = a.codes + tok0 * CRB;  // the tile's codes: one contiguous block
 #pragma unroll
   for (int k = 0; k < CCR; ++k) {
     const int q = tid + k * B;
     const int row = q / CCR, cc = q % CCR;
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(cbase + (int64_t)row * a.heads * CRB + cc * 16));
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(cbase + q * 16));
     *(u32x4*)(stage + row * CRB + swz_chunk(row, cc, CRB) * 16) = v;
   }
-  const float nrm = a.nsep ? f16_to_f32(a.norms[(row0 + tid) * a.heads + h]) : 1.f;
+  const float nrm = a.nsep ? f16_to_f32(a.norms[tok0 + tid]) : 1.f;
   __syncthreads();
   uint32_t cw[R / 8];
 #pragma unroll
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__(256) dequant_pchan_kernel(DequantArgs a, int64
   }
   __syncthreads();
 
-  const uint16_t* sc = a.scales + (sb * a.heads + h) * R;
+  const uint16_t* sc = a.scales + (hs * nb + blk) * R;
   float y[R];
 #pragma unroll
   for (int i = 0; i < R / 8; ++i) {
@@ -131,24 +132,29 @@ __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t
   const int64_t seg0 = xcd_tile(blockIdx.x, ntiles) * 64;
   const int nvalid = (int)(nseg - seg0 < 64 ? nseg - seg0 : 64);
 
-  const unsigned char* cbase = a.codes + seg0 * CRB;
+  const int L = 1 << lgL;
+  // codes are head-major: segment `sg` (x order) is segment head_major(vector) L + part
 #pragma unroll
   for (int k = 0; k < CCR; ++k) {
     const int q = lane + k * 64;
     const int row = q / CCR, cc = q % CCR;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < nvalid) v = __builtin_nontemporal_load((const u32x4*)(cbase + row * CRB + cc * 16));
+    if (row < nvalid) {
+      const int64_t sg = seg0 + row;
+      const int64_t src = a.heads == 1 ? sg : (head_major(a.heads, a.tokens, sg >> lgL) << lgL) + (sg & (L - 1));
+      v = __builtin_nontemporal_load((const u32x4*)(a.codes + src * CRB + cc * 16));
+    }
     *(u32x4*)(stage + row * CRB + swz_chunk(row, cc, CRB) * 16) = v;
   }
-  const int L = 1 << lgL;
   const int64_t seg = seg0 + lane;
   const int64_t vec = seg >> lgL;
   const int part = (int)(seg & (L - 1));
   const int64_t h = vec % a.heads;
   float f = 0.f;
   if (lane < nvalid) {
-    f = f16_to_f32(a.scales[vec]);
-    if (a.nsep) f *= f16_to_f32(a.norms[vec]);
+    const int64_t vh = head_major(a.heads, a.tokens, vec);
+    f = f16_to_f32(a.scales[vh]);
+    if (a.nsep) f *= f16_to_f32(a.norms[vh]);
   }
   wave_lds_sync();
   uint32_t cw[R / 8];

@@ -56,6 +56,15 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
   return x * per + (x < rem ? x : rem) + k;
 }
 
+// Outputs are head-major: the (token, head) vector at x row `row` = s T + t, head h (x index
+// row * heads + h) is entry (s heads + h) T + t of the codes / norms / scales streams.
+__device__ __forceinline__ int64_t head_major(int64_t heads, int64_t tokens, int64_t vec) {
+  if (heads == 1) return vec;
+  const int64_t h = vec % heads, row = vec / heads;
+  const int64_t s = row / tokens;
+  return (s * heads + h) * tokens + (row - s * tokens);
+}
+
 // 16-byte-chunk XOR swizzle for LDS tiles of `row_bytes` per row (power of two, >= 16):
 // consecutive rows land on different bank groups for both row-wise and chunk-wise access.
 __device__ __forceinline__ int swz_chunk(int row, int cc, int row_bytes) {

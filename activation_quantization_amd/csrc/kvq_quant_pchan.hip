@@ -134,7 +134,7 @@ template <int R, int LG> __device__ __forceinline__ constexpr int frag_beta(int 
 }
 
 template <int DT, int R, int LG, int B>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   constexpr int NK = R / 32;            // K steps of the contraction
   constexpr int NIW = R / 64;           // output I-blocks per wave
@@ -149,18 +149,24 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   constexpr int RB = R / 2;             // code row bytes
   static_assert(ST % 4 == 0 && NLD >= 1, "tile shape");
   // the tile's input rows; once every wave is done with them, the packed code rows
-  // [token][R/2 bytes] (wave w fills bytes [(R/8) w, (R/8)(w + 1)) of every row)
+  // [token][R/2 bytes] (wave w fills bytes [(R/8) w, (R/8)(w + 1)) of every row), which are
+  // then stored as one contiguous block (head-major codes)
   __shared__ __attribute__((aligned(16))) unsigned char stage[TSTAGE];
   __shared__ __attribute__((aligned(16))) int8_t sg[R];                 // the head's random signs
   __shared__ __attribute__((aligned(16))) float ninv[16 * ST];         // [j][s]: 1 / norm of token 16 s + j
 
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
-  const int64_t tile = xcd_tile(blockIdx.x, ntiles);
-  const int64_t h = tile % a.heads, sb = tile / a.heads;   // sb = sequence * (tokens / B) + block
-  const int64_t nb = a.tokens / B;
-  const int64_t seq = sb / nb;
-  const int64_t row0 = seq * a.tokens + (sb - seq * nb) * B;   // first token of the tile
+  // tile ids fit 32 bits (a tile holds >= 8 KiB of input); 32-bit divisions are much cheaper
+  // Tiles are numbered along the head-major output streams (block fastest), so the tiles in
+  // flight on one XCD write neighbouring blocks of one stream.
+  const uint32_t tile = (uint32_t)xcd_tile(blockIdx.x, ntiles);
+  const uint32_t nb = (uint32_t)(a.tokens / B);
+  const uint32_t hs32 = tile / nb, blk = tile - hs32 * nb;              // hs = seq * heads + h
+  const uint32_t seq = hs32 / (uint32_t)a.heads, h = hs32 - seq * (uint32_t)a.heads;
+  const int64_t row0 = (int64_t)seq * a.tokens + (int64_t)blk * B;   // x row of the tile's first token
+  const int64_t hs = hs32;                                            // (sequence, head) output stream
+  const int64_t tok0 = hs * a.tokens + (int64_t)blk * B;              // head-major index of that token
 
   // 1. this wave's B / 4 rows into LDS (instruction k moves 1 KiB; the chunk that lane p fetches
   //    is XOR-swizzled with its row, so slot cc of row r holds chunk cc ^ (r % CPR) and the
@@ -221,13 +227,13 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
     const float rinv = ssq > 0.f ? rq : 0.f;
     if (g == 0) {
       ninv[j * ST + s] = a.nsep ? rinv : 1.f;
-      if (a.nsep) a.norms[(row0 + 16 * s + j) * a.heads + h] = (uint16_t)f32_to_f16(ssq * rinv);   // sqrt(ssq)
+      if (a.nsep) a.norms[tok0 + 16 * s + j] = (uint16_t)f32_to_f16(ssq * rinv);   // sqrt(ssq)
     }
   }
 
   // 3. the rotation of this wave's channels, sub-tile by sub-tile (unnormalized)
   f32x4 u[ST][NIW];
-  auto rotate = [&](auto wc, int only_s, f32x4 (&ur)[NIW]) {
+  auto rotate = [&](auto wc) {
     constexpr int W = decltype(wc)::value;
     // fragments of the nonzero blocks of this wave, signed for the head
     u32x4 fk[NK][NIW];
@@ -271,12 +277,6 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
         }
       }
     };
-    if (only_s >= 0) {                                      // one sub-tile, for the rare path
-#pragma unroll
-      for (int s = 0; s < ST; ++s)
-        if (s == only_s) one(s, ur);
-      return;
-    }
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
       one(s, u[s]);
@@ -284,17 +284,11 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto run = [&](int only_s, f32x4 (&ur)[NIW]) {
-    switch (w) {
-      case 0: rotate(std::integral_constant<int, 0>{}, only_s, ur); break;
-      case 1: rotate(std::integral_constant<int, 1>{}, only_s, ur); break;
-      case 2: rotate(std::integral_constant<int, 2>{}, only_s, ur); break;
-      default: rotate(std::integral_constant<int, 3>{}, only_s, ur); break;
-    }
-  };
-  {
-    f32x4 unused[NIW];
-    run(-1, unused);
+  switch (w) {
+    case 0: rotate(std::integral_constant<int, 0>{}); break;
+    case 1: rotate(std::integral_constant<int, 1>{}); break;
+    case 2: rotate(std::integral_constant<int, 2>{}); break;
+    default: rotate(std::integral_constant<int, 3>{}); break;
   }
 
   // 4. every wave's norms are published: u = y / norm, the per-channel maxima over the tile
@@ -329,7 +323,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
     iv[q] = m > 0.f ? a.q * __builtin_amdgcn_rcpf(m) : 0.f;
     if (q == j) s16 = f32_to_f16(m * a.scale_mul);
   }
-  if (j < LCH) a.scales[(sb * a.heads + h) * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
+  if (j < LCH) a.scales[(hs * nb + blk) * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
 
   // 6. codes and near-tie flags
   uint32_t pk[ST];
@@ -352,27 +346,18 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
     pk[s] = pack8(b);
   }
 
-  // 7. rare path, wave-local: exact re-decision of this wave's near-ties.  u is recomputed
-  //    from the staged rows with the same instructions (bit-identical), so the main path need
-  //    not keep it alive.
+  // 7. rare path, wave-local: exact re-decision of this wave's near-ties (u is still live)
   if (__ballot((fl & 0xffffu) == 0u) != 0ull) {
-    uint64_t fbm = 0ull, cbm = 0ull;                        // bit LCH s + q: near-tie / near-max
-#pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 us[NIW];
-      run(s, us);
-#pragma unroll
-      for (int q = 0; q < LCH; ++q) {
-        const float uq = us[q >> 2][q & 3] * rn[s];
-        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_fmaf(uq, iv[q], CODE_MAGIC));
-        if ((bb & 0xffffu) == 0u) fbm |= 1ull << (LCH * s + q);
-        if (fabsf(uq) * iv[q] >= a.q * (1.f - 0x1p-12f)) cbm |= 1ull << (LCH * s + q);
-      }
-    }
     uint32_t cm = 0u;                                       // bit q: channel (R/4) w + LCH g + q
 #pragma unroll
-    for (int s = 0; s < ST; ++s) cm |= (uint32_t)(fbm >> (LCH * s)) & ((1u << LCH) - 1u);
+    for (int q = 0; q < LCH; ++q) {
+      uint32_t mn = 0xffffffffu;
+#pragma unroll
+      for (int s = 0; s < ST; s += 2)
+        mn = min3_u16(mn, __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s][q >> 2][q & 3], iv[q], CODE_MAGIC)),
+                      __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s + 1][q >> 2][q & 3], iv[q], CODE_MAGIC)));
+      cm |= ((mn & 0xffffu) == 0u ? 1u : 0u) << q;
+    }
     // OR over the 16 lanes of each row, then the four rows side by side
     cm = row_or16(cm);
     uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)cm, 0) |
@@ -397,20 +382,21 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
       const double nu = sqrt(ss);
       return a.nsep ? (nu > 0.0 ? y / nu : 0.0) : y;
     };
-    while (bits) {
-      const int cl = __builtin_ctz(bits);                   // channel (R/4) w + cl
-      bits &= bits - 1u;
-      const int gc = cl / LCH, q = cl % LCH;
-      const int c = (R / 4) * w + cl;
-      // pass 0: exact max over the candidate tokens; pass 1: exact codes of flagged values
+    // one flagged channel; its lane slot Q is a compile-time constant, so u and iv are plain
+    // registers (pass 0: exact max over the tokens near the fp32 max; pass 1: exact codes of
+    // the flagged values)
+    auto fix_channel = [&](auto qc, int gc, int c) {
+      constexpr int Q = decltype(qc)::value;
       double mm = 0.0;
 #pragma unroll 1
       for (int pass = 0; pass < 2; ++pass) {
-        const uint64_t src = pass == 0 ? cbm : fbm;
 #pragma unroll
         for (int s = 0; s < ST; ++s) {
-          const bool need = g == gc && ((src >> (LCH * s + q)) & 1ull) != 0ull;
-          uint64_t tok = (__ballot(need) >> (16 * gc)) & 0xffffull;
+          const float uq = u[s][Q >> 2][Q & 3];
+          const bool hit = pass == 0
+                               ? fabsf(uq) * iv[Q] >= a.q * (1.f - 0x1p-12f)
+                               : (__builtin_bit_cast(uint32_t, __builtin_fmaf(uq, iv[Q], CODE_MAGIC)) & 0xffffu) == 0u;
+          uint64_t tok = (__ballot(g == gc && hit) >> (16 * gc)) & 0xffffull;
           while (tok) {
             const int jt = __builtin_ctzll(tok);
             tok &= tok - 1ull;
@@ -419,17 +405,37 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
               mm = fmax(mm, fabs(uex));
             } else if (lane == 16 * gc + jt) {
               const uint32_t nib = mm > 0.0 ? exact_nibble(qd * uex / mm) : 0u;
-              const int sh = 4 * q;
-              pk[s] = (pk[s] & ~(0xFu << sh)) | (nib << sh);
+              pk[s] = (pk[s] & ~(0xFu << (4 * Q))) | (nib << (4 * Q));
             }
           }
         }
       }
+    };
+    while (bits) {
+      const int cl = __builtin_ctz(bits);                   // channel (R/4) w + cl
+      bits &= bits - 1u;
+      const int gc = cl / LCH, c = (R / 4) * w + cl;
+      switch (cl % LCH) {
+        case 0: fix_channel(std::integral_constant<int, 0>{}, gc, c); break;
+        case 1: fix_channel(std::integral_constant<int, 1>{}, gc, c); break;
+        case 2: fix_channel(std::integral_constant<int, 2>{}, gc, c); break;
+        case 3: fix_channel(std::integral_constant<int, 3>{}, gc, c); break;
+        default:
+          if constexpr (LCH == 8) {
+            switch (cl % LCH) {
+              case 4: fix_channel(std::integral_constant<int, 4 % LCH>{}, gc, c); break;
+              case 5: fix_channel(std::integral_constant<int, 5 % LCH>{}, gc, c); break;
+              case 6: fix_channel(std::integral_constant<int, 6 % LCH>{}, gc, c); break;
+              default: fix_channel(std::integral_constant<int, 7 % LCH>{}, gc, c); break;
+            }
+          }
+          break;
+      }
     }
   }
 
-  // 8. codes -> LDS rows (every wave is done with the staged input), then whole rows out:
-  //    wave w stores tokens [w B/4, (w + 1) B/4), one 64-byte (R = 128) row per 4 lanes
+  // 8. codes -> LDS rows (every wave is done with the staged input), then the tile's code
+  //    block out in contiguous 16-byte pieces
   lds_barrier();
 #pragma unroll
   for (int s = 0; s < ST; ++s) {
@@ -440,18 +446,14 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
       *(uint16_t*)cp = (uint16_t)pk[s];
   }
   lds_barrier();
-  constexpr int PPR = RB / 16;                              // 16-byte pieces per code row
-  constexpr int PIECES = (B / 4) * PPR;                     // per wave
-  unsigned char* cb = a.codes + ((row0 + (B / 4) * w) * a.heads + h) * RB;
-  const uint32_t code_row = (uint32_t)(a.heads * RB);
+  // the tile's codes are one contiguous block of B R/2 bytes; wave w stores its quarter
+  constexpr int WPIECES = B * RB / 64;                      // 16-byte pieces per wave
+  unsigned char* cb = a.codes + tok0 * RB + w * (B * RB / 4);
 #pragma unroll
-  for (int k = 0; k < (PIECES + 63) / 64; ++k) {
+  for (int k = 0; k < (WPIECES + 63) / 64; ++k) {
     const int pc = 64 * k + lane;
-    if (PIECES % 64 == 0 || pc < PIECES) {
-      const int t = pc / PPR, o = 16 * (pc % PPR);
-      const u32x4 cv = *(const u32x4*)(stage + ((B / 4) * w + t) * RB + o);
-      *(u32x4*)(cb + (uint32_t)t * code_row + o) = cv;
-    }
+    if (WPIECES % 64 == 0 || pc < WPIECES)
+      *(u32x4*)(cb + 16 * pc) = *(const u32x4*)(stage + w * (B * RB / 4) + 16 * pc);
   }
 }
 

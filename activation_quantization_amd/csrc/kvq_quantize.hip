@@ -317,15 +317,17 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
   const int L = 1 << lgL;
   const int64_t G = gridDim.x;
   const int64_t full_tiles = nseg / 64;                         // tiles without a ragged tail
+  // codes are head-major: segment `seg` (x order) goes to segment head_major(vector) L + part
   auto store_codes = [&](int64_t seg0, int nvalid) {
-    unsigned char* cb = a.codes + seg0 * CRB;
 #pragma unroll
     for (int k = 0; k < CCR; ++k) {
       const int q = lane + k * 64;
       const int row = q / CCR, cc = q % CCR;
       if (row < nvalid) {
         const u32x4 t = *(const u32x4*)(stage_codes + row * CRB + swz_chunk(row, cc, CRB) * 16);
-        __builtin_nontemporal_store(t, (u32x4*)(cb + row * CRB + cc * 16));
+        const int64_t sg = seg0 + row;
+        const int64_t dst = a.heads == 1 ? sg : (head_major(a.heads, a.tokens, sg >> lgL) << lgL) + (sg & (L - 1));
+        __builtin_nontemporal_store(t, (u32x4*)(a.codes + dst * CRB + cc * 16));
       }
     }
   };
@@ -409,9 +411,10 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     if (ball) ptok_exact<DT, R, LG>(a, ball, seg0, lgL, xb, stage_codes, F);
     if (part == 0 && lane < nvalid) {
       const float nu = sqrtf(ss);
-      if (a.nsep) a.norms[vec] = (uint16_t)f32_to_f16(nu);
+      const int64_t vh = head_major(a.heads, a.tokens, vec);
+      if (a.nsep) a.norms[vh] = (uint16_t)f32_to_f16(nu);
       const float scale = a.nsep ? (nu > 0.f ? m * a.scale_mul / nu : 0.f) : m * a.scale_mul;
-      a.scales[vec] = (uint16_t)f32_to_f16(scale);
+      a.scales[vh] = (uint16_t)f32_to_f16(scale);
     }
     wave_lds_sync();
     pseg0 = seg0;

@@ -101,14 +101,14 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   if (t_end > T) t_end = T;
   const int64_t nb = a.per_channel ? T / a.block : 1;
   int64_t cur = -1;
-  const int64_t rowbase = s * T;
+  const int64_t rowbase = (s * a.heads + kvh) * T;   // head-major (sequence, KV head) stream
   constexpr int CRB = R / 2;
 
   for (int64_t t0 = t_begin; t0 < t_end; t0 += 64) {
     if (a.per_channel) {
       const int64_t blk = t0 / a.block;
       if (blk != cur) {
-        build(a.scales + ((s * nb + blk) * a.heads + kvh) * R);
+        build(a.scales + ((s * a.heads + kvh) * nb + blk) * R);
         cur = blk;
       }
     }
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
       const int64_t t = t0 + 16 * tg + (lane & 15);
       uint32_t wd[KS];
       if (t < T) {
-        const unsigned char* cp = a.codes + ((rowbase + t) * a.heads + kvh) * CRB + grp * (KS * 4);
+        const unsigned char* cp = a.codes + (rowbase + t) * CRB + grp * (KS * 4);
         if constexpr (KS == 4) {
           const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
           wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
       const int64_t t = t0 + 16 * tg + (lane & 15);
       if (t >= T) continue;
       float f = 1.f;
-      const int64_t rix = (rowbase + t) * a.heads + kvh;
+      const int64_t rix = rowbase + t;
       if (a.nsep) f = f16_to_f32(a.norms[rix]);
       if (!a.per_channel) f *= f16_to_f32(a.scales[rix]);
 #pragma unroll

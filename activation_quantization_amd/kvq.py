@@ -111,13 +111,17 @@ class Desc:
     def scales_count(self) -> int:
         return lib().kvq_scales_count(ctypes.byref(self.c()))
 
+    # outputs are head-major: [seqs, heads, tokens, ...] (see include/kvq.h)
     def codes_shape(self):
-        return (self.rows, self.heads, self.head_dim // 2)
+        return (self.seqs, self.heads, self.tokens_per_seq, self.head_dim // 2)
+
+    def norms_shape(self):
+        return (self.seqs, self.heads, self.tokens_per_seq)
 
     def scales_shape(self):
         if self.per_channel:
-            return (self.rows // self.block_tokens, self.heads, self.head_dim)
-        return (self.rows, self.heads)
+            return (self.seqs, self.heads, self.tokens_per_seq // self.block_tokens, self.head_dim)
+        return (self.seqs, self.heads, self.tokens_per_seq)
 
 
 def _ptr(t):
@@ -143,7 +147,7 @@ def _need_cuda(*ts):
 
 def alloc_outputs(d: Desc, device):
     codes = torch.empty(d.codes_shape(), dtype=torch.uint8, device=device)
-    norms = torch.empty((d.rows, d.heads), dtype=torch.float16, device=device) if d.nsep else None
+    norms = torch.empty(d.norms_shape(), dtype=torch.float16, device=device) if d.nsep else None
     scales = torch.empty(d.scales_shape(), dtype=torch.float16, device=device)
     return codes, norms, scales
 
@@ -184,3 +188,36 @@ def score_decode(d: Desc, q: torch.Tensor, codes, norms, scales, signs=None,
                                 _ptr(scales), _ptr(signs), _ptr(out), _stream(stream))
     _check(st, "kvq_score_decode")
     return out
+
+
+def token_major(d: Desc, codes=None, norms=None, scales=None):
+    """Views of kvq_quantize's head-major outputs in x's token-major order (new contiguous
+    tensors): codes [rows, heads, head_dim/2], norms [rows, heads], scales [rows, heads] or
+    [rows/B, heads, head_dim].  Pure data movement; None passes through."""
+    S, H, T, D, D2 = d.seqs, d.heads, d.tokens_per_seq, d.head_dim, d.head_dim // 2
+    c = None if codes is None else codes.reshape(S, H, T, D2).transpose(1, 2).reshape(S * T, H, D2).contiguous()
+    n = None if norms is None else norms.reshape(S, H, T).transpose(1, 2).reshape(S * T, H).contiguous()
+    sc = None
+    if scales is not None:
+        if d.per_channel:
+            nb = T // d.block_tokens
+            sc = scales.reshape(S, H, nb, D).transpose(1, 2).reshape(S * nb, H, D).contiguous()
+        else:
+            sc = scales.reshape(S, H, T).transpose(1, 2).reshape(S * T, H).contiguous()
+    return c, n, sc
+
+
+def head_major(d: Desc, codes=None, norms=None, scales=None):
+    """Inverse of token_major: token-major codes / norms / scales -> the head-major layout the
+    kernels read (new contiguous tensors)."""
+    S, H, T, D, D2 = d.seqs, d.heads, d.tokens_per_seq, d.head_dim, d.head_dim // 2
+    c = None if codes is None else codes.reshape(S, T, H, D2).transpose(1, 2).contiguous()
+    n = None if norms is None else norms.reshape(S, T, H).transpose(1, 2).contiguous()
+    sc = None
+    if scales is not None:
+        if d.per_channel:
+            nb = T // d.block_tokens
+            sc = scales.reshape(S, nb, H, D).transpose(1, 2).contiguous()
+        else:
+            sc = scales.reshape(S, T, H).transpose(1, 2).contiguous()
+    return c, n, sc

@@ -28,15 +28,17 @@
  *     launched and no output is touched.  kvq_last_error() then describes the failure
  *     (thread-local string).  No C++ exception crosses this interface.
  *
- * Storage formats
- *   codes   uint8 [rows, heads, head_dim/2]: two 4-bit two's-complement codes per byte,
- *           channel 2i in the low nibble, 2i+1 in the high nibble.  INT3 and 2-bit codes use
- *           the same nibble layout.  Codes lie in [-Q, Q], Q = 2^(bits-1)-1.
- *   norms   fp16 bits [rows, heads]: the L2 norm of each (rotated) vector; NSEP modes only.
- *   scales  fp16 bits.  Per-token modes (NAIVE, NSEP): [rows, heads] = absmax / Q of the
- *           (rotated, normalized) vector.  Per-channel modes (PCHAN, NSEP_PCHAN):
- *           [seqs * tokens_per_seq / block_tokens, heads, head_dim] = max over the block's
- *           tokens of |u| / Q, one per channel.
+ * Storage formats (outputs are head-major: every (sequence, head) is one contiguous stream,
+ * so a cache block of one head is whole cache lines for every kernel that touches it)
+ *   codes   uint8 [seqs, heads, tokens_per_seq, head_dim/2]: two 4-bit two's-complement codes
+ *           per byte, channel 2i in the low nibble, 2i+1 in the high nibble.  INT3 and 2-bit
+ *           codes use the same nibble layout.  Codes lie in [-Q, Q], Q = 2^(bits-1)-1.
+ *   norms   fp16 bits [seqs, heads, tokens_per_seq]: the L2 norm of each (rotated) vector;
+ *           NSEP modes only.
+ *   scales  fp16 bits.  Per-token modes (NAIVE, NSEP): [seqs, heads, tokens_per_seq] =
+ *           absmax / Q of the (rotated, normalized) vector.  Per-channel modes (PCHAN,
+ *           NSEP_PCHAN): [seqs, heads, tokens_per_seq / block_tokens, head_dim] = max over the
+ *           block's tokens of |u| / Q, one per channel.
  *   signs   int8 [heads, head_dim] of +-1 (any value < 0 counts as -1).  Block k of n
  *           channels of head h uses signs[h, k*n : (k+1)*n].  NULL iff hadamard == 0.
  */

@@ -34,12 +34,13 @@ def test_zero_vectors_and_zero_blocks(mode, had):
     d = kvq.Desc(S, T, H, D, 4, mode, 128 if "pchan" in mode else 0, had)
     run_full(d, x, signs)
     codes, norms, scales = kvq.quantize(d, x.to(DEV), None if signs is None else signs.to(DEV))
-    c = oracle.unpack_nibbles(codes.cpu().numpy())
+    tc, tn, ts = kvq.token_major(d, codes, norms, scales)
+    c = oracle.unpack_nibbles(tc.cpu().numpy())
     assert np.all(c[5] == 0) and np.all(c[128:256, 1] == 0)
     if d.nsep:
-        assert np.all(norms.cpu().numpy()[5] == 0)
+        assert np.all(tn.cpu().numpy()[5] == 0)
     if d.per_channel:
-        assert np.all(scales.cpu().numpy()[1, 1] == 0)
+        assert np.all(ts.cpu().numpy()[1, 1] == 0)
 
 
 @pytest.mark.parametrize("rows,heads,dim,had,mode", [
@@ -125,7 +126,7 @@ def test_exact_ties_are_rounded_half_even(mode, had):
     sg = None if signs is None else torch.from_numpy(signs).to(DEV)
     codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).half().to(DEV), sg)
     torch.cuda.synchronize()
-    got = oracle.unpack_nibbles(codes.cpu().numpy())
+    got = oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy())
     np.testing.assert_array_equal(got, want)
     # and the oracle agrees (its own decision in fp32 of the fp64 quotient)
     sp = oracle.Spec(1, 128, 2, 64, 4, mode, d.block_tokens if "pchan" in mode else 0, had)

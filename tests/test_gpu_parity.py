@@ -40,7 +40,8 @@ def run_full(d: kvq.Desc, x_cpu: torch.Tensor, signs_cpu, lowp_out=True, deq=Tru
     sp = spec_of(d)
     sg_np = None if signs_cpu is None else signs_cpu.numpy()
     ref = oracle.quantize(x_cpu.double().numpy(), sp, sg_np)
-    gc, gn, gs = codes.cpu().numpy(), np16(norms), np16(scales)
+    tc, tn, ts = kvq.token_major(d, codes, norms, scales)     # the oracle's [rows, heads, ...] order
+    gc, gn, gs = tc.cpu().numpy(), np16(tn), np16(ts)
     stats = parity.check_codes(gc, ref, d.bits)
     if d.nsep:
         parity.check_rel_f16(gn, ref.nu, "norms")
@@ -71,7 +72,7 @@ def test_grid_bit_exact(bits, mode, had, dtype):
     codes, norms, scales = kvq.quantize(d, x.to(DEV), sg)
     y = kvq.dequantize(d, codes, norms, scales, sg, torch.float32)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(oracle.unpack_nibbles(codes.cpu().numpy()), k)
+    np.testing.assert_array_equal(oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy()), k)
     np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), x64)
 
 
@@ -83,7 +84,7 @@ def test_grid_bit_exact_d128(mode):
     codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).half().to(DEV), sg)
     y = kvq.dequantize(d, codes, norms, scales, sg, torch.float32)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(oracle.unpack_nibbles(codes.cpu().numpy()), k)
+    np.testing.assert_array_equal(oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy()), k)
     np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), x64)
 
 
@@ -124,7 +125,7 @@ def _sampled_tiles(d: kvq.Desc, x_cpu, signs_cpu, codes, norms, scales, n_tiles,
     """Oracle on randomly chosen (seq, block, head) tiles of a full-size GPU run."""
     rng = np.random.default_rng(seed)
     B, nb = d.block_tokens, d.tokens_per_seq // d.block_tokens
-    gc, gn, gs = codes.cpu(), norms.cpu(), scales.cpu()
+    gc, gn, gs = (t.cpu() for t in kvq.token_major(d, codes, norms, scales))
     flips, checked = 0, 0
     for _ in range(n_tiles):
         s, b, h = int(rng.integers(d.seqs)), int(rng.integers(nb)), int(rng.integers(d.heads))
@@ -160,7 +161,8 @@ def _score_check(d: kvq.Desc, q_cpu, codes, norms, scales, signs_cpu, scores, pa
     G = q_cpu.shape[1] // d.heads
     T, nb = d.tokens_per_seq, (d.tokens_per_seq // d.block_tokens if d.per_channel else 0)
     worst = 0.0
-    gc, gn, gs, gsc = codes.cpu(), None if norms is None else norms.cpu(), scales.cpu(), scores.cpu()
+    tc, tn, ts = kvq.token_major(d, codes, norms, scales)
+    gc, gn, gs, gsc = tc.cpu(), None if tn is None else tn.cpu(), ts.cpu(), scores.cpu()
     for s, h in pairs:
         rows = slice(s * T, (s + 1) * T)
         sp = oracle.Spec(1, T, 1, d.head_dim, d.bits, d.mode, d.block_tokens if d.per_channel else 0, d.hadamard)
