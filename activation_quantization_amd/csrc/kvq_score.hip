@@ -9,12 +9,17 @@
 //
 // scores[s, hq, t] = sum_d q[s,hq,d] k^[s,t,hq/G,d]
 //                  = norm[t] * sum_d (R q)[d] * scale[blk(t), d] * code[t, d]
-// The rotated query times the block's per-channel scales (g, split into an fp16 hi/lo pair)
-// is the MFMA A operand (rows = the G query heads of one KV head, padded to 16); the codes
-// are the B operand (columns = 16 tokens), converted from nibbles to fp16 with two bit ops
-// per pair: (word ^ 0x88888888) >> 4j & 0x000F000F | 0x64006400 is the fp16 pair
-// (1032 + c_j, 1032 + c_{j+4}); subtracting 1032 is exact.  The K order inside a lane is
-// therefore [n0 n4 n1 n5 n2 n6 n3 n7]; the A operand uses the same order.
+//
+// Work: a workgroup takes a chunk of one head-major (sequence, KV head) stream; each wave
+// walks units of U tokens (U = the scale block for per-channel modes, 128 otherwise).  Per unit
+// the wave issues all of its loads at once (16 bytes of codes per lane and 16-token group, the
+// unit's scale row, the norms), then builds the MFMA A operand: g = (R q) * scale in fp32, split
+// into an fp16 hi/lo pair, rows 2 h + {0, 1} = (hi, lo) of query head h (8 heads per pass).
+// The B operand is 16 tokens x 32 channels of codes, converted from nibbles to fp16 with two
+// bit operations per pair: (word ^ 0x88888888) >> 4i & 0x000F000F | 0x64006400 is the fp16 pair
+// (1032 + c_i, 1032 + c_{i+4}); subtracting 1032 is exact.  The K order inside a lane is
+// therefore [n0 n4 n1 n5 n2 n6 n3 n7]; the A operand uses the same order.  Lane (g, j) of the
+// result holds rows 4 g + r: heads 2 g and 2 g + 1 (hi and lo rows summed) of token j.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -37,22 +42,28 @@ __device__ __forceinline__ f16x8 codes_to_f16(uint32_t word) {
   return r;
 }
 
+constexpr int SCORE_UNITS_PER_BLOCK = 16;
+
 template <int R>
-__global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int chunk) {
+__global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
+                                                    int vec_scales) {
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
-  __shared__ float qr[16 * R];             // rotated queries of this KV head's group
+  constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
+  __shared__ __attribute__((aligned(16))) float qr[16 * R];   // rotated queries of this KV head's group
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
   const int G = (int)(a.q_heads / a.heads);
+  const int64_t T = a.tokens;
 
   const int64_t tile = xcd_tile(blockIdx.x, ntiles);
   const int64_t ci = tile % nchunks;
-  const int64_t sh = tile / nchunks;
+  const int64_t sh = tile / nchunks;                        // head-major stream: s * heads + kvh
   const int64_t kvh = sh % a.heads, s = sh / a.heads;
 
-  // 1. rotated queries R q = (1/sqrt n) H (sigma * q), once per workgroup
+  // 1. rotated queries R q = (1/sqrt n) H (sigma * q), once per workgroup (butterflies in LDS)
   for (int e = tid; e < G * R; e += 256) {
-    const int g = e / R, d = e % R;
-    float v = f16_to_f32(a.q[(s * a.q_heads + kvh * G + g) * R + d]);
+    const int hh = e / R, d = e % R;
+    float v = f16_to_f32(a.q[(s * a.q_heads + kvh * G + hh) * R + d]);
     if (a.lg_had && a.signs[kvh * R + d] < 0) v = -v;
     qr[e] = v;
   }
@@ -60,110 +71,123 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   for (int st = 0; st < a.lg_had; ++st) {
     const int half = 1 << st;
     for (int p = tid; p < G * R / 2; p += 256) {
-      const int g = p / (R / 2), pp = p % (R / 2);
+      const int hh = p / (R / 2), pp = p % (R / 2);
       const int i = ((pp >> st) << (st + 1)) | (pp & (half - 1));   // index with bit st clear
-      const float u = qr[g * R + i], v = qr[g * R + i + half];
-      qr[g * R + i] = u + v;
-      qr[g * R + i + half] = u - v;
+      const float u = qr[hh * R + i], v = qr[hh * R + i + half];
+      qr[hh * R + i] = u + v;
+      qr[hh * R + i + half] = u - v;
     }
     __syncthreads();
   }
+  if (a.lg_had) {
+    for (int e = tid; e < G * R; e += 256) qr[e] *= a.inv_sqrt_n;
+    __syncthreads();
+  }
 
-  // 2. this lane's slice of the A operand: row i = lane & 15 (query head), K group lane >> 4
-  const int ri = lane & 15, grp = lane >> 4;
-  const bool live = ri < G;
-  float qv[KS * 8];
-#pragma unroll
-  for (int sk = 0; sk < KS; ++sk)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qv[sk * 8 + e] = live ? qr[ri * R + 8 * (KS * grp + sk) + nib_of(e)] * a.inv_sqrt_n : 0.f;
+  const int NHC = (G + 7) / 8;                              // passes of 8 query heads
+  const int64_t nunits = (T + U - 1) / U;
+  const int64_t u_begin = ci * SCORE_UNITS_PER_BLOCK;
+  const int64_t u_end = u_begin + SCORE_UNITS_PER_BLOCK < nunits ? u_begin + SCORE_UNITS_PER_BLOCK : nunits;
+  const unsigned char* cstream = a.codes + sh * T * (R / 2);
+  const int64_t tstream = sh * T;                           // index of the stream's first token
+  const int64_t nb = a.per_channel ? T / a.block : 0;
+  const int ngr = U / 16;                                   // 16-token groups per unit
 
-  f16x8 ahi[KS], alo[KS];
-  auto build = [&](const uint16_t* sc) {
-#pragma unroll
-    for (int sk = 0; sk < KS; ++sk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float g = qv[sk * 8 + e];
-        if (sc) g *= f16_to_f32(sc[8 * (KS * grp + sk) + nib_of(e)]);
-        const _Float16 hi = (_Float16)g;
-        ahi[sk][e] = hi;
-        alo[sk][e] = (_Float16)(g - (float)hi);
-      }
-  };
-  if (!a.per_channel) build(nullptr);
-
-  const int64_t T = a.tokens;
-  const int64_t per_wave = chunk / 4;
-  const int64_t t_begin = ci * chunk + w * per_wave;
-  int64_t t_end = t_begin + per_wave;
-  if (t_end > T) t_end = T;
-  const int64_t nb = a.per_channel ? T / a.block : 1;
-  int64_t cur = -1;
-  const int64_t rowbase = (s * a.heads + kvh) * T;   // head-major (sequence, KV head) stream
-  constexpr int CRB = R / 2;
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 64) {
+  for (int64_t un = u_begin + w; un < u_end; un += 4) {
+    const int64_t t0 = un * U;
+    // scales of this lane's channels (LB g .. as fp16), loaded with the unit
+    float sc[KS * 8];
     if (a.per_channel) {
-      const int64_t blk = t0 / a.block;
-      if (blk != cur) {
-        build(a.scales + ((s * a.heads + kvh) * nb + blk) * R);
-        cur = blk;
-      }
-    }
-    f32x4 acc[4];
+      const uint16_t* srow = a.scales + (sh * nb + un) * R + (R / 4) * g;
+      if (vec_scales) {
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-      acc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int64_t t = t0 + 16 * tg + (lane & 15);
-      uint32_t wd[KS];
-      if (t < T) {
-        const unsigned char* cp = a.codes + (rowbase + t) * CRB + grp * (KS * 4);
-        if constexpr (KS == 4) {
-          const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
-          wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
-        } else {
-          const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
-          wd[0] = v.x; wd[1] = v.y;
+        for (int K = 0; K < KS; ++K) {
+          const u32x4 v = *(const u32x4*)(srow + 8 * K);
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int n = nib_of(e);
+            sc[8 * K + e] = f16_to_f32((n & 1) ? wv[n >> 1] >> 16 : wv[n >> 1] & 0xffffu);
+          }
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < KS; ++k) wd[k] = 0x88888888u;   // code 0
-      }
+        for (int K = 0; K < KS; ++K)
 #pragma unroll
-      for (int sk = 0; sk < KS; ++sk) {
-        const f16x8 b = codes_to_f16(wd[sk]);
-        acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sk], b, acc[tg], 0, 0, 0);
-        acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[sk], b, acc[tg], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) sc[8 * K + e] = f16_to_f32(srow[8 * K + nib_of(e)]);
       }
     }
-    // 3. epilogue: lane holds D[4*grp + r][lane & 15] = (head 4*grp + r, token lane & 15)
+    for (int hc = 0; hc < NHC; ++hc) {
+      // A operand: row i = lane & 15 -> head hc 8 + i / 2, hi (i even) or lo (i odd) part
+      const int hl = hc * 8 + (j >> 1);
+      const bool live = hl < G;
+      f16x8 av[KS];
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-      const int64_t t = t0 + 16 * tg + (lane & 15);
-      if (t >= T) continue;
-      float f = 1.f;
-      const int64_t rix = rowbase + t;
-      if (a.nsep) f = f16_to_f32(a.norms[rix]);
-      if (!a.per_channel) f *= f16_to_f32(a.scales[rix]);
+      for (int K = 0; K < KS; ++K) {
+        const float* qp = qr + hl * R + (R / 4) * g + 8 * K;   // inside qr even when not live
+        const f32x4 q0 = *(const f32x4*)qp, q1 = *(const f32x4*)(qp + 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * grp + r;
-        if (i < G) a.scores[((s * a.q_heads + kvh * G + i) * T) + t] = acc[tg][r] * f;
+        for (int e = 0; e < 8; ++e) {
+          const int n = nib_of(e);
+          float gv = live ? (n < 4 ? q0[n] : q1[n - 4]) : 0.f;
+          if (a.per_channel) gv *= sc[8 * K + e];
+          const _Float16 hi = (_Float16)gv;
+          av[K][e] = (j & 1) ? (_Float16)(gv - (float)hi) : hi;
+        }
+      }
+      // 16-token groups, four at a time: every load of the four first, then the products
+      for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
+        uint32_t wd[4][KS];
+        float f[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int64_t t = t0 + 16 * (gr0 + b) + j;
+          if (t < T) {
+            const unsigned char* cp = cstream + t * (R / 2) + LB * g;
+            if constexpr (KS == 4) {
+              const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
+              wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
+            } else {
+              const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
+              wd[b][0] = v.x; wd[b][1] = v.y;
+            }
+            f[b] = a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f;
+            if (!a.per_channel) f[b] *= f16_to_f32(a.scales[tstream + t]);
+          } else {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) wd[b][k] = 0u;      // code 0
+            f[b] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int64_t t = t0 + 16 * (gr0 + b) + j;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int K = 0; K < KS; ++K) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], codes_to_f16(wd[b][K]), acc, 0, 0, 0);
+          // rows 4 g + r: (head 2 g, hi), (2 g, lo), (2 g + 1, hi), (2 g + 1, lo) of this pass
+          if (t < T) {
+            const int h0 = hc * 8 + 2 * g;
+            float* sp = a.scores + (s * a.q_heads + kvh * G + h0) * T + t;
+            if (h0 < G) sp[0] = (acc.x + acc.y) * f[b];
+            if (h0 + 1 < G) sp[T] = (acc.z + acc.w) * f[b];
+          }
+        }
       }
     }
   }
 }
 
 hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t st) {
-  const int chunk = a.tokens >= 4096 ? 1024 : 256;
-  const int64_t nchunks = (a.tokens + chunk - 1) / chunk;
+  const int U = a.per_channel ? a.block : 128;
+  const int64_t nunits = (a.tokens + U - 1) / U;
+  const int64_t nchunks = (nunits + SCORE_UNITS_PER_BLOCK - 1) / SCORE_UNITS_PER_BLOCK;
   const int64_t ntiles = a.seqs * a.heads * nchunks;
+  const int vec_scales = ((uintptr_t)a.scales & 15u) == 0;
   if (a.dim == 128)
-    hipLaunchKernelGGL((score_kernel<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, chunk);
+    hipLaunchKernelGGL((score_kernel<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
   else
-    hipLaunchKernelGGL((score_kernel<64>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, chunk);
+    hipLaunchKernelGGL((score_kernel<64>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
   return hipGetLastError();
 }
 
