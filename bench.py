@@ -69,19 +69,23 @@ def cpu_baseline(w, n_seqs: int):
     sp = oracle.Spec(1, w.tokens, w.heads, w.head_dim, 4, "nsep_pchan", w.block_tokens, w.hadamard)
     signs = synth.make_signs(w).numpy()
     q_all = synth.make_q(w)
-    t_total = 0.0
+    t_total = cpu_total = 0.0
     for s in range(n_seqs):
         x = synth.make_x(w, seq_range=(s, s + 1)).double().numpy()
         q = q_all[s:s + 1].double().numpy()
-        t0 = time.perf_counter()
+        t0, c0 = time.perf_counter(), time.process_time()
         r = oracle.quantize(x, sp, signs)
         kh = oracle.dequantize(r.packed, r.norms16, r.scales16, sp, signs)
         oracle.score_decode(q, kh, sp)
         t_total += time.perf_counter() - t0
+        cpu_total += time.process_time() - c0
     b = algorithmic_bytes(sub, w.q_heads)
     step_bytes = (b["quantize"] + b["dequantize"] + b["score_decode"]) * n_seqs
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    return {"value": round(step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
+    # threads actually busy on average (process CPU time over wall time); BLAS may use up to
+    # the pool size reported by threadpoolctl
+    pool = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    used = max(1.0, round(cpu_total / t_total, 1))
+    return {"value": round(step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": used, "thread_pool": pool,
             "kind": "oracle",
             "sample": f"{n_seqs} of {w.seqs} sequences ({n_seqs * w.tokens * w.heads * w.head_dim} K elements), "
                       f"quantize+dequantize+score, fp64 numpy, {t_total:.1f} s"}
@@ -92,7 +96,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle baseline sample (0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=10, help="sequences in the oracle baseline sample (0 = skip)")
     ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode"), default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
