@@ -15,10 +15,9 @@
 // the wave issues all of its loads at once (16 bytes of codes per lane and 16-token group, the
 // unit's scale row, the norms), then builds the MFMA A operand: g = (R q) * scale in fp32, split
 // into an fp16 hi/lo pair, rows 2 h + {0, 1} = (hi, lo) of query head h (8 heads per pass).
-// The B operand is 16 tokens x 32 channels of codes, converted from nibbles to fp16 with two
-// bit operations per pair: (word ^ 0x88888888) >> 4i & 0x000F000F | 0x64006400 is the fp16 pair
-// (1032 + c_i, 1032 + c_{i+4}); subtracting 1032 is exact.  The K order inside a lane is
-// therefore [n0 n4 n1 n5 n2 n6 n3 n7]; the A operand uses the same order.  Lane (g, j) of the
+// The B operand is 16 tokens x 32 channels of codes as fp16 subnormals (c + 8) 2^-24 (two bit
+// operations per pair); the K order inside a lane is [n0 n4 n1 n5 n2 n6 n3 n7] and the A
+// operand uses the same order.  Lane (g, j) of the
 // result holds rows 4 g + r: heads 2 g and 2 g + 1 (hi and lo rows summed) of token j.
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -27,19 +26,13 @@ namespace kvq {
 
 __device__ __forceinline__ int nib_of(int e) { return (e >> 1) + ((e & 1) << 2); }
 
-// fp16x8 B operand (8 codes of one packed word) in [n0 n4 n1 n5 n2 n6 n3 n7] order
-__device__ __forceinline__ f16x8 codes_to_f16(uint32_t word) {
+// B operand of the 8 codes of one packed word, in [n0 n4 n1 n5 n2 n6 n3 n7] order, as the fp16
+// subnormals (c + 8) 2^-24: (word ^ 0x88888888) >> 4 q & 0x000F000F is the pair (c_q + 8,
+// c_{q+4} + 8) in the mantissa bits, exact.  The bias 8 leaves through the accumulator's start
+// value (-8 2^-24 times the row sums of A) and 2^24 through the epilogue factor.
+__device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
   const uint32_t xb = word ^ 0x88888888u;
-  f16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t p = ((xb >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-    f16x2 hv = __builtin_bit_cast(f16x2, p);
-    hv = hv - f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
-    r[2 * j] = hv[0];
-    r[2 * j + 1] = hv[1];
-  }
-  return r;
+  return u32x4{xb & 0x000F000Fu, (xb >> 4) & 0x000F000Fu, (xb >> 8) & 0x000F000Fu, (xb >> 12) & 0x000F000Fu};
 }
 
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
@@ -126,15 +119,31 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
       for (int K = 0; K < KS; ++K) {
         const float* qp = qr + hl * R + (R / 4) * g + 8 * K;   // inside qr even when not live
         const f32x4 q0 = *(const f32x4*)qp, q1 = *(const f32x4*)(qp + 4);
+        // rows of even j take hi = fp16(g), odd j take lo = fp16(g - hi); hi + lo = g to ~2^-21
+        // relative with any rounding, so the packed round-toward-zero conversion serves
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int n = nib_of(e);
-          float gv = live ? (n < 4 ? q0[n] : q1[n - 4]) : 0.f;
-          if (a.per_channel) gv *= sc[8 * K + e];
-          const _Float16 hi = (_Float16)gv;
-          av[K][e] = (j & 1) ? (_Float16)(gv - (float)hi) : hi;
+        for (int e = 0; e < 8; e += 2) {
+          const int n0 = nib_of(e), n1 = nib_of(e + 1);
+          float g0 = n0 < 4 ? q0[n0] : q1[n0 - 4], g1 = n1 < 4 ? q0[n1] : q1[n1 - 4];
+          if (a.per_channel) {
+            g0 *= sc[8 * K + e];
+            g1 *= sc[8 * K + e + 1];
+          }
+          const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(g0, g1));
+          const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(g0 - (float)hi[0], g1 - (float)hi[1]));
+          const f16x2 pv = live ? ((j & 1) ? lo : hi) : f16x2{(_Float16)0.f, (_Float16)0.f};
+          av[K][e] = pv[0];
+          av[K][e + 1] = pv[1];
         }
       }
+      // accumulator start: -8 2^-24 sum_k A[i][k], from one more product with B = ones (lane (g, j)
+      // receives rows 4 g + r)
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < KS; ++K)
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}), acc0, 0, 0, 0);
+      acc0 *= -8.f * 0x1p-24f;
       // 16-token groups, four at a time: every load of the four first, then the products
       for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
         uint32_t wd[4][KS];
@@ -151,7 +160,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
               const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
               wd[b][0] = v.x; wd[b][1] = v.y;
             }
-            f[b] = a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f;
+            f[b] = (a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f) * 0x1p24f;
             if (!a.per_channel) f[b] *= f16_to_f32(a.scales[tstream + t]);
           } else {
 #pragma unroll
@@ -162,9 +171,10 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int64_t t = t0 + 16 * (gr0 + b) + j;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          f32x4 acc = acc0;
 #pragma unroll
-          for (int K = 0; K < KS; ++K) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], codes_to_f16(wd[b][K]), acc, 0, 0, 0);
+          for (int K = 0; K < KS; ++K)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, codes_to_sub16(wd[b][K])), acc, 0, 0, 0);
           // rows 4 g + r: (head 2 g, hi), (2 g, lo), (2 g + 1, hi), (2 g + 1, lo) of this pass
           if (t < T) {
             const int h0 = hc * 8 + 2 * g;
