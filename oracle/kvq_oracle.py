@@ -217,6 +217,29 @@ def score_decode(q: np.ndarray, k_hat: np.ndarray, spec: Spec) -> np.ndarray:
     return out
 
 
+# ----------------------------------------------------------------------------- decode attention
+def attention_decode(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, spec: Spec) -> np.ndarray:
+    """One decode step of attention over the whole cache, in float64 (the step after the decode
+    score: NSNQuant summary, "implementation details" and "latency"; the norm-separation post,
+    "longer contexts get worse", on error accumulating in attention as the cache grows).
+
+    out[s, hq, :] = sum_t p[t] v^[s*T + t, hq // G, :],  p = softmax_t(q . k^_t / sqrt(D)),
+    with plain scores q . k^ as in score_decode.  q: [seqs, q_heads, D]; k_hat, v_hat: the
+    dequantized caches [seqs*T, heads, D].
+    """
+    sc = score_decode(q, k_hat, spec) / np.sqrt(spec.head_dim)          # [S, Hq, T]
+    sc = sc - sc.max(axis=-1, keepdims=True)                             # exp() is then <= 1
+    p = np.exp(sc)
+    p /= p.sum(axis=-1, keepdims=True)
+    S, Hq, T = p.shape
+    G = Hq // spec.heads
+    vh = np.asarray(v_hat, dtype=np.float64).reshape(S, T, spec.heads, spec.head_dim)
+    out = np.empty((S, Hq, spec.head_dim))
+    for hq in range(Hq):
+        out[:, hq, :] = np.einsum("st,std->sd", p[:, hq, :], vh[:, :, hq // G, :])
+    return out
+
+
 # ----------------------------------------------------------------------------- error report
 def reconstruction_errors(x: np.ndarray, x_hat: np.ndarray, outlier_mask: np.ndarray) -> dict:
     """Four relative-error measures of a reconstruction (for the mode ordering check).
