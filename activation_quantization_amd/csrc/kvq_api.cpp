@@ -222,6 +222,72 @@ kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_head
   return launched(kvq::launch_score_decode(a, static_cast<hipStream_t>(stream)), "score_decode");
 }
 
+namespace {
+kvq::AttnArgs attn_args(const kvq_desc* d, int64_t q_heads) {
+  kvq::AttnArgs a{};
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim; a.q_heads = q_heads;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.nsep = nsep_mode(d->mode);
+  return a;
+}
+
+kvq_status check_attention(const kvq_desc* d, int64_t q_heads) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (!pchan_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "fused attention needs a per-channel mode (PCHAN or NSEP_PCHAN)");
+  if (d->head_dim != 128) return fail(KVQ_ERR_UNSUPPORTED, "fused attention needs head_dim 128 (got %lld)", (long long)d->head_dim);
+  if (d->block_tokens != 64 && d->block_tokens != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "fused attention needs block_tokens 64 or 128 (got %d)", d->block_tokens);
+  if (q_heads <= 0 || q_heads % d->heads != 0)
+    return fail(KVQ_ERR_SHAPE, "q_heads %lld must be a positive multiple of heads %lld", (long long)q_heads,
+                (long long)d->heads);
+  if (q_heads / d->heads > 4) return fail(KVQ_ERR_UNSUPPORTED, "fused attention takes at most 4 query heads per KV head");
+  if (d->seqs > 0 && d->tokens_per_seq == 0) return fail(KVQ_ERR_SHAPE, "attention over an empty cache");
+  return ok();
+}
+}  // namespace
+
+int64_t kvq_attention_workspace_bytes(const kvq_desc* d, int64_t q_heads) {
+  if (check_attention(d, q_heads) != KVQ_OK) return -1;
+  const kvq::AttnArgs a = attn_args(d, q_heads);
+  return a.seqs * q_heads * kvq::attention_partials(a) * (d->head_dim + 2) * (int64_t)sizeof(float);
+}
+
+kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* k_codes,
+                                const uint16_t* k_norms, const uint16_t* k_scales, const int8_t* k_signs,
+                                const uint8_t* v_codes, const uint16_t* v_norms, const uint16_t* v_scales,
+                                const int8_t* v_signs, float* out, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  kvq_status s = check_attention(d, q_heads);
+  if (s != KVQ_OK) return s;
+  if (d->seqs == 0) return ok();
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out || !workspace)
+    return fail(KVQ_ERR_NULL, "q, codes, scales, out and workspace are required");
+  const bool nsep = nsep_mode(d->mode);
+  if (nsep != (k_norms != nullptr) || nsep != (v_norms != nullptr))
+    return fail(KVQ_ERR_NULL, nsep ? "NSEP modes need both norms buffers" : "norms must be NULL without NSEP");
+  if ((d->hadamard != 0) != (k_signs != nullptr) || (d->hadamard != 0) != (v_signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs both signs buffers" : "signs must be NULL when hadamard == 0");
+  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16) ||
+      (k_signs && !aligned(k_signs, 16)) || (v_signs && !aligned(v_signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "codes, scales and signs must be 16-byte aligned");
+  if (!aligned(q, 2) || (k_norms && !aligned(k_norms, 2)) || (v_norms && !aligned(v_norms, 2)) || !aligned(out, 4) ||
+      !aligned(workspace, 4))
+    return fail(KVQ_ERR_ALIGN, "q and norms must be 2-byte, out and workspace 4-byte aligned");
+  const int64_t need = kvq_attention_workspace_bytes(d, q_heads);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_SHAPE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+  if ((s = device_ready()) != KVQ_OK) return s;
+
+  kvq::AttnArgs a = attn_args(d, q_heads);
+  a.q = q; a.k_codes = k_codes; a.k_norms = k_norms; a.k_scales = k_scales; a.k_signs = k_signs;
+  a.v_codes = v_codes; a.v_norms = v_norms; a.v_scales = v_scales; a.v_signs = v_signs;
+  a.out = out; a.ws = static_cast<float*>(workspace);
+  return launched(kvq::launch_attention_decode(a, static_cast<hipStream_t>(stream)), "attention_decode");
+}
+
 const char* kvq_status_str(kvq_status s) {
   switch (s) {
     case KVQ_OK: return "KVQ_OK";
@@ -236,6 +302,6 @@ const char* kvq_status_str(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_version(void) { return 10000; }
+int32_t kvq_version(void) { return 10100; }
 
 }  // extern "C"

@@ -1,0 +1,373 @@
+// Fused decode attention over a packed K/V cache (gfx950): the scores never leave the chip.
+//
+// Method sources (page title, section): NSNQuant summary "implementation details" (attention
+// computed from the quantized cache with the stored byproducts folded into the kernel) and
+// "latency" (decode time falls because the memory-bound attention reads less); norm-separation
+// post "longer contexts get worse" (error accumulates in attention as the cache grows); Rotated
+// Runtime Smooth analysis, Figure 2 (a rotation cancels inside a product, so the value sum may
+// run in the rotated domain and be rotated back once).
+//
+//   out[s, hq] = sum_t p_t v^_t,  p = softmax_t(q . k^_t / sqrt(D)),
+//   v^_t = sigma_v (1/sqrt n) H (norm_v[t] scale_v[blk(t)] (.) c_v[t])
+// so  out = sigma_v (1/sqrt n) H  sum_blk scale_v[blk] (.) sum_{t in blk} p_t norm_v[t] c_v[t].
+//
+// Pass 1 (one workgroup of 4 waves per chunk of 16 scale blocks of one (sequence, KV head)
+// stream; every wave walks its own blocks): per block, the scores of the G query heads come from
+// the matrix cores exactly as in the decode-score kernel (query times K scales as an fp16 hi/lo
+// A operand, codes as fp16 subnormals), an online softmax keeps the running max m and sum l per
+// head, and the value sum runs on the vector units with v_dot2_f32_f16: the block's V codes are
+// copied to LDS (global_load_lds), lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens
+// t = a (mod 4) and takes them two at a time (t, t + 4) as fp16 subnormal pairs against the pair
+// (p' = p norm_v) of each head.  Each wave writes (m, l, partial sum) per query head to the
+// caller's workspace.  Pass 2 merges the partials of a head (log-sum-exp weights), rotates the
+// result back and writes it.
+#include <type_traits>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int ATT_UNITS_PER_GROUP = 16;   // scale blocks per workgroup (4 per wave)
+
+__device__ __forceinline__ int att_nib(int e) { return (e >> 1) + ((e & 1) << 2); }
+
+__device__ __forceinline__ u32x4 att_codes_sub16(uint32_t word) {
+  const uint32_t xb = word ^ 0x88888888u;
+  return u32x4{xb & 0x000F000Fu, (xb >> 4) & 0x000F000Fu, (xb >> 8) & 0x000F000Fu, (xb >> 12) & 0x000F000Fu};
+}
+
+// max / sum over the 16 lanes of each row (DPP row rotations), every lane gets the result
+__device__ __forceinline__ float row_max16f(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ float row_sum16f(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f); }
+
+// Pass 1.  R = 128 channels; U = the scale block (64 or 128 tokens); at most GM = 4 query heads
+// per KV head (value sums of GM heads per lane).
+template <int U>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
+  constexpr int R = 128, KS = 4, LB = 16, GM = 4, NGR = U / 16;
+  __shared__ __attribute__((aligned(16))) float qr[GM * R];                 // rotated queries
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf[4][U * 64];    // per wave: one block of V codes
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[4][GM][128];        // per wave: p' per head, paired order
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int G = (int)(a.q_heads / a.heads);
+  const int64_t T = a.tokens;
+
+  const int64_t tile = xcd_tile(blockIdx.x, ntiles);
+  const int64_t ci = tile % nchunks;
+  const int64_t sh = tile / nchunks;                                      // stream: s * heads + kvh
+  const int64_t kvh = sh % a.heads, s = sh / a.heads;
+
+  // 1. rotated queries R q = (1/sqrt n) H (sigma_k q), once per workgroup
+  for (int e = tid; e < G * R; e += 256) {
+    const int hh = e / R, d = e % R;
+    float v = f16_to_f32(a.q[(s * a.q_heads + kvh * G + hh) * R + d]);
+    if (a.lg_had && a.k_signs[kvh * R + d] < 0) v = -v;
+    qr[e] = v;
+  }
+  __syncthreads();
+  for (int st = 0; st < a.lg_had; ++st) {
+    const int half = 1 << st;
+    for (int p = tid; p < G * R / 2; p += 256) {
+      const int hh = p / (R / 2), pp = p % (R / 2);
+      const int i = ((pp >> st) << (st + 1)) | (pp & (half - 1));
+      const float u = qr[hh * R + i], v = qr[hh * R + i + half];
+      qr[hh * R + i] = u + v;
+      qr[hh * R + i + half] = u - v;
+    }
+    __syncthreads();
+  }
+  if (a.lg_had) {
+    for (int e = tid; e < G * R; e += 256) qr[e] *= a.inv_sqrt_n;
+    __syncthreads();
+  }
+
+  const int64_t nunits = T / U;
+  const int64_t u_begin = ci * ATT_UNITS_PER_GROUP;
+  const int64_t u_end = u_begin + ATT_UNITS_PER_GROUP < nunits ? u_begin + ATT_UNITS_PER_GROUP : nunits;
+  const unsigned char* kstream = a.k_codes + sh * T * (R / 2);
+  const unsigned char* vstream = a.v_codes + sh * T * (R / 2);
+  const int64_t tstream = sh * T;
+  const int64_t nb = T / U;
+  const float zscale = 1.f / sqrtf((float)R);
+
+  // per-lane softmax state of the row's heads 2 g, 2 g + 1 (replicated over the row), and the
+  // value sums: lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens t = a (mod 4)
+  float m_row[2] = {-INFINITY, -INFINITY}, l_row[2] = {0.f, 0.f};
+  float o[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
+  const int va = lane >> 4, vb = lane & 15;
+  unsigned char* vw = &vbuf[w][0];
+  uint16_t* pw = &pbuf[w][0][0];
+
+  for (int64_t un = u_begin + w; un < u_end; un += 4) {
+    const int64_t t0 = un * U;
+    // the block's V codes into LDS (U * 64 bytes, 1 KiB per instruction, linear)
+#pragma unroll
+    for (int k = 0; k < NGR; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(vstream + t0 * (R / 2) + k * 1024 + 16 * lane),
+                                       (__attribute__((address_space(3))) void*)(vw + k * 1024), 16, 0, 0);
+    // K scales of this lane's channels (R/4) g + 8 K + nib(e); V scales of channels 8 vb ..
+    // (scale rows are 16-byte aligned: the entry point requires it)
+    const uint16_t* ksrow = a.k_scales + (sh * nb + un) * R + (R / 4) * g;
+    float sc[KS * 8];
+#pragma unroll
+    for (int K = 0; K < KS; ++K) {
+      const u32x4 v = *(const u32x4*)(ksrow + 8 * K);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = att_nib(e);
+        sc[8 * K + e] = f16_to_f32((n & 1) ? wv[n >> 1] >> 16 : wv[n >> 1] & 0xffffu);
+      }
+    }
+    float vs[8];
+    {
+      const u32x4 v = *(const u32x4*)(a.v_scales + (sh * nb + un) * R + 8 * vb);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vs[c] = f16_to_f32((c & 1) ? wv[c >> 1] >> 16 : wv[c >> 1] & 0xffffu);
+    }
+
+    // 2. scores of the block: A = (R q) * K scale as fp16 hi/lo rows (row i = lane & 15 -> head
+    //    i / 2), B = K codes as fp16 subnormals (c + 8) 2^-24
+    f16x8 av[KS];
+    {
+      const int hl = j >> 1;
+      const bool live = hl < G;
+#pragma unroll
+      for (int K = 0; K < KS; ++K) {
+        const float* qp = qr + hl * R + (R / 4) * g + 8 * K;
+        const f32x4 q0 = *(const f32x4*)qp, q1 = *(const f32x4*)(qp + 4);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int n0 = att_nib(e), n1 = att_nib(e + 1);
+          const float g0 = (n0 < 4 ? q0[n0] : q1[n0 - 4]) * sc[8 * K + e];
+          const float g1 = (n1 < 4 ? q0[n1] : q1[n1 - 4]) * sc[8 * K + e + 1];
+          const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(g0, g1));
+          const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(g0 - (float)hi[0], g1 - (float)hi[1]));
+          const f16x2 pv = live ? ((j & 1) ? lo : hi) : f16x2{(_Float16)0.f, (_Float16)0.f};
+          av[K][e] = pv[0];
+          av[K][e + 1] = pv[1];
+        }
+      }
+    }
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = 0; K < KS; ++K)
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}), acc0, 0, 0, 0);
+    acc0 *= -8.f * 0x1p-24f;
+    // z[gr][0/1]: scaled scores of heads 2 g, 2 g + 1 for token 16 gr + j; nv: V norm of it
+    float z[NGR][2], nvv[NGR];
+#pragma unroll
+    for (int gr0 = 0; gr0 < NGR; gr0 += 4) {
+      uint32_t wd[4][KS];
+      float fk[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t t = t0 + 16 * (gr0 + b) + j;
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(kstream + t * (R / 2) + LB * g));
+        wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
+        fk[b] = (a.nsep ? f16_to_f32(a.k_norms[tstream + t]) : 1.f) * (0x1p24f * zscale);
+        nvv[gr0 + b] = a.nsep ? f16_to_f32(a.v_norms[tstream + t]) : 1.f;
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = acc0;
+#pragma unroll
+        for (int K = 0; K < KS; ++K)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, att_codes_sub16(wd[b][K])), acc, 0, 0, 0);
+        z[gr0 + b][0] = (acc.x + acc.y) * fk[b];
+        z[gr0 + b][1] = (acc.z + acc.w) * fk[b];
+      }
+    }
+
+    // 3. online softmax for the row's two heads; p' = p * norm_v to LDS in the pair order
+    //    slot(8 k + r) = 8 k + 2 (r % 4) + r / 4, so tokens t and t + 4 sit side by side
+    float alpha_row[2];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int gr = 0; gr < NGR; ++gr) mx = fmaxf(mx, z[gr][q2]);
+      mx = row_max16f(mx);
+      const float mnew = fmaxf(m_row[q2], mx);
+      alpha_row[q2] = exp_f(m_row[q2] - mnew);            // 0 on the first block (m = -inf)
+      float ps = 0.f;
+      const int h = 2 * g + q2;
+#pragma unroll
+      for (int gr = 0; gr < NGR; ++gr) {
+        const float p = exp_f(z[gr][q2] - mnew);
+        ps += p;
+        const int t = 16 * gr + j;
+        if (h < GM) pw[h * 128 + (t & ~7) + 2 * (t & 3) + ((t >> 2) & 1)] = __builtin_bit_cast(uint16_t, (_Float16)(p * nvv[gr]));
+      }
+      ps = row_sum16f(ps);
+      l_row[q2] = l_row[q2] * alpha_row[q2] + ps;
+      m_row[q2] = mnew;
+    }
+    // the alphas of every head, to every lane (head h lives in row h / 2)
+    float alpha[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+      alpha[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_row[h & 1]), 16 * (h >> 1)));
+
+    // 4. value sums of the block: tokens t = 8 i + va and t + 4, channels 8 vb ..
+    __builtin_amdgcn_s_waitcnt(0x0070);                   // the V codes (and everything else) landed
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    float acc[GM][8], accb[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      accb[h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+    }
+#pragma unroll 4
+    for (int i = 0; i < U / 8; ++i) {
+      const int ta = 8 * i + va;
+      const uint32_t x0 = *(const uint32_t*)(vw + ta * 64 + 4 * vb) ^ 0x88888888u;
+      const uint32_t x1 = *(const uint32_t*)(vw + (ta + 4) * 64 + 4 * vb) ^ 0x88888888u;
+      const uint32_t e0 = x0 & 0x0F0F0F0Fu, o0 = (x0 >> 4) & 0x0F0F0F0Fu;
+      const uint32_t e1 = x1 & 0x0F0F0F0Fu, o1 = (x1 >> 4) & 0x0F0F0F0Fu;
+      // channel 2 k: byte k of e0 (token ta) and of e1 (token ta + 4); 2 k + 1 from o0 / o1
+      f16x2 cp[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + k) << 16) | (uint32_t)k;   // (b_k of src1) | (b_k of src0) << 16
+        cp[2 * k] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e1, e0, sel));
+        cp[2 * k + 1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(o1, o0, sel));
+      }
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const f16x2 pp = __builtin_bit_cast(f16x2, *(const uint32_t*)(pw + h * 128 + 8 * i + 2 * va));
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[h][c] = __builtin_amdgcn_fdot2(cp[c], pp, acc[h][c], false);
+          accb[h] = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, accb[h], false);
+        }
+      }
+    }
+    // o = o alpha + scale_v (.) (2^24 acc - 8 sum p')
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        o[h][c] = o[h][c] * alpha[h] + vs[c] * __builtin_fmaf(acc[h][c], 0x1p24f, -8.f * accb[h]);
+    // every lane of the wave is done with this block's LDS before the next block's copy
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  // 5. the wave's partial: sum the four token classes a, then lanes 0..15 write
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = o[h][c];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[h][c] = v;
+    }
+  const int64_t NP = nchunks * 4;
+  const int64_t pidx = ci * 4 + w;
+  for (int h = 0; h < G; ++h) {
+    float* wp = a.ws + ((s * a.q_heads + kvh * G + h) * NP + pidx) * (R + 2);
+    if (lane < 16) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float v = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh)
+          if (hh == h) v = o[hh][c];
+        wp[8 * lane + c] = v;
+      }
+    }
+    const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_row[h & 1]), 16 * (h >> 1)));
+    const float lh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_row[h & 1]), 16 * (h >> 1)));
+    if (lane == 0) {
+      wp[R] = mh;
+      wp[R + 1] = lh;
+    }
+  }
+}
+
+// Pass 2: one workgroup of R threads per (sequence, query head): merge the partials, rotate back.
+__global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
+  constexpr int R = 128;
+  __shared__ float buf[R];
+  const int c = threadIdx.x;
+  const int64_t shq = blockIdx.x;                              // s * q_heads + hq
+  const int64_t hq = shq % a.q_heads;
+  const int64_t kvh = hq / (a.q_heads / a.heads);
+  const float* wp = a.ws + shq * NP * (R + 2);
+  float M = -INFINITY;
+  for (int64_t p = 0; p < NP; ++p) M = fmaxf(M, wp[p * (R + 2) + R]);
+  float L = 0.f, O = 0.f;
+  for (int64_t p = 0; p < NP; ++p) {
+    const float m = wp[p * (R + 2) + R];
+    const float f = m == -INFINITY ? 0.f : exp_f(m - M);
+    L += f * wp[p * (R + 2) + R + 1];
+    O += f * wp[p * (R + 2) + c];
+  }
+  buf[c] = L > 0.f ? O / L : 0.f;
+  __syncthreads();
+  // inverse rotation: sigma_v (1/sqrt n) H (blocks of n = 2^lg_had): butterflies (a, b) -> (a + b, a - b)
+  for (int st = 0; st < a.lg_had; ++st) {
+    const int half = 1 << st;
+    const float x = buf[c], y = buf[c ^ half];
+    __syncthreads();
+    buf[c] = (c & half) ? y - x : x + y;
+    __syncthreads();
+  }
+  float r = buf[c];
+  if (a.lg_had) {
+    r *= a.inv_sqrt_n;
+    if (a.v_signs[kvh * R + c] < 0) r = -r;
+  }
+  a.out[shq * R + c] = r;
+}
+
+}  // namespace
+
+int64_t attention_partials(const AttnArgs& a) {
+  const int64_t nunits = a.tokens / a.block;
+  return ((nunits + ATT_UNITS_PER_GROUP - 1) / ATT_UNITS_PER_GROUP) * 4;
+}
+
+hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t st) {
+  const int64_t nunits = a.tokens / a.block;
+  const int64_t nchunks = (nunits + ATT_UNITS_PER_GROUP - 1) / ATT_UNITS_PER_GROUP;
+  const int64_t ntiles = a.seqs * a.heads * nchunks;
+  if (a.block == 64)
+    hipLaunchKernelGGL((attn_partial<64>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
+  else
+    hipLaunchKernelGGL((attn_partial<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(a.seqs * a.q_heads)), dim3(128), 0, st, a, nchunks * 4);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -54,11 +54,32 @@ struct ScoreArgs {
   int32_t per_channel;
 };
 
+struct AttnArgs {
+  const uint16_t* q;        // [seqs, q_heads, D] fp16
+  const uint8_t* k_codes;
+  const uint16_t* k_norms;
+  const uint16_t* k_scales;
+  const int8_t* k_signs;
+  const uint8_t* v_codes;
+  const uint16_t* v_norms;
+  const uint16_t* v_scales;
+  const int8_t* v_signs;
+  float* out;               // [seqs, q_heads, D]
+  float* ws;                // per (sequence, query head, partial): R sums, max, normalizer
+  int64_t seqs, tokens, heads, dim, q_heads;
+  int32_t block;
+  int32_t lg_had;
+  float inv_sqrt_n;
+  int32_t nsep;
+};
+
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t stream);
+int64_t attention_partials(const AttnArgs& a);   // partials per (sequence, query head)
 
 }  // namespace kvq

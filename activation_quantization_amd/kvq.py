@@ -39,6 +39,9 @@ _SIGNATURES = {
     "kvq_quantize": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, _P]),
     "kvq_dequantize": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "kvq_score_decode": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
+    "kvq_attention_workspace_bytes": (ctypes.c_int64, [ctypes.POINTER(KvqDesc), ctypes.c_int64]),
+    "kvq_attention_decode": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, ctypes.c_int64, _P]),
     "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (ctypes.c_int32, []),
@@ -187,6 +190,36 @@ def score_decode(d: Desc, q: torch.Tensor, codes, norms, scales, signs=None,
     st = lib().kvq_score_decode(ctypes.byref(d.c()), _ptr(q), q_heads, _ptr(codes), _ptr(norms),
                                 _ptr(scales), _ptr(signs), _ptr(out), _stream(stream))
     _check(st, "kvq_score_decode")
+    return out
+
+
+def attention_workspace_bytes(d: Desc, q_heads: int) -> int:
+    return lib().kvq_attention_workspace_bytes(ctypes.byref(d.c()), q_heads)
+
+
+def attention_decode(d: Desc, q: torch.Tensor, k_cache, v_cache, k_signs=None, v_signs=None,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """kvq_attention_decode.  k_cache / v_cache: (codes, norms, scales) as kvq_quantize returns
+    them.  q fp16 [seqs, q_heads, head_dim] -> out fp32 [seqs, q_heads, head_dim].  The workspace
+    (caller-owned device memory) is allocated here with torch when not supplied."""
+    if q.dtype != torch.float16:
+        raise ValueError("q must be fp16")
+    q_heads = q.shape[1]
+    kc, kn, ks = k_cache
+    vc, vn, vs = v_cache
+    if out is None:
+        out = torch.empty((d.seqs, q_heads, d.head_dim), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = attention_workspace_bytes(d, q_heads)
+        if nbytes < 0:
+            _check(lib().kvq_validate(ctypes.byref(d.c())) or ERR_UNSUPPORTED, "kvq_attention_workspace_bytes")
+        workspace = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=q.device)
+    _need_cuda(q, kc, kn, ks, vc, vn, vs, k_signs, v_signs, out, workspace)
+    st = lib().kvq_attention_decode(ctypes.byref(d.c()), _ptr(q), q_heads, _ptr(kc), _ptr(kn), _ptr(ks), _ptr(k_signs),
+                                    _ptr(vc), _ptr(vn), _ptr(vs), _ptr(v_signs), _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "kvq_attention_decode")
     return out
 
 

@@ -35,9 +35,12 @@ def algorithmic_bytes(w, q_heads):
     x = 2 * n
     q = 2 * w.seqs * q_heads * w.head_dim
     scores = 4 * w.seqs * q_heads * w.tokens
+    out = 4 * w.seqs * q_heads * w.head_dim
     return {"quantize": x + signs + codes + norms + scales,
             "dequantize": codes + norms + scales + signs + x,
             "score_decode": q + signs + codes + norms + scales + scores,
+            # fused decode attention (a "next" row, outside the step): K and V caches in, fp32 out
+            "attention_decode": q + 2 * (signs + codes + norms + scales) + out,
             "elements": n}
 
 
@@ -97,7 +100,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seqs", type=int, default=10, help="sequences in the oracle baseline sample (0 = skip)")
-    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode"), default=None,
+    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode"), default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain device-to-device copy of the fp16 input (the reference kernel "
@@ -147,6 +150,9 @@ def main():
         return
     names = ("quantize", "dequantize", "score_decode")
     run = {n: args.only in (None, n) for n in names}
+    run_attn = args.only in (None, "attention_decode")
+    if args.only == "attention_decode":
+        run = {n: False for n in names}
 
     if args.only not in (None, "quantize"):
         kvq.quantize(d, x, signs, out=(codes, norms, scales), stream=stream)   # the cache it reads
@@ -178,6 +184,30 @@ def main():
 
     b = algorithmic_bytes(w, w.q_heads)
     step_bytes = sum(b[n] for n in names if run[n])
+
+    # fused decode attention over a K cache and a V cache of the same statistics (timed apart from
+    # the step: it is a "next" row, not one of the step's kernels)
+    attn_us = None
+    if run_attn:
+        if not run["quantize"]:
+            kvq.quantize(d, x, signs, out=(codes, norms, scales), stream=stream)
+        xv = synth.make_x(w, tensor_id=1, pin=True).to(dev, non_blocking=True)
+        vcache = kvq.alloc_outputs(d, dev)
+        kvq.quantize(d, xv, signs, out=vcache, stream=stream)
+        del xv
+        att_out = torch.empty((w.seqs, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+        ws = torch.empty(kvq.attention_workspace_bytes(d, w.q_heads) // 4, dtype=torch.float32, device=dev)
+        kc = (codes, norms, scales)
+        for _ in range(args.warmup):
+            kvq.attention_decode(d, q, kc, vcache, signs, signs, out=att_out, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(args.steps):
+            kvq.attention_decode(d, q, kc, vcache, signs, signs, out=att_out, workspace=ws, stream=stream)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        attn_us = a0.elapsed_time(a1) * 1e3 / args.steps
     kernels = {}
     for n in names:
         if not run[n]:
@@ -186,6 +216,10 @@ def main():
         kernels[n] = {"us": round(per_kernel_ms[n] * 1e3, 2), "bytes": b[n], "GB/s": round(gbs, 1),
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     traffic = measured_traffic("quantize")
+    if attn_us is not None:
+        gbs = b["attention_decode"] / (attn_us * 1e-6) / 1e9
+        kernels["attention_decode"] = {"us": round(attn_us, 2), "bytes": b["attention_decode"], "GB/s": round(gbs, 1),
+                                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "in_step": False}
     if args.only:
         print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
         return

@@ -135,13 +135,35 @@ kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_head
                             const uint8_t* codes, const uint16_t* norms, const uint16_t* scales,
                             const int8_t* signs, float* scores, void* stream);
 
+/*
+ * Fused decode attention over a packed K cache and a packed V cache, both written by
+ * kvq_quantize with descriptor d (one decode step; the scores stay on the chip).  Source: NSNQuant
+ * summary, "implementation details" and "latency"; norm-separation post, "longer contexts get
+ * worse".
+ *   out[s, hq, :] = sum_t p_t v^[s*T + t, hq / G, :],  p = softmax_t(q[s, hq] . k^_t / sqrt(D))
+ * with G = q_heads / heads and k^, v^ the dequantized caches.  Requirements: a per-channel mode
+ * (PCHAN or NSEP_PCHAN), head_dim 128, block_tokens 64 or 128, tokens_per_seq >= 1, G <= 4.
+ *   q: fp16 bits [seqs, q_heads, head_dim]; out: fp32 [seqs, q_heads, head_dim].
+ *   k_signs / v_signs: the signs each cache was quantized with (NULL iff hadamard == 0).
+ *   workspace: device memory of at least kvq_attention_workspace_bytes(d, q_heads) bytes, 4-byte
+ *   aligned, owned by the caller; its contents on entry do not matter and are overwritten.
+ *   Codes and scales must be 16-byte aligned; q, norms 2-byte; out 4-byte.
+ * The call enqueues two kernels (partial softmax sums per cache chunk, then their merge).
+ */
+int64_t kvq_attention_workspace_bytes(const kvq_desc* d, int64_t q_heads);
+kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads,
+                                const uint8_t* k_codes, const uint16_t* k_norms, const uint16_t* k_scales,
+                                const int8_t* k_signs, const uint8_t* v_codes, const uint16_t* v_norms,
+                                const uint16_t* v_scales, const int8_t* v_signs, float* out, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_str(kvq_status s);
 
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* kvq_last_error(void);
 
-/* ABI version: 10000 * major + 100 * minor + patch. */
+/* ABI version: 10000 * major + 100 * minor + patch (1.1: fused decode attention). */
 int32_t kvq_version(void);
 
 #ifdef __cplusplus

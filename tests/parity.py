@@ -104,3 +104,19 @@ def check_scores(gpu: np.ndarray, ref: np.ndarray, q: np.ndarray, k_hat: np.ndar
     bad = err > tol
     assert not np.any(bad), f"scores: {int(bad.sum())} outside tolerance, worst {np.max(err / tol):.3g}x"
     return float(np.max(err / tol))
+
+
+REL_ATTN = 2e-3
+
+
+def check_attention(gpu: np.ndarray, ref: np.ndarray):
+    """gpu/ref [S, Hq, D]: |gpu - ref| <= 2e-3 max(|ref|, rms of the reference vector).  The output
+    is a convex combination of value vectors, so its own rms is the natural magnitude floor."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    tol = REL_ATTN * np.maximum(np.abs(r), rms)
+    err = np.abs(g - r)
+    bad = err > tol
+    assert not np.any(bad), f"attention: {int(bad.sum())} outside tolerance, worst {np.max(err / tol):.3g}x"
+    return float(np.max(err / tol))

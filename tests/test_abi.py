@@ -120,3 +120,35 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(kvq, "LIB_PATH", "/nonexistent/libkvq.so")
     with pytest.raises(ImportError):
         kvq.lib()
+
+
+def _att(d, q_heads=16, ws_bytes=1 << 30, **ptr):
+    p = dict(q=FAKE, kc=FAKE, kn=FAKE, ks=FAKE, ksg=FAKE, vc=FAKE, vn=FAKE, vs=FAKE, vsg=FAKE, out=FAKE, ws=FAKE)
+    p.update(ptr)
+    return kvq.lib().kvq_attention_decode(ctypes.byref(d.c()), p["q"], q_heads, p["kc"], p["kn"], p["ks"], p["ksg"],
+                                          p["vc"], p["vn"], p["vs"], p["vsg"], p["out"], p["ws"], ws_bytes, None)
+
+
+def test_attention_workspace_size():
+    d = kvq.Desc(**GOOD)                                   # 2 seqs x 256 tokens: 2 blocks -> 1 chunk -> 4 partials
+    assert kvq.attention_workspace_bytes(d, 16) == 2 * 16 * 4 * (128 + 2) * 4
+    long = kvq.Desc(64, 32768, 8, 128, 4, "nsep_pchan", 128, 128)
+    assert kvq.attention_workspace_bytes(long, 32) == 64 * 32 * (256 // 16) * 4 * 130 * 4
+    assert kvq.attention_workspace_bytes(kvq.Desc(**{**GOOD, "mode": "nsep"}), 16) == -1
+    assert kvq.attention_workspace_bytes(d, 20) == -1     # 5 query heads per KV head
+
+
+def test_attention_validation_before_any_device_call():
+    d = kvq.Desc(**GOOD)
+    assert _att(kvq.Desc(**{**GOOD, "mode": "nsep", "block_tokens": 0})) == kvq.ERR_UNSUPPORTED   # per-token scales
+    assert _att(kvq.Desc(**{**GOOD, "head_dim": 64, "hadamard": 64})) == kvq.ERR_UNSUPPORTED
+    assert _att(d, q_heads=20) == kvq.ERR_UNSUPPORTED     # G = 5
+    assert _att(d, q_heads=6) == kvq.ERR_SHAPE            # not a multiple of heads
+    assert _att(kvq.Desc(**{**GOOD, "tokens_per_seq": 0})) == kvq.ERR_SHAPE
+    assert _att(kvq.Desc(**{**GOOD, "seqs": 0})) == kvq.OK   # nothing to do
+    assert _att(d, ws=None) == kvq.ERR_NULL
+    assert _att(d, vn=None) == kvq.ERR_NULL               # NSEP needs both norms
+    assert _att(d, ksg=None) == kvq.ERR_NULL              # Hadamard needs both signs
+    assert _att(d, vs=FAKE + 2) == kvq.ERR_ALIGN          # scales are read as 16-byte vectors
+    assert _att(d, out=FAKE + 2) == kvq.ERR_ALIGN
+    assert _att(d, ws_bytes=100) == kvq.ERR_SHAPE
