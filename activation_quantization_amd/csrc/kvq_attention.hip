@@ -64,8 +64,9 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   constexpr int R = 128, KS = 4, LB = 16, GM = 4, NGR = U / 16;
   __shared__ __attribute__((aligned(16))) float qr[GM * R];                 // rotated queries
   __shared__ __attribute__((aligned(16))) unsigned char vbuf[4][U * 64];    // per wave: one block of V codes
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[4][GM][128];        // per wave: p' per head, paired order
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[4][64][GM];        // per wave: p' pairs (t, t + 4) x head
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index, in a scalar register
   const int g = lane >> 4, j = lane & 15;
   const int G = (int)(a.q_heads / a.heads);
   const int64_t T = a.tokens;
@@ -118,7 +119,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
   const int va = lane >> 4, vb = lane & 15;
   unsigned char* vw = &vbuf[w][0];
-  uint16_t* pw = &pbuf[w][0][0];
+  uint16_t* pw = (uint16_t*)&pbuf[w][0][0];
 
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
@@ -205,7 +206,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
 
     // 3. online softmax for the row's two heads; p' = p * norm_v to LDS in the pair order
     //    slot(8 k + r) = 8 k + 2 (r % 4) + r / 4, so tokens t and t + 4 sit side by side
-    float alpha_row[2];
+    float alpha_row[2], sp_row[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       float mx = -INFINITY;
@@ -214,36 +215,39 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       mx = row_max16f(mx);
       const float mnew = fmaxf(m_row[q2], mx);
       alpha_row[q2] = exp_f(m_row[q2] - mnew);            // 0 on the first block (m = -inf)
-      float ps = 0.f;
+      float ps = 0.f, psn = 0.f;                           // sums of p and of p' = p norm_v
       const int h = 2 * g + q2;
 #pragma unroll
       for (int gr = 0; gr < NGR; ++gr) {
         const float p = exp_f(z[gr][q2] - mnew);
         ps += p;
-        const int t = 16 * gr + j;
-        if (h < GM) pw[h * 128 + (t & ~7) + 2 * (t & 3) + ((t >> 2) & 1)] = __builtin_bit_cast(uint16_t, (_Float16)(p * nvv[gr]));
+        const int t = 16 * gr + j;                          // pair (t & ~4) slot 4 (t / 8) + t % 4, half (t / 4) % 2
+        const _Float16 pn = (_Float16)(p * nvv[gr]);
+        psn += (float)pn;                                   // the rounded value the dot products use
+        if (h < GM) pw[2 * GM * (4 * (t >> 3) + (t & 3)) + 2 * h + ((t >> 2) & 1)] = __builtin_bit_cast(uint16_t, pn);
       }
       ps = row_sum16f(ps);
+      sp_row[q2] = row_sum16f(psn);
       l_row[q2] = l_row[q2] * alpha_row[q2] + ps;
       m_row[q2] = mnew;
     }
     // the alphas of every head, to every lane (head h lives in row h / 2)
-    float alpha[GM];
+    float alpha[GM], spn[GM];
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
+    for (int h = 0; h < GM; ++h) {
       alpha[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_row[h & 1]), 16 * (h >> 1)));
+      spn[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sp_row[h & 1]), 16 * (h >> 1)));
+    }
 
     // 4. value sums of the block: tokens t = 8 i + va and t + 4, channels 8 vb ..
     __builtin_amdgcn_s_waitcnt(0x0070);                   // the V codes (and everything else) landed
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    float acc[GM][8], accb[GM];
+    float acc[GM][8];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      accb[h] = 0.f;
+    for (int h = 0; h < GM; ++h)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
-    }
 #pragma unroll 4
     for (int i = 0; i < U / 8; ++i) {
       const int ta = 8 * i + va;
@@ -259,22 +263,25 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
         cp[2 * k] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e1, e0, sel));
         cp[2 * k + 1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(o1, o0, sel));
       }
+      // p' pairs (ta, ta + 4) of the four heads in one 16-byte read
+      const u32x4 pq = *(const u32x4*)(pbuf[w][4 * i + va]);
+      const uint32_t pp4[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h < G) {
-          const f16x2 pp = __builtin_bit_cast(f16x2, *(const uint32_t*)(pw + h * 128 + 8 * i + 2 * va));
+          const f16x2 pp = __builtin_bit_cast(f16x2, pp4[h]);
 #pragma unroll
           for (int c = 0; c < 8; ++c) acc[h][c] = __builtin_amdgcn_fdot2(cp[c], pp, acc[h][c], false);
-          accb[h] = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, accb[h], false);
         }
       }
     }
-    // o = o alpha + scale_v (.) (2^24 acc - 8 sum p')
+    // o = o alpha + scale_v (.) (2^24 acc - 8 sum p'); the bias is split evenly over the four
+    // token classes a, whose partial sums are added up at the end
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        o[h][c] = o[h][c] * alpha[h] + vs[c] * __builtin_fmaf(acc[h][c], 0x1p24f, -8.f * accb[h]);
+        o[h][c] = o[h][c] * alpha[h] + vs[c] * __builtin_fmaf(acc[h][c], 0x1p24f, -2.f * spn[h]);
     // every lane of the wave is done with this block's LDS before the next block's copy
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
