@@ -202,23 +202,6 @@ __device__ __attribute__((noinline)) double exact_rot64(const unsigned char* __r
   return acc;
 }
 
-template <int DT, int R>
-__device__ __attribute__((noinline)) double exact_sumsq64(const unsigned char* __restrict__ row) {
-  double acc = 0.0;
-#pragma unroll 1
-  for (int j0 = 0; j0 < R; j0 += 8) {
-    const u32x4 v = *(const u32x4*)(row + 2 * j0);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
-      const double x = (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
-      acc = __builtin_fma(x, x, acc);
-    }
-  }
-  return acc;
-}
-
 // the exact rounding decision: rne of the fp32 value of the fp64 quotient
 __device__ __forceinline__ uint32_t exact_code(double v) {
   return (uint32_t)(int)__builtin_rintf((float)v) & 0xfu;
@@ -251,54 +234,50 @@ __device__ __forceinline__ void load_tile_lds(unsigned char* lds, const unsigned
   }
 }
 
-// Per-token rare path: every code of each vector holding a near-tie is recomputed exactly
-// (fp64 transform in LDS, shared by the wave); v = Q Y_c / max |Y| for both per-token modes.
+// Per-token rare path, one lane per row segment: a code whose fp32 quotient lies within 2^-17
+// of a half-integer is re-decided from the exact quotient Q Y_c / max |Y| (the norm cancels in
+// both per-token modes).  That needs the exact Y_c and the exact max of the vector.  The fp32
+// transform is accurate to far better than a relative 2^-12 of the max, so the max is attained
+// among the channels whose fp32 magnitude is within that distance of the fp32 max; each lane
+// recomputes its own such channels in fp64 and the vector's L lanes reduce them.  Lanes of
+// vectors without a near-tie return at once.  row: this lane's input segment (global), sg: its
+// R sign bytes.
 template <int DT, int R, int LG>
-__device__ __forceinline__ void ptok_exact(const QuantArgs& a, uint64_t ball, int64_t seg0, int lgL,
-                                                     const unsigned char* xb, unsigned char* stage_codes, double* F) {
-  constexpr int ROWB = R * 2, CRB = R / 2;
+__device__ __forceinline__ void ptok_fix(const float (&y)[R], float m, float inv_scale, float q, int L, uint64_t ball,
+                                         const unsigned char* __restrict__ row, const int8_t* __restrict__ sg,
+                                         unsigned char* stage_codes) {
+  constexpr int CRB = R / 2;
   const int lane = threadIdx.x;
-  const int L = 1 << lgL;
-  while (ball) {
-    const int l0 = __builtin_ctzll(ball);
-    const int64_t v0 = (seg0 + l0) >> lgL;
-    const int lane0 = (int)((v0 << lgL) - seg0);
-    ball &= ~((L == 64 ? ~0ull : ((1ull << L) - 1ull)) << lane0);
-    const int64_t hv = v0 % a.heads;
-    double mx = 0.0;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int p = 0; p < L; ++p) {
-        const unsigned char* xr = xb + (lane0 + p) * ROWB;
-        const int8_t* sgp = a.signs ? a.signs + hv * a.dim + p * R : nullptr;
-        wave_lds_sync();
-        for (int i = lane; i < R; i += 64) {
-          const uint32_t hb = *(const uint16_t*)(xr + 2 * i);
-          double x = (double)(DT == DT_F16 ? f16_to_f32(hb) : bf16_to_f32(hb));
-          if (sgp && sgp[i] < 0) x = -x;
-          F[i] = x;
-        }
-        for (int st = 0; st < LG; ++st) {
-          wave_lds_sync();
-          for (int pp = lane; pp < R / 2; pp += 64) {
-            const int i = ((pp >> st) << (st + 1)) | (pp & ((1 << st) - 1));
-            const double u = F[i], w2 = F[i + (1 << st)];
-            F[i] = u + w2;
-            F[i + (1 << st)] = u - w2;
-          }
-        }
-        wave_lds_sync();
-        if (pass == 0) {
-          for (int i = lane; i < R; i += 64) mx = fmax(mx, fabs(F[i]));
-        } else if (lane < R / 2) {
-          const uint32_t lo = mx > 0.0 ? exact_code((double)a.q * F[2 * lane] / mx) : 0u;
-          const uint32_t hi = mx > 0.0 ? exact_code((double)a.q * F[2 * lane + 1] / mx) : 0u;
-          const int row = lane0 + p;
-          stage_codes[row * CRB + swz_chunk(row, lane >> 4, CRB) * 16 + (lane & 15)] = (unsigned char)(lo | (hi << 4));
-        }
-      }
-      if (pass == 0) {
-        for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-      }
+  const uint64_t gm = (L == 64 ? ~0ull : ((1ull << L) - 1ull)) << (lane & ~(L - 1));
+  if ((ball & gm) == 0ull) return;
+  uint32_t cand[R / 32], flg[R / 32];
+  const float thr = m - m * 0x1p-12f;
+#pragma unroll
+  for (int g = 0; g < R / 32; ++g) {
+    uint32_t cg = 0u, fg = 0u;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float v = y[32 * g + e];
+      const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_fmaf(v, inv_scale, MAGIC));
+      fg |= (uint32_t)((b & 0xffffu) == 0u) << e;
+      cg |= (uint32_t)(fabsf(v) >= thr) << e;
+    }
+    cand[g] = cg;
+    flg[g] = fg;
+  }
+  double mx = 0.0;
+#pragma unroll 1
+  for (int g = 0; g < R / 32; ++g) {
+    for (uint32_t mk = cand[g]; mk; mk &= mk - 1u)
+      mx = fmax(mx, fabs(exact_rot64<DT>(row, sg, 32 * g + __builtin_ctz(mk), LG)));
+  }
+  for (int o = 1; o < L; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o));
+#pragma unroll 1
+  for (int g = 0; g < R / 32; ++g) {
+    for (uint32_t mk = flg[g]; mk; mk &= mk - 1u) {
+      const int c = 32 * g + __builtin_ctz(mk);
+      const uint32_t nib = mx > 0.0 ? exact_code((double)q * exact_rot64<DT>(row, sg, c, LG) / mx) : 0u;
+      patch_nibble(stage_codes, lane, CRB, c, nib);
     }
   }
 }
@@ -312,7 +291,6 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
   constexpr int ROWB = R * 2, CPR = ROWB / 16, CRB = R / 2, CCR = CRB / 16;
   __shared__ __attribute__((aligned(16))) unsigned char stage_in[64 * ROWB];
   __shared__ __attribute__((aligned(16))) unsigned char stage_codes[64 * CRB];
-  __shared__ double F[R];                                       // exact re-decision workspace
   const int lane = threadIdx.x;
   const int L = 1 << lgL;
   const int64_t G = gridDim.x;
@@ -406,9 +384,9 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
       *(u32x4*)(stage_codes + lane * CRB + swz_chunk(lane, cc, CRB) * 16) = t;
     }
 
-    // rare path: recompute every code of a vector holding a near-tie, exactly
+    // rare path: re-decide the near-ties exactly
     const uint64_t ball = __ballot(lane < nvalid && flagged);
-    if (ball) ptok_exact<DT, R, LG>(a, ball, seg0, lgL, xb, stage_codes, F);
+    if (ball) ptok_fix<DT, R, LG>(y, m, inv_scale, a.q, L, ball, xb + lane * ROWB, sg, stage_codes);
     if (part == 0 && lane < nvalid) {
       const float nu = sqrtf(ss);
       const int64_t vh = head_major(a.heads, a.tokens, vec);

@@ -94,6 +94,56 @@ def cpu_baseline(w, n_seqs: int):
                       f"quantize+dequantize+score, fp64 numpy, {t_total:.1f} s"}
 
 
+def config_bytes(w, bits_mode):
+    """Algorithmic bytes of quantize / dequantize for workload w (input dtype 2 bytes)."""
+    n = w.seqs * w.tokens * w.heads * w.head_dim
+    tok = w.seqs * w.tokens * w.heads
+    per_channel = "pchan" in w.mode
+    nsep = w.mode in ("nsep", "nsep_pchan")
+    scales = 2 * ((w.seqs * w.tokens // w.block_tokens) * w.heads * w.head_dim if per_channel else tok)
+    norms = 2 * tok if nsep else 0
+    signs = w.heads * w.head_dim if w.hadamard else 0
+    q = 2 * n + signs + n // 2 + norms + scales
+    return q, q
+
+
+def other_configs(torch, kvq, synth, dev, steps, warmup):
+    """Quantize and dequantize of the other workloads, each iteration after a 512 MiB write that
+    evicts L2 and the MALL (the events bracket the kernel only)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name in ("qwen_kv_layer", "batched_hadamard", "activation_4096"):
+        w = synth.WORKLOADS[name]
+        dt = synth.torch_dtype(w)
+        d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, 4, w.mode, w.block_tokens, w.hadamard, dt)
+        x = synth.make_x(w).to(dev)
+        sg = synth.make_signs(w).to(dev) if w.hadamard else None
+        out = kvq.alloc_outputs(d, dev)
+        y = torch.empty_like(x)
+        qb, db = config_bytes(w, w.mode)
+        for kname, fn, nbytes in (("quantize", lambda: kvq.quantize(d, x, sg, out=out, stream=stream), qb),
+                                  ("dequantize", lambda: kvq.dequantize(d, *out, sg, out_dtype=dt, out=y, stream=stream), db)):
+            for _ in range(warmup):
+                fn()
+            tot = 0.0
+            for _ in range(steps):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                tot += e0.elapsed_time(e1)
+            us = tot * 1e3 / steps
+            gbs = nbytes / (us * 1e-6) / 1e9
+            rows.append({"workload": name, "kernel": kname, "shape": [w.seqs, w.tokens, w.heads, w.head_dim],
+                         "mode": w.mode, "bits": 4, "hadamard": w.hadamard, "dtype": w.dtype, "us": round(us, 2),
+                         "bytes": nbytes, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        del x, y, out
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +152,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=10, help="sequences in the oracle baseline sample (0 = skip)")
     ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode"), default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
+    ap.add_argument("--other-configs", type=int, default=1,
+                    help="also time quantize / dequantize of the other workloads (1 = yes), after an L2/MALL flush")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain device-to-device copy of the fp16 input (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -242,6 +294,10 @@ def main():
                      "frac": round(qa / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
+    if args.other_configs:
+        del y
+        out["other_configs"] = other_configs(torch, kvq, synth, dev, min(args.steps, 10), min(args.warmup, 2))
+        y = None
     if args.cpu_seqs > 0:
         del x, y
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)

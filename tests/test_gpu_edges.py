@@ -131,3 +131,19 @@ def test_exact_ties_are_rounded_half_even(mode, had):
     # and the oracle agrees (its own decision in fp32 of the fp64 quotient)
     sp = oracle.Spec(1, 128, 2, 64, 4, mode, d.block_tokens if "pchan" in mode else 0, had)
     np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
+
+
+@pytest.mark.parametrize("dim,had", [(256, 0), (512, 64), (1024, 16)])
+@pytest.mark.parametrize("mode", ["naive", "nsep"])
+def test_exact_ties_wide_per_token(mode, dim, had):
+    # a vector spans several 128-channel row segments: every code is a tie and the exact max
+    # (the lone 7) sits in one segment, so the re-decision needs the max from another lane
+    x64, signs, want = grid.all_ties(had, seed=dim, T=96, H=2, D=dim)
+    d = kvq.Desc(1, 96, 2, dim, 4, mode, 0, had, torch.float16)
+    sg = None if signs is None else torch.from_numpy(signs).to(DEV)
+    codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).half().to(DEV), sg)
+    torch.cuda.synchronize()
+    got = oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy())
+    np.testing.assert_array_equal(got, want)
+    sp = oracle.Spec(1, 96, 2, dim, 4, mode, 0, had)
+    np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
