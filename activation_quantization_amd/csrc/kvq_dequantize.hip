@@ -10,6 +10,7 @@
 // values go out through XOR-swizzled LDS tiles so both HBM streams are coalesced.
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_launch.h"
 
 namespace kvq {
 
@@ -52,10 +53,12 @@ __device__ __forceinline__ void stage_row(unsigned char* stage, int row, const f
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-channel modes on the matrix cores.  A workgroup (4 waves) walks DQ_CHUNKS consecutive
-// 64-token chunks of one head-major (sequence, head) stream; wave w takes tokens
-// [16 w, 16 w + 16) of each chunk.  Three waves per SIMD keep enough loads in flight (an
-// explicit prefetch of the next chunk measured no faster).
+// Per-channel modes on the matrix cores.  The grid holds only as many workgroups (4 waves) as
+// fit on the chip at once; each walks an equal share of the 64-token chunks of all head-major
+// (sequence, head) streams, in order (a share may span streams), so no partly filled last
+// round of workgroups is left.  Wave w takes tokens [16 w, 16 w + 16) of each chunk.  Three
+// waves per SIMD keep enough loads in flight (an explicit prefetch of the next chunk measured
+// no faster).
 //
 //   x^[t, c] = norm[t] * sigma[c] / sqrt(n) * sum_k H[c, k] * scale[k] * code[t, k]
 //
@@ -69,7 +72,6 @@ __device__ __forceinline__ void stage_row(unsigned char* stage, int row, const f
 // holds tokens 4 g + r, channel L j + I; after all I it owns channels [L j, L j + L) of four
 // tokens, so the 16 lanes of a row store whole output rows.  The products scale * code are
 // exact in fp32 (11 x 4 bits).
-constexpr int DQ_CHUNKS = 8;
 
 template <int R>
 struct DqPre {
@@ -81,7 +83,7 @@ struct DqPre {
 
 template <int ODT, int R, int LG, int WPE = 3>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
-dequant_pchan_mfma(DequantArgs a, int64_t ngroups, int64_t gps, int vec) {
+dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
   constexpr int L = R / 16;                 // I-blocks: output channels per lane and token
   constexpr int KS = R / 32;                // K steps
   constexpr int LB = R / 8;                 // code bytes per lane and token
@@ -90,12 +92,7 @@ dequant_pchan_mfma(DequantArgs a, int64_t ngroups, int64_t gps, int vec) {
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int64_t grp = xcd_tile(blockIdx.x, ngroups);
-  const int64_t hs = grp / gps;                              // stream: s * heads + h
   const int64_t nch = a.tokens / 64;                         // 64-token chunks per stream
-  const int64_t ch0 = (grp - hs * gps) * DQ_CHUNKS;
-  const int nt = (int)(nch - ch0 < DQ_CHUNKS ? nch - ch0 : DQ_CHUNKS);
-  const int64_t s = hs / a.heads, h = hs - s * a.heads;
   const int64_t nb = a.tokens / a.block;
   const int lgb = __builtin_ctz((unsigned)a.block);          // block = 64, 128 or 256
 
@@ -114,139 +111,148 @@ dequant_pchan_mfma(DequantArgs a, int64_t ngroups, int64_t gps, int vec) {
                 ((uint32_t)(__builtin_popcount((uint32_t)((L * j) & (k0 + 4) & NMASK)) & 1) << 31);
     }
   }
-  uint32_t sgn = 0u;                                         // bit I: sigma[L j + I] < 0
-  if constexpr (LG != 0) {
-    const int8_t* sp = a.signs + h * R + L * j;
-    if constexpr (L == 8) {
-      const u32x2 v = *(const u32x2*)sp;
+  int64_t k = (int64_t)blockIdx.x * nchunks / gridDim.x;   // this workgroup's chunks [k, kend)
+  const int64_t kend = ((int64_t)blockIdx.x + 1) * nchunks / gridDim.x;
+  while (k < kend) {
+    const int64_t hs = k / nch;                                // stream: s * heads + h
+    const int64_t ch0 = k - hs * nch;
+    const int nt = (int)(kend - k < nch - ch0 ? kend - k : nch - ch0);
+    k += nt;
+    const int64_t s = hs / a.heads, h = hs - s * a.heads;
+    uint32_t sgn = 0u;                                         // bit I: sigma[L j + I] < 0
+    if constexpr (LG != 0) {
+      const int8_t* sp = a.signs + h * R + L * j;
+      if constexpr (L == 8) {
+        const u32x2 v = *(const u32x2*)sp;
 #pragma unroll
-      for (int I = 0; I < 8; ++I) sgn |= (((I < 4 ? v.x : v.y) >> (8 * (I & 3) + 7)) & 1u) << I;
-    } else {
-      const uint32_t v = *(const uint32_t*)sp;
-#pragma unroll
-      for (int I = 0; I < 4; ++I) sgn |= ((v >> (8 * I + 7)) & 1u) << I;
-    }
-  }
-
-  const unsigned char* cstream = a.codes + hs * a.tokens * (R / 2);
-  const uint16_t* nstream = a.nsep ? a.norms + hs * a.tokens : nullptr;
-  const uint16_t* sstream = a.scales + hs * nb * R;
-  auto load = [&](int i, DqPre<R>& p) {
-    const uint32_t t = (uint32_t)((ch0 + i) * 64) + 16 * w;   // stream token of the wave's first row
-    const unsigned char* cp = cstream + (size_t)(t + j) * (R / 2) + LB * g;
-    if constexpr (KS == 4) {
-      const u32x4 v = *(const u32x4*)cp;
-      p.wd[0] = v.x; p.wd[1] = v.y; p.wd[2] = v.z; p.wd[3] = v.w;
-    } else {
-      const u32x2 v = *(const u32x2*)cp;
-      p.wd[0] = v.x; p.wd[1] = v.y;
-    }
-    if (a.nsep) {
-      const uint16_t* np = nstream + t + 4 * g;
-      if (vec) {
-        const u32x2 v = *(const u32x2*)np;
-        p.nw[0] = v.x; p.nw[1] = v.y;
+        for (int I = 0; I < 8; ++I) sgn |= (((I < 4 ? v.x : v.y) >> (8 * (I & 3) + 7)) & 1u) << I;
       } else {
-        p.nw[0] = np[0] | ((uint32_t)np[1] << 16);
-        p.nw[1] = np[2] | ((uint32_t)np[3] << 16);
+        const uint32_t v = *(const uint32_t*)sp;
+#pragma unroll
+        for (int I = 0; I < 4; ++I) sgn |= ((v >> (8 * I + 7)) & 1u) << I;
       }
     }
-    const uint16_t* srow = sstream + (size_t)(t >> lgb) * R + (R / 4) * g;
-#pragma unroll
-    for (int K = 0; K < KS; ++K) {
-      if (vec) {
-        p.sc[K] = *(const u32x4*)(srow + 8 * K);
+
+    const unsigned char* cstream = a.codes + hs * a.tokens * (R / 2);
+    const uint16_t* nstream = a.nsep ? a.norms + hs * a.tokens : nullptr;
+    const uint16_t* sstream = a.scales + hs * nb * R;
+    auto load = [&](int i, DqPre<R>& p) {
+      const uint32_t t = (uint32_t)((ch0 + i) * 64) + 16 * w;   // stream token of the wave's first row
+      const unsigned char* cp = cstream + (size_t)(t + j) * (R / 2) + LB * g;
+      if constexpr (KS == 4) {
+        const u32x4 v = *(const u32x4*)cp;
+        p.wd[0] = v.x; p.wd[1] = v.y; p.wd[2] = v.z; p.wd[3] = v.w;
       } else {
-        uint32_t t4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t4[q] = srow[8 * K + 2 * q] | ((uint32_t)srow[8 * K + 2 * q + 1] << 16);
-        p.sc[K] = u32x4{t4[0], t4[1], t4[2], t4[3]};
+        const u32x2 v = *(const u32x2*)cp;
+        p.wd[0] = v.x; p.wd[1] = v.y;
       }
-    }
-  };
-
-  const size_t orow = (size_t)a.heads * R * OB;              // bytes between x rows
-  unsigned char* const ybase = (unsigned char*)a.y + ((s * a.tokens) * a.heads + h) * R * OB + L * j * OB;
-  DqPre<R> cur;
-  for (int i = 0; i < nt; ++i) {
-    load(i, cur);
-
-    // base fragments: scale pairs in the [n0 n4 n1 n5 ...] order, lane keep and sign masks
-    u32x4 base[KS];
-#pragma unroll
-    for (int K = 0; K < KS; ++K) {
-      const u32x4 v = cur.sc[K];                            // (s0 s1) (s2 s3) (s4 s5) (s6 s7)
-      const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (s0 s4)
-      const uint32_t p1 = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (s1 s5)
-      const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (s2 s6)
-      const uint32_t p3 = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (s3 s7)
-      base[K] = (u32x4{p0, p1, p2, p3} & keepm[K]) ^ negm[K];
-    }
-    // A operand: codes as fp16 pairs (c_q, c_{q+4}) = ((word ^ 0x88888888) >> 4 q & 0x000F000F | 0x64006400) - 1032
-    u32x4 av[KS];
-#pragma unroll
-    for (int K = 0; K < KS; ++K) {
-      const uint32_t xb = cur.wd[K] ^ 0x88888888u;
-      uint32_t q4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f16x2 hv2 = __builtin_bit_cast(f16x2, ((xb >> (4 * q)) & 0x000F000Fu) | 0x64006400u) -
-                          f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
-        q4[q] = __builtin_bit_cast(uint32_t, hv2);
+      if (a.nsep) {
+        const uint16_t* np = nstream + t + 4 * g;
+        if (vec) {
+          const u32x2 v = *(const u32x2*)np;
+          p.nw[0] = v.x; p.nw[1] = v.y;
+        } else {
+          p.nw[0] = np[0] | ((uint32_t)np[1] << 16);
+          p.nw[1] = np[2] | ((uint32_t)np[3] << 16);
+        }
       }
-      av[K] = u32x4{q4[0], q4[1], q4[2], q4[3]};
-    }
-    float nu[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) nu[r] = (a.nsep ? f16_to_f32(cur.nw[r >> 1] >> (16 * (r & 1))) : 1.f) * a.inv_sqrt_n;
-
-    // results: lane (g, j) owns channels [L j, L j + L) of tokens 4 g + r; f16/bf16 outputs are
-    // packed as each pair of I-blocks completes (fp32 outputs keep L floats per token)
-    constexpr int OW = ODT == DT_F32 ? L : L / 2;            // output words per token row
-    uint32_t ow[4][OW];
-#pragma unroll
-    for (int I = 0; I < L; ++I) {
-      const uint32_t sbit = ((sgn >> I) & 1u) << 31;              // sigma of column j's channel
-      uint32_t m[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n0 = q, n1 = q + 4;                       // nib of e = 2 q and 2 q + 1
-        if constexpr (LG == 0)
-          m[q] = ((n0 & (L - 1)) == I ? 0x0000ffffu : 0u) | ((n1 & (L - 1)) == I ? 0xffff0000u : 0u);
-        else
-          m[q] = ((__builtin_popcount(I & n0 & (L - 1)) & 1) ? 0x00008000u : 0u) |
-                 ((__builtin_popcount(I & n1 & (L - 1)) & 1) ? 0x80000000u : 0u);
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* srow = sstream + (size_t)(t >> lgb) * R + (R / 4) * g;
 #pragma unroll
       for (int K = 0; K < KS; ++K) {
-        const u32x4 bI = LG == 0 ? (base[K] & u32x4{m[0], m[1], m[2], m[3]}) : (base[K] ^ u32x4{m[0], m[1], m[2], m[3]});
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[K]), __builtin_bit_cast(f16x8, bI), acc,
-                                                     0, 0, 0);
+        if (vec) {
+          p.sc[K] = *(const u32x4*)(srow + 8 * K);
+        } else {
+          uint32_t t4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t4[q] = srow[8 * K + 2 * q] | ((uint32_t)srow[8 * K + 2 * q + 1] << 16);
+          p.sc[K] = u32x4{t4[0], t4[1], t4[2], t4[3]};
+        }
       }
+    };
+
+    const size_t orow = (size_t)a.heads * R * OB;              // bytes between x rows
+    unsigned char* const ybase = (unsigned char*)a.y + ((s * a.tokens) * a.heads + h) * R * OB + L * j * OB;
+    DqPre<R> cur;
+    for (int i = 0; i < nt; ++i) {
+      load(i, cur);
+
+      // base fragments: scale pairs in the [n0 n4 n1 n5 ...] order, lane keep and sign masks
+      u32x4 base[KS];
+#pragma unroll
+      for (int K = 0; K < KS; ++K) {
+        const u32x4 v = cur.sc[K];                            // (s0 s1) (s2 s3) (s4 s5) (s6 s7)
+        const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (s0 s4)
+        const uint32_t p1 = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (s1 s5)
+        const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (s2 s6)
+        const uint32_t p3 = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (s3 s7)
+        base[K] = (u32x4{p0, p1, p2, p3} & keepm[K]) ^ negm[K];
+      }
+      // A operand: codes as fp16 pairs (c_q, c_{q+4}) = ((word ^ 0x88888888) >> 4 q & 0x000F000F | 0x64006400) - 1032
+      u32x4 av[KS];
+#pragma unroll
+      for (int K = 0; K < KS; ++K) {
+        const uint32_t xb = cur.wd[K] ^ 0x88888888u;
+        uint32_t q4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f16x2 hv2 = __builtin_bit_cast(f16x2, ((xb >> (4 * q)) & 0x000F000Fu) | 0x64006400u) -
+                            f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
+          q4[q] = __builtin_bit_cast(uint32_t, hv2);
+        }
+        av[K] = u32x4{q4[0], q4[1], q4[2], q4[3]};
+      }
+      float nu[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nu[r] = (a.nsep ? f16_to_f32(cur.nw[r >> 1] >> (16 * (r & 1))) : 1.f) * a.inv_sqrt_n;
+
+      // results: lane (g, j) owns channels [L j, L j + L) of tokens 4 g + r; f16/bf16 outputs are
+      // packed as each pair of I-blocks completes (fp32 outputs keep L floats per token)
+      constexpr int OW = ODT == DT_F32 ? L : L / 2;            // output words per token row
+      uint32_t ow[4][OW];
+#pragma unroll
+      for (int I = 0; I < L; ++I) {
+        const uint32_t sbit = ((sgn >> I) & 1u) << 31;              // sigma of column j's channel
+        uint32_t m[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n0 = q, n1 = q + 4;                       // nib of e = 2 q and 2 q + 1
+          if constexpr (LG == 0)
+            m[q] = ((n0 & (L - 1)) == I ? 0x0000ffffu : 0u) | ((n1 & (L - 1)) == I ? 0xffff0000u : 0u);
+          else
+            m[q] = ((__builtin_popcount(I & n0 & (L - 1)) & 1) ? 0x00008000u : 0u) |
+                   ((__builtin_popcount(I & n1 & (L - 1)) & 1) ? 0x80000000u : 0u);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = 0; K < KS; ++K) {
+          const u32x4 bI = LG == 0 ? (base[K] & u32x4{m[0], m[1], m[2], m[3]}) : (base[K] ^ u32x4{m[0], m[1], m[2], m[3]});
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[K]), __builtin_bit_cast(f16x8, bI), acc,
+                                                       0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc[r] * nu[r]) ^ sbit);
+          if constexpr (ODT == DT_F32)
+            ow[r][I] = __builtin_bit_cast(uint32_t, v);
+          else if ((I & 1) == 0)
+            ow[r][I / 2] = __builtin_bit_cast(uint32_t, v);   // held until its partner arrives
+          else
+            ow[r][I / 2] = pack2<ODT>(__builtin_bit_cast(float, ow[r][I / 2]), v);
+        }
+        // one I-block's fragments live at a time
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // whole output rows: lanes j = 0..15 of a row cover the R channels of token 4 g + r
+      unsigned char* yw = ybase + (size_t)((ch0 + i) * 64 + 16 * w + 4 * g) * orow;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc[r] * nu[r]) ^ sbit);
-        if constexpr (ODT == DT_F32)
-          ow[r][I] = __builtin_bit_cast(uint32_t, v);
-        else if ((I & 1) == 0)
-          ow[r][I / 2] = __builtin_bit_cast(uint32_t, v);   // held until its partner arrives
-        else
-          ow[r][I / 2] = pack2<ODT>(__builtin_bit_cast(float, ow[r][I / 2]), v);
+        unsigned char* op = yw + r * orow;
+#pragma unroll
+        for (int q = 0; q < OW / 4; ++q)
+          *(u32x4*)(op + 16 * q) = u32x4{ow[r][4 * q], ow[r][4 * q + 1], ow[r][4 * q + 2], ow[r][4 * q + 3]};
+        if constexpr (OW % 4 == 2) *(u32x2*)(op + 16 * (OW / 4)) = u32x2{ow[r][OW - 2], ow[r][OW - 1]};
       }
-      // one I-block's fragments live at a time
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // whole output rows: lanes j = 0..15 of a row cover the R channels of token 4 g + r
-    unsigned char* yw = ybase + (size_t)((ch0 + i) * 64 + 16 * w + 4 * g) * orow;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      unsigned char* op = yw + r * orow;
-#pragma unroll
-      for (int q = 0; q < OW / 4; ++q)
-        *(u32x4*)(op + 16 * q) = u32x4{ow[r][4 * q], ow[r][4 * q + 1], ow[r][4 * q + 2], ow[r][4 * q + 3]};
-      if constexpr (OW % 4 == 2) *(u32x2*)(op + 16 * (OW / 4)) = u32x2{ow[r][OW - 2], ow[r][OW - 1]};
     }
   }
 }
@@ -325,11 +331,10 @@ __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t
 // ---------------------------------------------------------------------------------------
 template <int ODT, int R, int LG>
 static void dq_pchan_k(const DequantArgs& a, hipStream_t st) {
-  const int64_t nch = a.tokens / 64;                                   // blocks are multiples of 64
-  const int64_t gps = (nch + DQ_CHUNKS - 1) / DQ_CHUNKS;               // workgroups per stream
-  const int64_t ngroups = a.seqs * a.heads * gps;
+  const int64_t nchunks = a.seqs * a.heads * (a.tokens / 64);          // blocks are multiples of 64
+  const int64_t grid = persistent_grid(dequant_pchan_mfma<ODT, R, LG>, 256, nchunks);
   const int vec = ((uintptr_t)a.scales & 15u) == 0 && (!a.norms || ((uintptr_t)a.norms & 7u) == 0);
-  hipLaunchKernelGGL((dequant_pchan_mfma<ODT, R, LG>), dim3((unsigned)ngroups), dim3(256), 0, st, a, ngroups, gps, vec);
+  hipLaunchKernelGGL((dequant_pchan_mfma<ODT, R, LG>), dim3((unsigned)grid), dim3(256), 0, st, a, nchunks, vec);
 }
 
 template <int ODT, int R, int LG>

@@ -26,6 +26,7 @@
 //     the code is rne(fp32(v)), the rounding decision taken on the fp32 value of the quotient.
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_launch.h"
 
 namespace kvq {
 
@@ -173,35 +174,6 @@ __device__ __forceinline__ bool quantize_row(const float (&u)[R], InvF inv, uint
 }
 
 // ---------------------------------------------------------------------------------- exact
-// fp64 value of channel c of the unnormalized rotation of one input row (R values at `row`):
-// Y_c = sum over c's n-block of (-1)^popcount(c & j) s_j x_j.  Exact for fp16 inputs (the sum
-// of 128 fp16 values fits in 53 bits).
-template <int DT>
-__device__ __attribute__((noinline)) double exact_rot64(const unsigned char* __restrict__ row, const int8_t* __restrict__ sg, int c, int lg) {
-  if (lg == 0) {
-    const uint32_t h = *(const uint16_t*)(row + 2 * c);
-    return (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
-  }
-  const int n = 1 << lg, base = (c >> lg) << lg;
-  double acc = 0.0;
-#pragma unroll 1
-  for (int j0 = base; j0 < base + n; j0 += 8) {
-    const u32x4 v = *(const u32x4*)(row + 2 * j0);
-    const u32x2 s8 = *(const u32x2*)(sg + j0);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e;
-      const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
-      const double x = (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
-      const uint32_t sneg = ((e < 4 ? s8.x : s8.y) >> (8 * (e & 3) + 7)) & 1u;
-      const uint32_t hneg = (uint32_t)__builtin_popcount((uint32_t)(c & j & (n - 1))) & 1u;
-      acc += (sneg ^ hneg) ? -x : x;
-    }
-  }
-  return acc;
-}
-
 // the exact rounding decision: rne of the fp32 value of the fp64 quotient
 __device__ __forceinline__ uint32_t exact_code(double v) {
   return (uint32_t)(int)__builtin_rintf((float)v) & 0xfu;
@@ -234,50 +206,98 @@ __device__ __forceinline__ void load_tile_lds(unsigned char* lds, const unsigned
   }
 }
 
-// Per-token rare path, one lane per row segment: a code whose fp32 quotient lies within 2^-17
-// of a half-integer is re-decided from the exact quotient Q Y_c / max |Y| (the norm cancels in
-// both per-token modes).  That needs the exact Y_c and the exact max of the vector.  The fp32
-// transform is accurate to far better than a relative 2^-12 of the max, so the max is attained
-// among the channels whose fp32 magnitude is within that distance of the fp32 max; each lane
-// recomputes its own such channels in fp64 and the vector's L lanes reduce them.  Lanes of
-// vectors without a near-tie return at once.  row: this lane's input segment (global), sg: its
-// R sign bytes.
+// Exact fp64 value of channel c of the unnormalized rotation of one row segment (R inputs at
+// `row`, signs `sg`), computed by the whole wave: lane l takes channels 2l and 2l + 1, straight
+// from memory, and the sum over c's 2^LG-block is reduced across the lanes.  Exact for fp16
+// inputs (a sum of 128 fp16 values fits in 53 bits); every lane returns the same value.
 template <int DT, int R, int LG>
-__device__ __forceinline__ void ptok_fix(const float (&y)[R], float m, float inv_scale, float q, int L, uint64_t ball,
-                                         const unsigned char* __restrict__ row, const int8_t* __restrict__ sg,
-                                         unsigned char* stage_codes) {
-  constexpr int CRB = R / 2;
+__device__ __forceinline__ double wave_exact_y(const unsigned char* __restrict__ row, const int8_t* __restrict__ sg, int c) {
+  const int lane = threadIdx.x;
+  double t = 0.0;
+  if (lane < R / 2) {
+    const int j = 2 * lane;
+    const bool in0 = ((j ^ c) >> LG) == 0, in1 = (((j + 1) ^ c) >> LG) == 0;
+    if (in0 || in1) {
+      const uint32_t w = *(const uint32_t*)(row + 4 * lane);
+      double x0 = (double)lo_f32<DT>(w), x1 = (double)hi_f32<DT>(w);
+      if constexpr (LG != 0) {
+        constexpr int NM = (1 << LG) - 1;
+        const uint32_t s2 = *(const uint16_t*)(sg + j);
+        if (((s2 >> 7) ^ (uint32_t)__builtin_popcount(c & j & NM)) & 1u) x0 = -x0;
+        if (((s2 >> 15) ^ (uint32_t)__builtin_popcount(c & (j + 1) & NM)) & 1u) x1 = -x1;
+      }
+      t = (in0 ? x0 : 0.0) + (in1 ? x1 : 0.0);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+  return t;
+}
+
+// Per-token rare path.  A code whose fp32 quotient lies within 2^-17 of a half-integer is
+// re-decided from the exact quotient Q Y_c / max |Y| (the norm cancels in both per-token
+// modes); that needs the exact Y_c and the exact max of its vector.  The fp32 transform is
+// accurate to far better than a relative 2^-12 of the max, so the max is attained among the
+// channels whose fp32 magnitude lies within that distance of the fp32 max ("candidates", taken
+// only in vectors holding a near-tie).  Per channel, one ballot each gives the lanes with a
+// near-tie and with a candidate; channels with either are queued in LDS, and each (lane,
+// channel) item is then computed exactly by the whole wave: first the candidates (exact max
+// per lane, reduced over the vector's L lanes), then the near-ties, patched into the staged
+// codes.  xb: the tile's first input row segment; queue: 5 R words of LDS.
+template <int DT, int R, int LG>
+__device__ __forceinline__ void ptok_fix(const QuantArgs& a, const float (&y)[R], float m, float inv_scale, int L, int lgL,
+                                         uint64_t ball, int64_t seg0, const unsigned char* __restrict__ xb,
+                                         unsigned char* stage_codes, uint32_t* queue) {
+  constexpr int ROWB = 2 * R, CRB = R / 2;
   const int lane = threadIdx.x;
   const uint64_t gm = (L == 64 ? ~0ull : ((1ull << L) - 1ull)) << (lane & ~(L - 1));
-  if ((ball & gm) == 0ull) return;
-  uint32_t cand[R / 32], flg[R / 32];
+  const uint64_t fv = __ballot((ball & gm) != 0ull);      // lanes of vectors holding a near-tie
   const float thr = m - m * 0x1p-12f;
+  int nq = 0;
 #pragma unroll
-  for (int g = 0; g < R / 32; ++g) {
-    uint32_t cg = 0u, fg = 0u;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float v = y[32 * g + e];
-      const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_fmaf(v, inv_scale, MAGIC));
-      fg |= (uint32_t)((b & 0xffffu) == 0u) << e;
-      cg |= (uint32_t)(fabsf(v) >= thr) << e;
+  for (int i = 0; i < R; ++i) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_fmaf(y[i], inv_scale, MAGIC));
+    const uint64_t fb = __ballot((b & 0xffffu) == 0u) & ball;
+    const uint64_t cb = __ballot(fabsf(y[i]) >= thr) & fv;
+    if (fb | cb) {
+      if (lane == 0) {
+        queue[5 * nq] = (uint32_t)i;
+        queue[5 * nq + 1] = (uint32_t)fb;
+        queue[5 * nq + 2] = (uint32_t)(fb >> 32);
+        queue[5 * nq + 3] = (uint32_t)cb;
+        queue[5 * nq + 4] = (uint32_t)(cb >> 32);
+      }
+      ++nq;
     }
-    cand[g] = cg;
-    flg[g] = fg;
   }
-  double mx = 0.0;
-#pragma unroll 1
-  for (int g = 0; g < R / 32; ++g) {
-    for (uint32_t mk = cand[g]; mk; mk &= mk - 1u)
-      mx = fmax(mx, fabs(exact_rot64<DT>(row, sg, 32 * g + __builtin_ctz(mk), LG)));
+  wave_lds_sync();
+  auto row_signs = [&](int l) -> const int8_t* {
+    if constexpr (LG == 0) return nullptr;
+    const int64_t seg = seg0 + l;
+    return a.signs + ((seg >> lgL) % a.heads) * a.dim + (seg & (L - 1)) * R;
+  };
+  auto entry = [&](int k, int w) -> uint64_t {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)queue[5 * k + w]);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)queue[5 * k + w + 1]);
+    return ((uint64_t)hi << 32) | lo;
+  };
+  double mxl = 0.0;
+  for (int k = 0; k < nq; ++k) {
+    const int c = __builtin_amdgcn_readfirstlane((int)queue[5 * k]);
+    for (uint64_t cb = entry(k, 3); cb; cb &= cb - 1ull) {
+      const int l = __builtin_ctzll(cb);
+      const double v = fabs(wave_exact_y<DT, R, LG>(xb + l * ROWB, row_signs(l), c));
+      if (lane == l) mxl = fmax(mxl, v);
+    }
   }
-  for (int o = 1; o < L; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o));
-#pragma unroll 1
-  for (int g = 0; g < R / 32; ++g) {
-    for (uint32_t mk = flg[g]; mk; mk &= mk - 1u) {
-      const int c = 32 * g + __builtin_ctz(mk);
-      const uint32_t nib = mx > 0.0 ? exact_code((double)q * exact_rot64<DT>(row, sg, c, LG) / mx) : 0u;
-      patch_nibble(stage_codes, lane, CRB, c, nib);
+  for (int o = 1; o < L; o <<= 1) mxl = fmax(mxl, __shfl_xor(mxl, o));
+  for (int k = 0; k < nq; ++k) {
+    const int c = __builtin_amdgcn_readfirstlane((int)queue[5 * k]);
+    for (uint64_t fb = entry(k, 1); fb; fb &= fb - 1ull) {
+      const int l = __builtin_ctzll(fb);
+      const double v = wave_exact_y<DT, R, LG>(xb + l * ROWB, row_signs(l), c);
+      const double mx = __shfl(mxl, l);
+      if (lane == l) patch_nibble(stage_codes, l, CRB, c, mx > 0.0 ? exact_code((double)a.q * v / mx) : 0u);
     }
   }
 }
@@ -291,6 +311,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
   constexpr int ROWB = R * 2, CPR = ROWB / 16, CRB = R / 2, CCR = CRB / 16;
   __shared__ __attribute__((aligned(16))) unsigned char stage_in[64 * ROWB];
   __shared__ __attribute__((aligned(16))) unsigned char stage_codes[64 * CRB];
+  __shared__ uint32_t queue[5 * R];                             // near-tie work list
   const int lane = threadIdx.x;
   const int L = 1 << lgL;
   const int64_t G = gridDim.x;
@@ -386,7 +407,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
 
     // rare path: re-decide the near-ties exactly
     const uint64_t ball = __ballot(lane < nvalid && flagged);
-    if (ball) ptok_fix<DT, R, LG>(y, m, inv_scale, a.q, L, ball, xb + lane * ROWB, sg, stage_codes);
+    if (ball) ptok_fix<DT, R, LG>(a, y, m, inv_scale, L, lgL, ball, seg0, xb, stage_codes, queue);
     if (part == 0 && lane < nvalid) {
       const float nu = sqrtf(ss);
       const int64_t vh = head_major(a.heads, a.tokens, vec);
@@ -399,36 +420,6 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     pvalid = nvalid;
   }
   if (pseg0 >= 0) store_codes(pseg0, pvalid);
-}
-
-}  // namespace kvq
-#include <mutex>
-#include <unordered_map>
-namespace kvq {
-template <typename K>
-static int64_t persistent_grid(K kernel, int threads, int64_t ntiles) {
-  static std::mutex mu;
-  static std::unordered_map<uint64_t, int64_t> cache;     // (device, kernel) -> resident workgroups
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  const uint64_t key = ((uint64_t)(uintptr_t)(const void*)kernel << 8) ^ (uint64_t)dev;
-  int64_t g;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(key);
-    if (it == cache.end()) {
-      int cus = 0, per_cu = 0;
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
-      if (cus < 8) cus = 8;
-      g = (int64_t)per_cu * cus;
-      g -= g % 8;
-      cache.emplace(key, g);
-    } else {
-      g = it->second;
-    }
-  }
-  return ntiles < g ? ntiles : g;
 }
 
 template <int DT, int R, int LG>

@@ -108,9 +108,10 @@ def config_bytes(w, bits_mode):
 
 
 def other_configs(torch, kvq, synth, dev, steps, warmup):
-    """Quantize and dequantize of the other workloads, each iteration after a 512 MiB write that
-    evicts L2 and the MALL (the events bracket the kernel only)."""
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    """Quantize and dequantize of the other workloads, each iteration after a 512 MiB read that
+    evicts L2 and the MALL (the events bracket the kernel only).  A read, not a write: a written
+    flush buffer leaves dirty lines whose write-back would land inside the timed kernel."""
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     rows = []
     for name in ("qwen_kv_layer", "batched_hadamard", "activation_4096"):
@@ -128,7 +129,7 @@ def other_configs(torch, kvq, synth, dev, steps, warmup):
                 fn()
             tot = 0.0
             for _ in range(steps):
-                flush.fill_(1)
+                flush.sum()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 fn()

@@ -57,13 +57,15 @@ def make(bits, mode, hadamard, head_dim=64, seqs=2, tokens=128, heads=2, seed=0)
     return spec, x, signs, k.astype(np.int8)
 
 
-def all_ties(had, seed=0, T=128, H=2, D=64):
+def all_ties(had, seed=0, T=128, H=2, D=64, extra_max=0):
     """Every quotient an exact half-integer (or +-7): tokens are signed permutations of one
     multiset {7, half-integers} with the 7 in channel (t mod D), so all norms are equal and every
-    per-token and per-channel max is 7 * 2^p.  With a rotation of size 16 the input is
-    sigma * H y / 4 of such a y (exact in fp16)."""
+    per-token and per-channel max is 7 * 2^p.  extra_max > 0 turns that many of the half-integers
+    into further 7s (the max then sits in several channels).  With a rotation of size 16 the
+    input is sigma * H y / 4 of such a y (exact in fp16)."""
     rng = np.random.default_rng(seed)
     halves = rng.choice(np.arange(0.5, 7.0, 1.0), size=D - 1)
+    halves[:extra_max] = 7.0
     y = np.zeros((T, H, D))
     for t in range(T):
         for h in range(H):

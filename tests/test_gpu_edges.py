@@ -133,12 +133,13 @@ def test_exact_ties_are_rounded_half_even(mode, had):
     np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
 
 
-@pytest.mark.parametrize("dim,had", [(256, 0), (512, 64), (1024, 16)])
+@pytest.mark.parametrize("dim,had,extra_max", [(256, 0, 0), (512, 64, 0), (1024, 16, 0), (512, 64, 3), (128, 64, 2)])
 @pytest.mark.parametrize("mode", ["naive", "nsep"])
-def test_exact_ties_wide_per_token(mode, dim, had):
+def test_exact_ties_wide_per_token(mode, dim, had, extra_max):
     # a vector spans several 128-channel row segments: every code is a tie and the exact max
-    # (the lone 7) sits in one segment, so the re-decision needs the max from another lane
-    x64, signs, want = grid.all_ties(had, seed=dim, T=96, H=2, D=dim)
+    # (the 7s) sits in one segment, or in several, so the re-decision needs the max from other
+    # lanes
+    x64, signs, want = grid.all_ties(had, seed=dim, T=96, H=2, D=dim, extra_max=extra_max)
     d = kvq.Desc(1, 96, 2, dim, 4, mode, 0, had, torch.float16)
     sg = None if signs is None else torch.from_numpy(signs).to(DEV)
     codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).half().to(DEV), sg)
