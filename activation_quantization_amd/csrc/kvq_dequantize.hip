@@ -73,17 +73,22 @@ __device__ __forceinline__ void stage_row(unsigned char* stage, int row, const f
 // tokens, so the 16 lanes of a row store whole output rows.  The products scale * code are
 // exact in fp32 (11 x 4 bits).
 
-template <int R>
+template <int R, bool PT>
 struct DqPre {
   static constexpr int KS = R / 32;
   uint32_t wd[KS];          // packed codes of token j, channels (R/4) g ..
   uint32_t nw[2];           // fp16 norms of tokens 4 g + r, r = 0..3
-  u32x4 sc[KS];             // fp16 scales of channels (R/4) g + 8 K + [0, 8)
+  u32x4 sc[PT ? 1 : KS];    // per-channel: fp16 scales of channels (R/4) g + 8 K + [0, 8);
+                            // per-token: sc[0].x, .y = fp16 scales of tokens 4 g + r
 };
 
-template <int ODT, int R, int LG, int WPE = 3>
+//
+// Per-token scales (PT) use the same contraction with diag(scale) = I; the token's scale joins
+// its norm in the row factor.  A vector of D = 2^lgL R channels is 2^lgL row segments, each
+// walked as a stream of its own (the rotation is block-diagonal with blocks of at most R).
+template <int ODT, int R, int LG, bool PT, int WPE = 3>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
-dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
+dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
   constexpr int L = R / 16;                 // I-blocks: output channels per lane and token
   constexpr int KS = R / 32;                // K steps
   constexpr int LB = R / 8;                 // code bytes per lane and token
@@ -93,8 +98,8 @@ dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int64_t nch = a.tokens / 64;                         // 64-token chunks per stream
-  const int64_t nb = a.tokens / a.block;
-  const int lgb = __builtin_ctz((unsigned)a.block);          // block = 64, 128 or 256
+  const int64_t nb = PT ? 0 : a.tokens / a.block;           // per-channel scale blocks per stream
+  const int lgb = PT ? 0 : __builtin_ctz((unsigned)a.block); // block = 64, 128 or 256
 
   // lane constants: keep / sign masks of the base fragment per K; per I the constant pattern
   // with the lane's output sign folded in
@@ -114,14 +119,15 @@ dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
   int64_t k = (int64_t)blockIdx.x * nchunks / gridDim.x;   // this workgroup's chunks [k, kend)
   const int64_t kend = ((int64_t)blockIdx.x + 1) * nchunks / gridDim.x;
   while (k < kend) {
-    const int64_t hs = k / nch;                                // stream: s * heads + h
-    const int64_t ch0 = k - hs * nch;
+    const int64_t vs = k / nch;                                // (s * heads + h) 2^lgL + segment
+    const int64_t ch0 = k - vs * nch;
     const int nt = (int)(kend - k < nch - ch0 ? kend - k : nch - ch0);
     k += nt;
+    const int64_t hs = vs >> lgL, seg = vs & ((1 << lgL) - 1);
     const int64_t s = hs / a.heads, h = hs - s * a.heads;
     uint32_t sgn = 0u;                                         // bit I: sigma[L j + I] < 0
     if constexpr (LG != 0) {
-      const int8_t* sp = a.signs + h * R + L * j;
+      const int8_t* sp = a.signs + h * a.dim + seg * R + L * j;
       if constexpr (L == 8) {
         const u32x2 v = *(const u32x2*)sp;
 #pragma unroll
@@ -133,12 +139,13 @@ dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
       }
     }
 
-    const unsigned char* cstream = a.codes + hs * a.tokens * (R / 2);
+    const size_t cstride = (size_t)(R / 2) << lgL;             // code bytes between tokens
+    const unsigned char* cstream = a.codes + hs * a.tokens * cstride + seg * (R / 2);
     const uint16_t* nstream = a.nsep ? a.norms + hs * a.tokens : nullptr;
-    const uint16_t* sstream = a.scales + hs * nb * R;
-    auto load = [&](int i, DqPre<R>& p) {
+    const uint16_t* sstream = PT ? a.scales + hs * a.tokens : a.scales + hs * nb * R;
+    auto load = [&](int i, DqPre<R, PT>& p) {
       const uint32_t t = (uint32_t)((ch0 + i) * 64) + 16 * w;   // stream token of the wave's first row
-      const unsigned char* cp = cstream + (size_t)(t + j) * (R / 2) + LB * g;
+      const unsigned char* cp = cstream + (size_t)(t + j) * cstride + LB * g;
       if constexpr (KS == 4) {
         const u32x4 v = *(const u32x4*)cp;
         p.wd[0] = v.x; p.wd[1] = v.y; p.wd[2] = v.z; p.wd[3] = v.w;
@@ -156,31 +163,47 @@ dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
           p.nw[1] = np[2] | ((uint32_t)np[3] << 16);
         }
       }
-      const uint16_t* srow = sstream + (size_t)(t >> lgb) * R + (R / 4) * g;
-#pragma unroll
-      for (int K = 0; K < KS; ++K) {
+      if constexpr (PT) {
+        const uint16_t* sp = sstream + t + 4 * g;
         if (vec) {
-          p.sc[K] = *(const u32x4*)(srow + 8 * K);
+          const u32x2 v = *(const u32x2*)sp;
+          p.sc[0].x = v.x; p.sc[0].y = v.y;
         } else {
-          uint32_t t4[4];
+          p.sc[0].x = sp[0] | ((uint32_t)sp[1] << 16);
+          p.sc[0].y = sp[2] | ((uint32_t)sp[3] << 16);
+        }
+      } else {
+        const uint16_t* srow = sstream + (size_t)(t >> lgb) * R + (R / 4) * g;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) t4[q] = srow[8 * K + 2 * q] | ((uint32_t)srow[8 * K + 2 * q + 1] << 16);
-          p.sc[K] = u32x4{t4[0], t4[1], t4[2], t4[3]};
+        for (int K = 0; K < KS; ++K) {
+          if (vec) {
+            p.sc[K] = *(const u32x4*)(srow + 8 * K);
+          } else {
+            uint32_t t4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t4[q] = srow[8 * K + 2 * q] | ((uint32_t)srow[8 * K + 2 * q + 1] << 16);
+            p.sc[K] = u32x4{t4[0], t4[1], t4[2], t4[3]};
+          }
         }
       }
     };
 
-    const size_t orow = (size_t)a.heads * R * OB;              // bytes between x rows
-    unsigned char* const ybase = (unsigned char*)a.y + ((s * a.tokens) * a.heads + h) * R * OB + L * j * OB;
-    DqPre<R> cur;
+    const size_t orow = (size_t)a.heads * a.dim * OB;          // bytes between x rows
+    unsigned char* const ybase =
+        (unsigned char*)a.y + ((s * a.tokens) * a.heads + h) * a.dim * OB + (seg * R + L * j) * OB;
+    DqPre<R, PT> cur;
     for (int i = 0; i < nt; ++i) {
       load(i, cur);
 
-      // base fragments: scale pairs in the [n0 n4 n1 n5 ...] order, lane keep and sign masks
+      // base fragments: scale pairs in the [n0 n4 n1 n5 ...] order, lane keep and sign masks.
+      // Per-token scales make every B fragment loop-invariant; the opaque fp16 pair of ones
+      // keeps the compiler from holding all L KS of them in registers across chunks.
+      uint32_t one = 0x3C003C00u;
+      if constexpr (PT) asm volatile("" : "+v"(one));
       u32x4 base[KS];
 #pragma unroll
       for (int K = 0; K < KS; ++K) {
-        const u32x4 v = cur.sc[K];                            // (s0 s1) (s2 s3) (s4 s5) (s6 s7)
+        const u32x4 v = PT ? u32x4{one, one, one, one} : cur.sc[PT ? 0 : K];   // (s0 s1) (s2 s3) (s4 s5) (s6 s7)
         const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (s0 s4)
         const uint32_t p1 = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (s1 s5)
         const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (s2 s6)
@@ -203,7 +226,13 @@ dequant_pchan_mfma(DequantArgs a, int64_t nchunks, int vec) {
       }
       float nu[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nu[r] = (a.nsep ? f16_to_f32(cur.nw[r >> 1] >> (16 * (r & 1))) : 1.f) * a.inv_sqrt_n;
+      for (int r = 0; r < 4; ++r) {
+      nu[r] = (a.nsep ? f16_to_f32(cur.nw[r >> 1] >> (16 * (r & 1))) : 1.f) * a.inv_sqrt_n;
+      if constexpr (PT) {
+        const uint32_t sw = r < 2 ? cur.sc[0].x : cur.sc[0].y;
+        nu[r] *= f16_to_f32(sw >> (16 * (r & 1)));
+      }
+    }
 
       // results: lane (g, j) owns channels [L j, L j + L) of tokens 4 g + r; f16/bf16 outputs are
       // packed as each pair of I-blocks completes (fp32 outputs keep L floats per token)
@@ -329,12 +358,17 @@ __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t
 }
 
 // ---------------------------------------------------------------------------------------
+template <int ODT, int R, int LG, bool PT>
+static void dq_mfma_k(const DequantArgs& a, hipStream_t st, int lgL) {
+  const int64_t nchunks = (a.seqs * a.heads << lgL) * (a.tokens / 64);
+  const int64_t grid = persistent_grid(dequant_mfma<ODT, R, LG, PT>, 256, nchunks);
+  const int vec = ((uintptr_t)a.scales & (PT ? 7u : 15u)) == 0 && (!a.norms || ((uintptr_t)a.norms & 7u) == 0);
+  hipLaunchKernelGGL((dequant_mfma<ODT, R, LG, PT>), dim3((unsigned)grid), dim3(256), 0, st, a, nchunks, lgL, vec);
+}
+
 template <int ODT, int R, int LG>
 static void dq_pchan_k(const DequantArgs& a, hipStream_t st) {
-  const int64_t nchunks = a.seqs * a.heads * (a.tokens / 64);          // blocks are multiples of 64
-  const int64_t grid = persistent_grid(dequant_pchan_mfma<ODT, R, LG>, 256, nchunks);
-  const int vec = ((uintptr_t)a.scales & 15u) == 0 && (!a.norms || ((uintptr_t)a.norms & 7u) == 0);
-  hipLaunchKernelGGL((dequant_pchan_mfma<ODT, R, LG>), dim3((unsigned)grid), dim3(256), 0, st, a, nchunks, vec);
+  dq_mfma_k<ODT, R, LG, false>(a, st, 0);               // blocks are multiples of 64 tokens
 }
 
 template <int ODT, int R, int LG>
@@ -342,6 +376,10 @@ static void dq_ptok_k(const DequantArgs& a, hipStream_t st) {
   constexpr int OB = ODT == DT_F32 ? 4 : 2;
   int lgL = 0;
   while ((R << lgL) < a.dim) ++lgL;
+  if (a.tokens % 64 == 0) {                             // whole 64-token chunks: matrix cores
+    dq_mfma_k<ODT, R, LG, true>(a, st, lgL);
+    return;
+  }
   const int64_t nseg = a.seqs * a.tokens * a.heads * (a.dim / R);
   const int64_t ntiles = (nseg + 63) / 64;
   hipLaunchKernelGGL((dequant_ptok_kernel<ODT, R, LG>), dim3((unsigned)ntiles), dim3(64), (size_t)64 * R * OB, st, a,

@@ -57,6 +57,22 @@ def test_per_token_ragged_and_wide(rows, heads, dim, had, mode, dtype):
     run_full(d, x, signs)
 
 
+@pytest.mark.parametrize("seqs,rows,heads,dim,had,mode", [
+    (2, 128, 3, 64, 16, "naive"), (2, 64, 3, 128, 128, "nsep"), (3, 128, 2, 512, 64, "nsep"),
+    (1, 192, 1, 8192, 128, "naive"), (2, 64, 5, 1024, 0, "nsep"),
+])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_per_token_whole_chunks(seqs, rows, heads, dim, had, mode, dtype):
+    # tokens per sequence a multiple of 64: per-token dequantize runs on the matrix cores, a
+    # vector of more than 128 channels walked as 128-channel segments
+    rng = np.random.default_rng(seqs * rows * dim + heads)
+    x = torch.from_numpy(rng.standard_normal((seqs * rows, heads, dim)).astype(np.float32) *
+                         rng.uniform(0.2, 4.0, size=(seqs * rows, 1, 1)).astype(np.float32)).to(dtype)
+    signs = torch.from_numpy(rng.choice(np.array([-1, 1], np.int8), size=(heads, dim))) if had else None
+    d = kvq.Desc(seqs, rows, heads, dim, 4, mode, 0, had, dtype)
+    run_full(d, x, signs)
+
+
 def test_block_256_d64():
     w = synth.scaled("single_head_d64", tokens=1024, heads=3)
     d = kvq.Desc(1, 1024, 3, 64, 3, "nsep_pchan", 256, 64, torch.float16)
