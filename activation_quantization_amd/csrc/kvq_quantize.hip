@@ -206,25 +206,25 @@ __device__ __forceinline__ void load_tile_lds(unsigned char* lds, const unsigned
   }
 }
 
-// Exact fp64 value of channel c of the unnormalized rotation of one row segment (R inputs at
-// `row`, signs `sg`), computed by the whole wave: lane l takes channels 2l and 2l + 1, straight
-// from memory, and the sum over c's 2^LG-block is reduced across the lanes.  Exact for fp16
+// Exact fp64 value of channel c of the unnormalized rotation of row `r` of a staged tile
+// (R signed inputs per row, XOR-swizzled), computed by the whole wave: lane l takes channels
+// 2l and 2l + 1, and the sum over c's 2^LG-block is reduced across the lanes.  Exact for fp16
 // inputs (a sum of 128 fp16 values fits in 53 bits); every lane returns the same value.
 template <int DT, int R, int LG>
-__device__ __forceinline__ double wave_exact_y(const unsigned char* __restrict__ row, const int8_t* __restrict__ sg, int c) {
+__device__ __forceinline__ double wave_exact_y(const unsigned char* tile, int r, int c) {
+  constexpr int ROWB = 2 * R;
   const int lane = threadIdx.x;
   double t = 0.0;
   if (lane < R / 2) {
     const int j = 2 * lane;
     const bool in0 = ((j ^ c) >> LG) == 0, in1 = (((j + 1) ^ c) >> LG) == 0;
     if (in0 || in1) {
-      const uint32_t w = *(const uint32_t*)(row + 4 * lane);
+      const uint32_t w = *(const uint32_t*)(tile + r * ROWB + swz_chunk(r, lane >> 2, ROWB) * 16 + (lane & 3) * 4);
       double x0 = (double)lo_f32<DT>(w), x1 = (double)hi_f32<DT>(w);
       if constexpr (LG != 0) {
         constexpr int NM = (1 << LG) - 1;
-        const uint32_t s2 = *(const uint16_t*)(sg + j);
-        if (((s2 >> 7) ^ (uint32_t)__builtin_popcount(c & j & NM)) & 1u) x0 = -x0;
-        if (((s2 >> 15) ^ (uint32_t)__builtin_popcount(c & (j + 1) & NM)) & 1u) x1 = -x1;
+        if (__builtin_popcount(c & j & NM) & 1) x0 = -x0;
+        if (__builtin_popcount(c & (j + 1) & NM) & 1) x1 = -x1;
       }
       t = (in0 ? x0 : 0.0) + (in1 ? x1 : 0.0);
     }
@@ -243,12 +243,11 @@ __device__ __forceinline__ double wave_exact_y(const unsigned char* __restrict__
 // near-tie and with a candidate; channels with either are queued in LDS, and each (lane,
 // channel) item is then computed exactly by the whole wave: first the candidates (exact max
 // per lane, reduced over the vector's L lanes), then the near-ties, patched into the staged
-// codes.  xb: the tile's first input row segment; queue: 5 R words of LDS.
+// codes.  tile: the staged input tile, signs applied; queue: 5 R words of LDS.
 template <int DT, int R, int LG>
-__device__ __forceinline__ void ptok_fix(const QuantArgs& a, const float (&y)[R], float m, float inv_scale, int L, int lgL,
-                                         uint64_t ball, int64_t seg0, const unsigned char* __restrict__ xb,
-                                         unsigned char* stage_codes, uint32_t* queue) {
-  constexpr int ROWB = 2 * R, CRB = R / 2;
+__device__ __forceinline__ void ptok_fix(const float (&y)[R], float m, float inv_scale, float q, int L, uint64_t ball,
+                                         const unsigned char* tile, unsigned char* stage_codes, uint32_t* queue) {
+  constexpr int CRB = R / 2;
   const int lane = threadIdx.x;
   const uint64_t gm = (L == 64 ? ~0ull : ((1ull << L) - 1ull)) << (lane & ~(L - 1));
   const uint64_t fv = __ballot((ball & gm) != 0ull);      // lanes of vectors holding a near-tie
@@ -271,11 +270,6 @@ __device__ __forceinline__ void ptok_fix(const QuantArgs& a, const float (&y)[R]
     }
   }
   wave_lds_sync();
-  auto row_signs = [&](int l) -> const int8_t* {
-    if constexpr (LG == 0) return nullptr;
-    const int64_t seg = seg0 + l;
-    return a.signs + ((seg >> lgL) % a.heads) * a.dim + (seg & (L - 1)) * R;
-  };
   auto entry = [&](int k, int w) -> uint64_t {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)queue[5 * k + w]);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)queue[5 * k + w + 1]);
@@ -286,7 +280,7 @@ __device__ __forceinline__ void ptok_fix(const QuantArgs& a, const float (&y)[R]
     const int c = __builtin_amdgcn_readfirstlane((int)queue[5 * k]);
     for (uint64_t cb = entry(k, 3); cb; cb &= cb - 1ull) {
       const int l = __builtin_ctzll(cb);
-      const double v = fabs(wave_exact_y<DT, R, LG>(xb + l * ROWB, row_signs(l), c));
+      const double v = fabs(wave_exact_y<DT, R, LG>(tile, l, c));
       if (lane == l) mxl = fmax(mxl, v);
     }
   }
@@ -295,9 +289,9 @@ __device__ __forceinline__ void ptok_fix(const QuantArgs& a, const float (&y)[R]
     const int c = __builtin_amdgcn_readfirstlane((int)queue[5 * k]);
     for (uint64_t fb = entry(k, 1); fb; fb &= fb - 1ull) {
       const int l = __builtin_ctzll(fb);
-      const double v = wave_exact_y<DT, R, LG>(xb + l * ROWB, row_signs(l), c);
+      const double v = wave_exact_y<DT, R, LG>(tile, l, c);
       const double mx = __shfl(mxl, l);
-      if (lane == l) patch_nibble(stage_codes, l, CRB, c, mx > 0.0 ? exact_code((double)a.q * v / mx) : 0u);
+      if (lane == l) patch_nibble(stage_codes, l, CRB, c, mx > 0.0 ? exact_code((double)q * v / mx) : 0u);
     }
   }
 }
@@ -309,7 +303,7 @@ __device__ __forceinline__ void ptok_fix(const QuantArgs& a, const float (&y)[R]
 template <int DT, int R, int LG>
 __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nseg, int64_t ntiles, int lgL) {
   constexpr int ROWB = R * 2, CPR = ROWB / 16, CRB = R / 2, CCR = CRB / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char stage_in[64 * ROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_in[2][64 * ROWB];   // current / prefetched tile
   __shared__ __attribute__((aligned(16))) unsigned char stage_codes[64 * CRB];
   __shared__ uint32_t queue[5 * R];                             // near-tie work list
   const int lane = threadIdx.x;
@@ -337,8 +331,9 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
   int64_t pseg0 = -1;
   int pvalid = 0;
   if (v < ntiles && xcd_tile(v, ntiles) < full_tiles)
-    load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + xcd_tile(v, ntiles) * 64 * ROWB, ROWB, 64, 0, 1, lane);
-  for (; v < ntiles; v += G) {
+    load_tile_lds<ROWB>(stage_in[0], (const unsigned char*)a.x + xcd_tile(v, ntiles) * 64 * ROWB, ROWB, 64, 0, 1, lane);
+  for (int buf = 0; v < ntiles; v += G, buf ^= 1) {
+    unsigned char* const tile = stage_in[buf];
     const int64_t seg0 = xcd_tile(v, ntiles) * 64;
     const int nvalid = (int)(nseg - seg0 < 64 ? nseg - seg0 : 64);
     const unsigned char* xb = (const unsigned char*)a.x + seg0 * ROWB;
@@ -350,7 +345,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
         const int row = q / CPR, cc = q % CPR;
         u32x4 t = {0u, 0u, 0u, 0u};
         if (row < nvalid) t = __builtin_nontemporal_load((const u32x4*)(xb + row * ROWB + cc * 16));
-        *(u32x4*)(stage_in + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = t;
+        *(u32x4*)(tile + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = t;
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the prefetch landed
@@ -358,7 +353,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     uint32_t wv[R / 2];
 #pragma unroll
     for (int cc = 0; cc < CPR; ++cc) {
-      const u32x4 t = *(const u32x4*)(stage_in + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16);
+      const u32x4 t = *(const u32x4*)(tile + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16);
       wv[4 * cc] = t.x; wv[4 * cc + 1] = t.y; wv[4 * cc + 2] = t.z; wv[4 * cc + 3] = t.w;
     }
     wave_lds_sync();
@@ -368,11 +363,17 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     const int64_t h = vec % a.heads;
     const int8_t* sg = a.signs ? a.signs + h * a.dim + part * R : nullptr;
     // per-lane signs are vector loads: apply them before the next prefetch is in flight, so
-    // their wait does not include it; then store the previous tile's codes and prefetch
-    if constexpr (LG != 0) apply_signs_packed<R>(wv, sg);
+    // their wait does not include it; then store the previous tile's codes and prefetch.  The
+    // signed row goes back into the tile, where the exact near-tie path reads it.
+    if constexpr (LG != 0) {
+      apply_signs_packed<R>(wv, sg);
+#pragma unroll
+      for (int cc = 0; cc < CPR; ++cc)
+        *(u32x4*)(tile + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16) = u32x4{wv[4 * cc], wv[4 * cc + 1], wv[4 * cc + 2], wv[4 * cc + 3]};
+    }
     if (pseg0 >= 0) store_codes(pseg0, pvalid);
     if (v + G < ntiles && xcd_tile(v + G, ntiles) < full_tiles)
-      load_tile_lds<ROWB>(stage_in, (const unsigned char*)a.x + xcd_tile(v + G, ntiles) * 64 * ROWB, ROWB, 64, 0, 1, lane);
+      load_tile_lds<ROWB>(stage_in[buf ^ 1], (const unsigned char*)a.x + xcd_tile(v + G, ntiles) * 64 * ROWB, ROWB, 64, 0, 1, lane);
 
     float ss = 0.f;
     if (a.nsep) {
@@ -407,7 +408,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
 
     // rare path: re-decide the near-ties exactly
     const uint64_t ball = __ballot(lane < nvalid && flagged);
-    if (ball) ptok_fix<DT, R, LG>(a, y, m, inv_scale, L, lgL, ball, seg0, xb, stage_codes, queue);
+    if (ball) ptok_fix<DT, R, LG>(y, m, inv_scale, a.q, L, ball, tile, stage_codes, queue);
     if (part == 0 && lane < nvalid) {
       const float nu = sqrtf(ss);
       const int64_t vh = head_major(a.heads, a.tokens, vec);
