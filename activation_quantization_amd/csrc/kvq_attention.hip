@@ -18,9 +18,9 @@
 // head, and the value sum runs on the vector units with v_dot2_f32_f16: the block's V codes are
 // copied to LDS (global_load_lds), lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens
 // t = a (mod 4) and takes them two at a time (t, t + 4) as fp16 subnormal pairs against the pair
-// (p' = p norm_v) of each head.  Each wave writes (m, l, partial sum) per query head to the
-// caller's workspace.  Pass 2 merges the partials of a head (log-sum-exp weights), rotates the
-// result back and writes it.
+// (p' = p norm_v) of each head.  The four waves' (m, l, partial sum) are merged in LDS and the
+// workgroup writes one partial per query head to the caller's workspace.  Pass 2 merges the
+// partials of a head (log-sum-exp weights), rotates the result back and writes it.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -287,7 +287,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     asm volatile("" ::: "memory");
   }
 
-  // 5. the wave's partial: sum the four token classes a, then lanes 0..15 write
+  // 5. the wave's partial: sum the four token classes a (lanes 0..15 then hold it)
 #pragma unroll
   for (int h = 0; h < GM; ++h)
 #pragma unroll
@@ -297,25 +297,46 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       v += __shfl_xor(v, 32);
       o[h][c] = v;
     }
-  const int64_t NP = nchunks * 4;
-  const int64_t pidx = ci * 4 + w;
-  for (int h = 0; h < G; ++h) {
-    float* wp = a.ws + ((s * a.q_heads + kvh * G + h) * NP + pidx) * (R + 2);
-    if (lane < 16) {
+  // 6. merge the four waves' partials through LDS (each wave's V buffer is free now), then one
+  // partial (max, sum, vector) per head for the workgroup
+  float* mw = (float*)&vbuf[w][0];                         // [GM][R] sums, [GM] maxima, [GM] sums of p
+  if (lane < 16) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float v = 0.f;
+    for (int h = 0; h < GM; ++h)
 #pragma unroll
-        for (int hh = 0; hh < GM; ++hh)
-          if (hh == h) v = o[hh][c];
-        wp[8 * lane + c] = v;
-      }
-    }
+      for (int c = 0; c < 8; ++c) mw[h * R + 8 * lane + c] = o[h][c];
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
     const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_row[h & 1]), 16 * (h >> 1)));
     const float lh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_row[h & 1]), 16 * (h >> 1)));
     if (lane == 0) {
-      wp[R] = mh;
-      wp[R + 1] = lh;
+      mw[GM * R + h] = mh;
+      mw[GM * R + GM + h] = lh;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * R; e += 256) {
+    const int h = e / R, c = e - h * R;
+    float mx[4], M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      mx[ww] = ((const float*)&vbuf[ww][0])[GM * R + h];
+      M = fmaxf(M, mx[ww]);
+    }
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float* pw4 = (const float*)&vbuf[ww][0];
+      const float f = mx[ww] == -INFINITY ? 0.f : exp_f(mx[ww] - M);
+      L += f * pw4[GM * R + GM + h];
+      O += f * pw4[h * R + c];
+    }
+    float* wp = a.ws + ((s * a.q_heads + kvh * G + h) * nchunks + ci) * (R + 2);
+    wp[c] = O;
+    if (c == 0) {
+      wp[R] = M;
+      wp[R + 1] = L;
     }
   }
 }
@@ -330,8 +351,10 @@ __global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
   const int64_t kvh = hq / (a.q_heads / a.heads);
   const float* wp = a.ws + shq * NP * (R + 2);
   float M = -INFINITY;
+#pragma unroll 4
   for (int64_t p = 0; p < NP; ++p) M = fmaxf(M, wp[p * (R + 2) + R]);
   float L = 0.f, O = 0.f;
+#pragma unroll 4
   for (int64_t p = 0; p < NP; ++p) {
     const float m = wp[p * (R + 2) + R];
     const float f = m == -INFINITY ? 0.f : exp_f(m - M);
@@ -360,7 +383,7 @@ __global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
 
 int64_t attention_partials(const AttnArgs& a) {
   const int64_t nunits = a.tokens / a.block;
-  return ((nunits + ATT_UNITS_PER_GROUP - 1) / ATT_UNITS_PER_GROUP) * 4;
+  return (nunits + ATT_UNITS_PER_GROUP - 1) / ATT_UNITS_PER_GROUP;     // one per workgroup
 }
 
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t st) {
@@ -373,7 +396,7 @@ hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((attn_partial<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(a.seqs * a.q_heads)), dim3(128), 0, st, a, nchunks * 4);
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(a.seqs * a.q_heads)), dim3(128), 0, st, a, nchunks);
   return hipGetLastError();
 }
 

@@ -130,10 +130,10 @@ def _att(d, q_heads=16, ws_bytes=1 << 30, **ptr):
 
 
 def test_attention_workspace_size():
-    d = kvq.Desc(**GOOD)                                   # 2 seqs x 256 tokens: 2 blocks -> 1 chunk -> 4 partials
-    assert kvq.attention_workspace_bytes(d, 16) == 2 * 16 * 4 * (128 + 2) * 4
+    d = kvq.Desc(**GOOD)                                   # 2 seqs x 256 tokens: 2 blocks -> 1 chunk -> 1 partial
+    assert kvq.attention_workspace_bytes(d, 16) == 2 * 16 * 1 * (128 + 2) * 4
     long = kvq.Desc(64, 32768, 8, 128, 4, "nsep_pchan", 128, 128)
-    assert kvq.attention_workspace_bytes(long, 32) == 64 * 32 * (256 // 16) * 4 * 130 * 4
+    assert kvq.attention_workspace_bytes(long, 32) == 64 * 32 * (256 // 16) * 130 * 4
     assert kvq.attention_workspace_bytes(kvq.Desc(**{**GOOD, "mode": "nsep"}), 16) == -1
     assert kvq.attention_workspace_bytes(d, 20) == -1     # 5 query heads per KV head
 
