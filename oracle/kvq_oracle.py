@@ -240,6 +240,57 @@ def attention_decode(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, spec: 
     return out
 
 
+# ----------------------------------------------------------------------------- streaming append
+@dataclasses.dataclass
+class StreamState:
+    """A cache after a run of appends: whole B-token blocks quantized, the rest at full precision."""
+    cached: int                   # tokens appended per sequence so far
+    quantized: Quantized | None   # the whole blocks, [seqs * whole, heads, D] (None when there is none)
+    residual: np.ndarray          # the trailing cached - whole tokens, [seqs, r, heads, D] float64
+
+
+def stream_state(x_hist: np.ndarray, spec: Spec, signs: np.ndarray | None = None) -> StreamState:
+    """The cache after every token of x_hist ([seqs, n, heads, D]) has been appended, by any
+    number of appends of any sizes (NSNQuant summary, "implementation details": the cache is a
+    quantized part plus a full-precision residual; a residual that fills up is quantized and
+    joins the quantized part).
+
+    With per-channel scales a block can only be quantized once all its B tokens are there, so
+    the quantized part is the floor(n / B) whole blocks, quantized exactly as quantize() does a
+    cache of that many tokens, and the residual is the last n mod B tokens, unchanged.
+    """
+    x_hist = np.asarray(x_hist, dtype=np.float64)
+    S, n, Hh, D = x_hist.shape
+    assert spec.per_channel and Hh == spec.heads and D == spec.head_dim
+    B = spec.block_tokens
+    whole = (n // B) * B
+    qz = None
+    if whole:
+        qz = quantize(x_hist[:, :whole].reshape(S * whole, Hh, D), dataclasses.replace(spec, seqs=S, tokens=whole), signs)
+    return StreamState(cached=n, quantized=qz, residual=x_hist[:, whole:].copy())
+
+
+def attention_decode_stream(q: np.ndarray, k_hat: np.ndarray | None, v_hat: np.ndarray | None,
+                            k_res: np.ndarray, v_res: np.ndarray, spec: Spec) -> np.ndarray:
+    """Decode attention over a streamed cache, in float64: one softmax over the Tq dequantized
+    cached tokens (k_hat, v_hat: [seqs * Tq, heads, D], or None when Tq = 0) followed by the r
+    residual tokens at full precision (k_res, v_res: [seqs, r, heads, D]); otherwise exactly
+    attention_decode (scores q . k / sqrt(D), query head hq reads KV head hq // G)."""
+    q = np.asarray(q, dtype=np.float64)
+    S = q.shape[0]
+    Hh, D = spec.heads, spec.head_dim
+    r = k_res.shape[1]
+    Tq = 0 if k_hat is None else k_hat.shape[0] // S
+    parts_k = [np.asarray(k_res, dtype=np.float64)]
+    parts_v = [np.asarray(v_res, dtype=np.float64)]
+    if Tq:
+        parts_k.insert(0, np.asarray(k_hat, dtype=np.float64).reshape(S, Tq, Hh, D))
+        parts_v.insert(0, np.asarray(v_hat, dtype=np.float64).reshape(S, Tq, Hh, D))
+    kk = np.concatenate(parts_k, axis=1).reshape(S * (Tq + r), Hh, D)
+    vv = np.concatenate(parts_v, axis=1).reshape(S * (Tq + r), Hh, D)
+    return attention_decode(q, kk, vv, dataclasses.replace(spec, seqs=S, tokens=Tq + r))
+
+
 # ----------------------------------------------------------------------------- error report
 def reconstruction_errors(x: np.ndarray, x_hat: np.ndarray, outlier_mask: np.ndarray) -> dict:
     """Four relative-error measures of a reconstruction (for the mode ordering check).
