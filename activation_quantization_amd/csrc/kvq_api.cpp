@@ -126,6 +126,26 @@ int64_t kvq_scales_count(const kvq_desc* d) {
   return pchan_mode(d->mode) ? rows / d->block_tokens * d->heads * d->head_dim : rows * d->heads;
 }
 
+namespace {
+kvq::QuantArgs quant_args(const kvq_desc* d, const void* x, const int8_t* signs, uint8_t* codes, uint16_t* norms,
+                          uint16_t* scales) {
+  kvq::QuantArgs a{};
+  a.x = x; a.signs = signs; a.codes = codes; a.norms = norms; a.scales = scales;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.q = qmax(d->bits);
+  a.scale_mul = float((d->hadamard ? 1.0 / std::sqrt(double(d->hadamard)) : 1.0) / double(qmax(d->bits)));
+  a.nsep = nsep_mode(d->mode);
+  a.dtype = d->dtype == KVQ_F16 ? kvq::DT_F16 : kvq::DT_BF16;
+  a.in_seq_tokens = d->tokens_per_seq;
+  a.out_tokens = d->tokens_per_seq;
+  a.out_tok0 = 0;
+  return a;
+}
+}  // namespace
+
 kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs, uint8_t* codes,
                         uint16_t* norms, uint16_t* scales, void* stream) {
   kvq_status s = check_desc(d);
@@ -142,19 +162,66 @@ kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs, u
     return fail(KVQ_ERR_ALIGN, "norms and scales must be 2-byte aligned");
   if ((s = device_ready()) != KVQ_OK) return s;
 
-  kvq::QuantArgs a{};
-  a.x = x; a.signs = signs; a.codes = codes; a.norms = norms; a.scales = scales;
-  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim;
-  a.block = d->block_tokens;
-  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
-  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
-  a.q = qmax(d->bits);
-  a.scale_mul = float((d->hadamard ? 1.0 / std::sqrt(double(d->hadamard)) : 1.0) / double(qmax(d->bits)));
-  a.nsep = nsep_mode(d->mode);
-  a.dtype = d->dtype == KVQ_F16 ? kvq::DT_F16 : kvq::DT_BF16;
+  const kvq::QuantArgs a = quant_args(d, x, signs, codes, norms, scales);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return launched(pchan_mode(d->mode) ? kvq::launch_quantize_pchan(a, st) : kvq::launch_quantize_ptok(a, st),
                   "quantize");
+}
+
+kvq_status kvq_append(const kvq_desc* d, int64_t tokens_cached, const void* x_new, int64_t n_new, void* residual,
+                      const int8_t* signs, uint8_t* codes, uint16_t* norms, uint16_t* scales, void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (!pchan_mode(d->mode))
+    return fail(KVQ_ERR_UNSUPPORTED, "the streaming append is for per-channel modes (per-token codes need no residual)");
+  if (tokens_cached < 0 || n_new < 0 || tokens_cached > d->tokens_per_seq - n_new)
+    return fail(KVQ_ERR_SHAPE, "tokens_cached %lld + n_new %lld must stay within the capacity tokens_per_seq %lld",
+                (long long)tokens_cached, (long long)n_new, (long long)d->tokens_per_seq);
+  if (d->seqs == 0 || n_new == 0) return ok();
+  if (!x_new || !residual || !codes || !scales) return fail(KVQ_ERR_NULL, "x_new, residual, codes and scales are required");
+  if (nsep_mode(d->mode) != (norms != nullptr))
+    return fail(KVQ_ERR_NULL, nsep_mode(d->mode) ? "NSEP modes need a norms buffer" : "norms must be NULL without NSEP");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(x_new, 16) || !aligned(residual, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "x_new, residual, codes and signs must be 16-byte aligned");
+  if (!aligned(scales, 2) || (norms && !aligned(norms, 2)))
+    return fail(KVQ_ERR_ALIGN, "norms and scales must be 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+
+  // the residual holds tokens [whole, tokens_cached) of every sequence in its first slots
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t B = d->block_tokens, S = d->seqs;
+  const int64_t rowb = d->heads * d->head_dim * 2;              // bytes per token (fp16 / bf16)
+  const unsigned char* xn = static_cast<const unsigned char*>(x_new);
+  unsigned char* res = static_cast<unsigned char*>(residual);
+  const kvq::QuantArgs base = quant_args(d, nullptr, signs, codes, norms, scales);
+  auto quantize_blocks = [&](const void* x, int64_t tokens, int64_t in_seq_tokens, int64_t out_tok0) {
+    kvq::QuantArgs a = base;
+    a.x = x; a.tokens = tokens; a.in_seq_tokens = in_seq_tokens; a.out_tok0 = out_tok0;
+    return kvq::launch_quantize_pchan(a, st);
+  };
+  int64_t whole = tokens_cached - tokens_cached % B, r = tokens_cached % B, used = 0;
+  hipError_t e = hipSuccess;
+  if (r > 0) {                                                   // top up the residual
+    const int64_t k = n_new < B - r ? n_new : B - r;
+    e = kvq::launch_copy_tokens(xn, res + r * rowb, S, k, rowb, n_new, B, st);
+    used = k;
+    r += k;
+    if (e == hipSuccess && r == B) {                             // it filled: quantize it into the cache
+      e = quantize_blocks(res, B, B, whole);
+      whole += B;
+      r = 0;
+    }
+  }
+  const int64_t full = (n_new - used) / B * B;                   // whole blocks straight from x_new
+  if (e == hipSuccess && full > 0) {
+    e = quantize_blocks(xn + used * rowb, full, n_new, whole);
+    used += full;
+  }
+  if (e == hipSuccess && used < n_new)                           // the tail starts a new residual
+    e = kvq::launch_copy_tokens(xn + used * rowb, res, S, n_new - used, rowb, n_new, B, st);
+  return launched(e, "append");
 }
 
 kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_t* norms,
@@ -226,6 +293,7 @@ namespace {
 kvq::AttnArgs attn_args(const kvq_desc* d, int64_t q_heads) {
   kvq::AttnArgs a{};
   a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim; a.q_heads = q_heads;
+  a.stream_tokens = d->tokens_per_seq;
   a.block = d->block_tokens;
   a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
   a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
@@ -255,16 +323,21 @@ int64_t kvq_attention_workspace_bytes(const kvq_desc* d, int64_t q_heads) {
   return a.seqs * q_heads * kvq::attention_partials(a) * (d->head_dim + 2) * (int64_t)sizeof(float);
 }
 
-kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* k_codes,
-                                const uint16_t* k_norms, const uint16_t* k_scales, const int8_t* k_signs,
-                                const uint8_t* v_codes, const uint16_t* v_norms, const uint16_t* v_scales,
-                                const int8_t* v_signs, float* out, void* workspace, int64_t workspace_bytes,
-                                void* stream) {
-  kvq_status s = check_attention(d, q_heads);
-  if (s != KVQ_OK) return s;
-  if (d->seqs == 0) return ok();
+namespace {
+// shared by both attention entry points: tokens_cached tokens per sequence, the whole blocks in
+// the packed caches and the rest (fewer than block_tokens) in the residuals
+kvq_status attention_impl(const kvq_desc* d, int64_t tokens_cached, const uint16_t* q, int64_t q_heads,
+                          const uint8_t* k_codes, const uint16_t* k_norms, const uint16_t* k_scales,
+                          const int8_t* k_signs, const void* k_res, const uint8_t* v_codes, const uint16_t* v_norms,
+                          const uint16_t* v_scales, const int8_t* v_signs, const void* v_res, float* out,
+                          void* workspace, int64_t workspace_bytes, void* stream, const char* what) {
+  kvq_status s;
   if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out || !workspace)
     return fail(KVQ_ERR_NULL, "q, codes, scales, out and workspace are required");
+  const int64_t nres = tokens_cached % d->block_tokens;
+  if (nres > 0 && (!k_res || !v_res)) return fail(KVQ_ERR_NULL, "a partly filled block needs both residual buffers");
+  if ((k_res && !aligned(k_res, 2)) || (v_res && !aligned(v_res, 2)))
+    return fail(KVQ_ERR_ALIGN, "residuals must be 2-byte aligned");
   const bool nsep = nsep_mode(d->mode);
   if (nsep != (k_norms != nullptr) || nsep != (v_norms != nullptr))
     return fail(KVQ_ERR_NULL, nsep ? "NSEP modes need both norms buffers" : "norms must be NULL without NSEP");
@@ -282,10 +355,43 @@ kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_
   if ((s = device_ready()) != KVQ_OK) return s;
 
   kvq::AttnArgs a = attn_args(d, q_heads);
+  a.tokens = tokens_cached - nres;
   a.q = q; a.k_codes = k_codes; a.k_norms = k_norms; a.k_scales = k_scales; a.k_signs = k_signs;
   a.v_codes = v_codes; a.v_norms = v_norms; a.v_scales = v_scales; a.v_signs = v_signs;
   a.out = out; a.ws = static_cast<float*>(workspace);
-  return launched(kvq::launch_attention_decode(a, static_cast<hipStream_t>(stream)), "attention_decode");
+  a.k_res = k_res; a.v_res = v_res; a.nres = (int32_t)nres;
+  a.res_dtype = d->dtype == KVQ_F16 ? kvq::DT_F16 : kvq::DT_BF16;
+  return launched(kvq::launch_attention_decode(a, static_cast<hipStream_t>(stream)), what);
+}
+}  // namespace
+
+kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* k_codes,
+                                const uint16_t* k_norms, const uint16_t* k_scales, const int8_t* k_signs,
+                                const uint8_t* v_codes, const uint16_t* v_norms, const uint16_t* v_scales,
+                                const int8_t* v_signs, float* out, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  kvq_status s = check_attention(d, q_heads);
+  if (s != KVQ_OK) return s;
+  if (d->seqs == 0) return ok();
+  return attention_impl(d, d->tokens_per_seq, q, q_heads, k_codes, k_norms, k_scales, k_signs, nullptr, v_codes,
+                        v_norms, v_scales, v_signs, nullptr, out, workspace, workspace_bytes, stream, "attention_decode");
+}
+
+kvq_status kvq_attention_decode_stream(const kvq_desc* d, int64_t tokens_cached, const uint16_t* q, int64_t q_heads,
+                                       const uint8_t* k_codes, const uint16_t* k_norms, const uint16_t* k_scales,
+                                       const int8_t* k_signs, const void* k_residual, const uint8_t* v_codes,
+                                       const uint16_t* v_norms, const uint16_t* v_scales, const int8_t* v_signs,
+                                       const void* v_residual, float* out, void* workspace, int64_t workspace_bytes,
+                                       void* stream) {
+  kvq_status s = check_attention(d, q_heads);
+  if (s != KVQ_OK) return s;
+  if (tokens_cached < 1 || tokens_cached > d->tokens_per_seq)
+    return fail(KVQ_ERR_SHAPE, "tokens_cached %lld must be in [1, tokens_per_seq %lld]", (long long)tokens_cached,
+                (long long)d->tokens_per_seq);
+  if (d->seqs == 0) return ok();
+  return attention_impl(d, tokens_cached, q, q_heads, k_codes, k_norms, k_scales, k_signs, k_residual, v_codes,
+                        v_norms, v_scales, v_signs, v_residual, out, workspace, workspace_bytes, stream,
+                        "attention_decode_stream");
 }
 
 const char* kvq_status_str(kvq_status s) {
@@ -302,6 +408,6 @@ const char* kvq_status_str(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_version(void) { return 10100; }
+int32_t kvq_version(void) { return 10200; }
 
 }  // extern "C"

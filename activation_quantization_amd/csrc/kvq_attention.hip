@@ -15,10 +15,11 @@
 // stream; every wave walks its own blocks): per block, the scores of the G query heads come from
 // the matrix cores exactly as in the decode-score kernel (query times K scales as an fp16 hi/lo
 // A operand, codes as fp16 subnormals), an online softmax keeps the running max m and sum l per
-// head, and the value sum runs on the vector units with v_dot2_f32_f16: the block's V codes are
-// copied to LDS (global_load_lds), lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens
-// t = a (mod 4) and takes them two at a time (t, t + 4) as fp16 subnormal pairs against the pair
-// (p' = p norm_v) of each head.  The four waves' (m, l, partial sum) are merged in LDS and the
+// head, and the value sum runs on the vector units: the block's V codes are copied to LDS
+// (global_load_lds), lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens t = a (mod 4) and
+// takes them two at a time (t, t + 4) as 16-bit integer pairs against the pairs of 30-bit integer
+// weights (p' = p norm_v against the block's largest, in two 15-bit halves) of each head, in
+// exact integer dot products (v_dot2_u32_u16).  The four waves' (m, l, partial sum) are merged in LDS and the
 // workgroup writes one partial per query head to the caller's workspace.  Pass 2 merges the
 // partials of a head (log-sum-exp weights), rotates the result back and writes it.
 #include <type_traits>
@@ -64,7 +65,8 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   constexpr int R = 128, KS = 4, LB = 16, GM = 4, NGR = U / 16;
   __shared__ __attribute__((aligned(16))) float qr[GM * R];                 // rotated queries
   __shared__ __attribute__((aligned(16))) unsigned char vbuf[4][U * 64];    // per wave: one block of V codes
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[4][64][GM];        // per wave: p' pairs (t, t + 4) x head
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[4][64][GM];        // per wave: weight pairs (t, t + 4) x head, high
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf_lo[4][64][GM];     // ... and low 15 bits
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index, in a scalar register
   const int g = lane >> 4, j = lane & 15;
@@ -103,10 +105,11 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   const int64_t nunits = T / U;
   const int64_t u_begin = ci * ATT_UNITS_PER_GROUP;
   const int64_t u_end = u_begin + ATT_UNITS_PER_GROUP < nunits ? u_begin + ATT_UNITS_PER_GROUP : nunits;
-  const unsigned char* kstream = a.k_codes + sh * T * (R / 2);
-  const unsigned char* vstream = a.v_codes + sh * T * (R / 2);
-  const int64_t tstream = sh * T;
-  const int64_t nb = T / U;
+  const int64_t TS = a.stream_tokens;                                       // stream length (capacity)
+  const unsigned char* kstream = a.k_codes + sh * TS * (R / 2);
+  const unsigned char* vstream = a.v_codes + sh * TS * (R / 2);
+  const int64_t tstream = sh * TS;
+  const int64_t nb = TS / U;                                                // scale rows per stream
   const float zscale = 1.f / sqrtf((float)R);
 
   // per-lane softmax state of the row's heads 2 g, 2 g + 1 (replicated over the row), and the
@@ -120,6 +123,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   const int va = lane >> 4, vb = lane & 15;
   unsigned char* vw = &vbuf[w][0];
   uint16_t* pw = (uint16_t*)&pbuf[w][0][0];
+  uint16_t* pwl = (uint16_t*)&pbuf_lo[w][0][0];
 
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
@@ -204,9 +208,12 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       }
     }
 
-    // 3. online softmax for the row's two heads; p' = p * norm_v to LDS in the pair order
-    //    slot(8 k + r) = 8 k + 2 (r % 4) + r / 4, so tokens t and t + 4 sit side by side
-    float alpha_row[2], sp_row[2];
+    // 3. online softmax for the row's two heads.  The value weights p' = p * norm_v go to LDS as
+    //    integers W = rint(p' 2^30 / wmax) against the block's largest weight wmax of the head,
+    //    split into 15-bit halves (fp16 weights, 2^-12 relative, and 15-bit ones, 2^-16 wmax,
+    //    both move a long, nearly cancelling value sum past 2e-3 of the output's rms), in the pair
+    //    order slot(8 k + r) = 8 k + 2 (r % 4) + r / 4, so tokens t and t + 4 sit side by side
+    float alpha_row[2], wf_row[2], ws_row[2], wsl_row[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       float mx = -INFINITY;
@@ -215,39 +222,59 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       mx = row_max16f(mx);
       const float mnew = fmaxf(m_row[q2], mx);
       alpha_row[q2] = exp_f(m_row[q2] - mnew);            // 0 on the first block (m = -inf)
-      float ps = 0.f, psn = 0.f;                           // sums of p and of p' = p norm_v
+      float ps = 0.f, wmax = 0.f;                          // sum of p, largest p'
       const int h = 2 * g + q2;
 #pragma unroll
       for (int gr = 0; gr < NGR; ++gr) {
         const float p = exp_f(z[gr][q2] - mnew);
         ps += p;
+        z[gr][q2] = p * nvv[gr];                            // p', in place of the score
+        wmax = fmaxf(wmax, z[gr][q2]);
+      }
+      wmax = row_max16f(wmax);
+      const float wscale = wmax > 0.f ? 0x1p30f / wmax : 0.f;
+      float wsum = 0.f, wsuml = 0.f;                       // sums of the halves (integers < 2^22: exact)
+#pragma unroll
+      for (int gr = 0; gr < NGR; ++gr) {
+        const uint32_t wq = (uint32_t)__builtin_rintf(z[gr][q2] * wscale);   // <= 2^30
+        const uint32_t whi = wq >> 15, wlo = wq & 0x7fffu;
+        wsum += (float)whi;
+        wsuml += (float)wlo;
         const int t = 16 * gr + j;                          // pair (t & ~4) slot 4 (t / 8) + t % 4, half (t / 4) % 2
-        const _Float16 pn = (_Float16)(p * nvv[gr]);
-        psn += (float)pn;                                   // the rounded value the dot products use
-        if (h < GM) pw[2 * GM * (4 * (t >> 3) + (t & 3)) + 2 * h + ((t >> 2) & 1)] = __builtin_bit_cast(uint16_t, pn);
+        if (h < GM) {
+          const int slot = 2 * GM * (4 * (t >> 3) + (t & 3)) + 2 * h + ((t >> 2) & 1);
+          pw[slot] = (uint16_t)whi;
+          pwl[slot] = (uint16_t)wlo;
+        }
       }
       ps = row_sum16f(ps);
-      sp_row[q2] = row_sum16f(psn);
+      ws_row[q2] = row_sum16f(wsum);
+      wsl_row[q2] = row_sum16f(wsuml);
+      wf_row[q2] = wmax * 0x1p-30f;
       l_row[q2] = l_row[q2] * alpha_row[q2] + ps;
       m_row[q2] = mnew;
     }
-    // the alphas of every head, to every lane (head h lives in row h / 2)
-    float alpha[GM], spn[GM];
+    // alpha, weight unit and weight sum of every head, to every lane (head h lives in row h / 2)
+    float alpha[GM], wf[GM];
+    int wsb[GM], wsbl[GM];
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
-      alpha[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_row[h & 1]), 16 * (h >> 1)));
-      spn[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sp_row[h & 1]), 16 * (h >> 1)));
+      const int src = 16 * (h >> 1);
+      alpha[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_row[h & 1]), src));
+      wf[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wf_row[h & 1]), src));
+      wsb[h] = 2 * (int)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ws_row[h & 1]), src));
+      wsbl[h] = 2 * (int)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsl_row[h & 1]), src));
     }
 
     // 4. value sums of the block: tokens t = 8 i + va and t + 4, channels 8 vb ..
     __builtin_amdgcn_s_waitcnt(0x0070);                   // the V codes (and everything else) landed
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    float acc[GM][8];
+    uint32_t acc[GM][8], accl[GM][8];
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+      for (int c = 0; c < 8; ++c) acc[h][c] = accl[h][c] = 0u;
 #pragma unroll 4
     for (int i = 0; i < U / 8; ++i) {
       const int ta = 8 * i + va;
@@ -255,33 +282,43 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       const uint32_t x1 = *(const uint32_t*)(vw + (ta + 4) * 64 + 4 * vb) ^ 0x88888888u;
       const uint32_t e0 = x0 & 0x0F0F0F0Fu, o0 = (x0 >> 4) & 0x0F0F0F0Fu;
       const uint32_t e1 = x1 & 0x0F0F0F0Fu, o1 = (x1 >> 4) & 0x0F0F0F0Fu;
-      // channel 2 k: byte k of e0 (token ta) and of e1 (token ta + 4); 2 k + 1 from o0 / o1
-      f16x2 cp[8];
+      // channel 2 k: byte k of e0 (token ta) and of e1 (token ta + 4); 2 k + 1 from o0 / o1, as
+      // 16-bit pairs of c + 8 (exact integer products and sums: the +8 is taken out per block)
+      u16x2 cp[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + k) << 16) | (uint32_t)k;   // (b_k of src1) | (b_k of src0) << 16
-        cp[2 * k] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e1, e0, sel));
-        cp[2 * k + 1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(o1, o0, sel));
+        cp[2 * k] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(e1, e0, sel));
+        cp[2 * k + 1] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(o1, o0, sel));
       }
-      // p' pairs (ta, ta + 4) of the four heads in one 16-byte read
+      // weight pairs (ta, ta + 4) of the four heads in one 16-byte read per half
       const u32x4 pq = *(const u32x4*)(pbuf[w][4 * i + va]);
+      const u32x4 pql = *(const u32x4*)(pbuf_lo[w][4 * i + va]);
       const uint32_t pp4[4] = {pq.x, pq.y, pq.z, pq.w};
+      const uint32_t pl4[4] = {pql.x, pql.y, pql.z, pql.w};
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h < G) {
-          const f16x2 pp = __builtin_bit_cast(f16x2, pp4[h]);
+          const u16x2 pp = __builtin_bit_cast(u16x2, pp4[h]);
+          const u16x2 pl = __builtin_bit_cast(u16x2, pl4[h]);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[h][c] = __builtin_amdgcn_fdot2(cp[c], pp, acc[h][c], false);
+          for (int c = 0; c < 8; ++c) {
+            acc[h][c] = __builtin_amdgcn_udot2(cp[c], pp, acc[h][c], false);
+            accl[h][c] = __builtin_amdgcn_udot2(cp[c], pl, accl[h][c], false);
+          }
         }
       }
     }
-    // o = o alpha + scale_v (.) (2^24 acc - 8 sum p'); the bias is split evenly over the four
-    // token classes a, whose partial sums are added up at the end
+    // o = o alpha + scale_v (.) wmax 2^-30 (sum W c); per half sum W (c + 8) - 8 sum W, the +8 bias
+    // split evenly over the four token classes a (2 sum W each, exact in integers: every term
+    // stays below 2^24), whose partial sums are added up at the end
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        o[h][c] = o[h][c] * alpha[h] + vs[c] * __builtin_fmaf(acc[h][c], 0x1p24f, -2.f * spn[h]);
+      for (int c = 0; c < 8; ++c) {
+        const float hi = (float)((int)acc[h][c] - wsb[h]), lo = (float)((int)accl[h][c] - wsbl[h]);
+        o[h][c] = o[h][c] * alpha[h] + vs[c] * (wf[h] * __builtin_fmaf(hi, 32768.f, lo));
+      }
     // every lane of the wave is done with this block's LDS before the next block's copy
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
@@ -341,13 +378,16 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   }
 }
 
-// Pass 2: one workgroup of R threads per (sequence, query head): merge the partials, rotate back.
+// Pass 2: one workgroup of R threads per (sequence, query head): merge the cached part's
+// partials, rotate their value sum back, then merge the residual tokens (if any), which are
+// attended at full precision in the original domain.
 __global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
   constexpr int R = 128;
   __shared__ float buf[R];
+  __shared__ float red[R];
   const int c = threadIdx.x;
   const int64_t shq = blockIdx.x;                              // s * q_heads + hq
-  const int64_t hq = shq % a.q_heads;
+  const int64_t s = shq / a.q_heads, hq = shq - s * a.q_heads;
   const int64_t kvh = hq / (a.q_heads / a.heads);
   const float* wp = a.ws + shq * NP * (R + 2);
   float M = -INFINITY;
@@ -361,9 +401,9 @@ __global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
     L += f * wp[p * (R + 2) + R + 1];
     O += f * wp[p * (R + 2) + c];
   }
-  buf[c] = L > 0.f ? O / L : 0.f;
+  // inverse rotation of the (unnormalized) value sum: sigma_v (1/sqrt n) H, blocks of n = 2^lg_had
+  buf[c] = O;
   __syncthreads();
-  // inverse rotation: sigma_v (1/sqrt n) H (blocks of n = 2^lg_had): butterflies (a, b) -> (a + b, a - b)
   for (int st = 0; st < a.lg_had; ++st) {
     const int half = 1 << st;
     const float x = buf[c], y = buf[c ^ half];
@@ -371,12 +411,55 @@ __global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
     buf[c] = (c & half) ? y - x : x + y;
     __syncthreads();
   }
-  float r = buf[c];
+  O = buf[c];
   if (a.lg_had) {
-    r *= a.inv_sqrt_n;
-    if (a.v_signs[kvh * R + c] < 0) r = -r;
+    O *= a.inv_sqrt_n;
+    if (a.v_signs[kvh * R + c] < 0) O = -O;
   }
-  a.out[shq * R + c] = r;
+  if (a.nres == 0) {                                           // uniform over the workgroup
+    a.out[shq * R + c] = L > 0.f ? O / L : 0.f;
+    return;
+  }
+
+  // residual tokens t < nres: scores q . k_t / sqrt(D) (thread t), their max and sum, and the
+  // value sum (thread c = channel)
+  const int r = a.nres;
+  const int64_t rrow = (int64_t)a.heads * R;                   // elements between residual tokens
+  const int64_t rbase = (s * a.block * a.heads + kvh) * R;     // token 0 of this sequence and head
+  auto res = [&](const void* base, int64_t i) -> float {
+    const uint32_t h = ((const uint16_t*)base)[i];
+    return a.res_dtype == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+  };
+  buf[c] = f16_to_f32(a.q[shq * R + c]);
+  __syncthreads();
+  float z = -INFINITY;
+  if (c < r) {
+    float acc = 0.f;
+    for (int d = 0; d < R; ++d) acc = __builtin_fmaf(buf[d], res(a.k_res, rbase + c * rrow + d), acc);
+    z = acc * (1.f / sqrtf((float)R));
+  }
+  red[c] = z;
+  __syncthreads();
+  for (int half = R / 2; half > 0; half >>= 1) {
+    if (c < half) red[c] = fmaxf(red[c], red[c + half]);
+    __syncthreads();
+  }
+  const float mr = red[0];
+  __syncthreads();
+  const float p = c < r ? exp_f(z - mr) : 0.f;
+  buf[c] = p;                                                  // the query is no longer needed
+  red[c] = p;
+  __syncthreads();
+  for (int half = R / 2; half > 0; half >>= 1) {
+    if (c < half) red[c] += red[c + half];
+    __syncthreads();
+  }
+  const float lr = red[0];
+  float orr = 0.f;
+  for (int t = 0; t < r; ++t) orr = __builtin_fmaf(buf[t], res(a.v_res, rbase + t * rrow + c), orr);
+  const float mx = fmaxf(M, mr);
+  const float fq = M == -INFINITY ? 0.f : exp_f(M - mx), fr = exp_f(mr - mx);
+  a.out[shq * R + c] = (fq * O + fr * orr) / (fq * L + fr * lr);
 }
 
 }  // namespace
@@ -390,12 +473,14 @@ hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t st) {
   const int64_t nunits = a.tokens / a.block;
   const int64_t nchunks = (nunits + ATT_UNITS_PER_GROUP - 1) / ATT_UNITS_PER_GROUP;
   const int64_t ntiles = a.seqs * a.heads * nchunks;
-  if (a.block == 64)
-    hipLaunchKernelGGL((attn_partial<64>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
-  else
-    hipLaunchKernelGGL((attn_partial<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (ntiles > 0) {                                            // no whole block cached: residual only
+    if (a.block == 64)
+      hipLaunchKernelGGL((attn_partial<64>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
+    else
+      hipLaunchKernelGGL((attn_partial<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(a.seqs * a.q_heads)), dim3(128), 0, st, a, nchunks);
   return hipGetLastError();
 }

@@ -22,6 +22,10 @@ struct QuantArgs {
   float scale_mul;          // 1 / (sqrt(n) Q): stored scale = max of the unnormalized |u| * scale_mul
   int32_t nsep;             // norm separation on/off
   int32_t dtype;            // DT_F16 / DT_BF16
+  // per-channel kernel only (the streaming append writes blocks into a larger cache):
+  int64_t in_seq_tokens;    // x rows (tokens) from one sequence to the next (= tokens for a plain call)
+  int64_t out_tokens;       // tokens per head-major output stream (= tokens for a plain call)
+  int64_t out_tok0;         // stream token of the first quantized token (a multiple of B; 0 for a plain call)
 };
 
 struct DequantArgs {
@@ -66,11 +70,17 @@ struct AttnArgs {
   const int8_t* v_signs;
   float* out;               // [seqs, q_heads, D]
   float* ws;                // per (sequence, query head, partial): R sums, max, normalizer
-  int64_t seqs, tokens, heads, dim, q_heads;
+  int64_t seqs, tokens, heads, dim, q_heads;   // tokens: cached whole-block tokens attended per sequence
+  int64_t stream_tokens;    // tokens per head-major cache stream (the capacity; >= tokens)
   int32_t block;
   int32_t lg_had;
   float inv_sqrt_n;
   int32_t nsep;
+  // full-precision residual after the cached tokens (streaming append): [seqs, block, heads, D]
+  const void* k_res;
+  const void* v_res;
+  int32_t nres;             // residual tokens per sequence (0: none)
+  int32_t res_dtype;        // DT_F16 / DT_BF16
 };
 
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
@@ -80,6 +90,9 @@ hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t stream);
+// k tokens of rowb bytes per sequence, token-major runs: src sequences src_seq tokens apart, dst dst_seq
+hipError_t launch_copy_tokens(const void* src, void* dst, int64_t seqs, int64_t k, int64_t rowb, int64_t src_seq,
+                              int64_t dst_seq, hipStream_t stream);
 int64_t attention_partials(const AttnArgs& a);   // partials per (sequence, query head)
 
 }  // namespace kvq

@@ -164,9 +164,10 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   const uint32_t nb = (uint32_t)(a.tokens / B);
   const uint32_t hs32 = tile / nb, blk = tile - hs32 * nb;              // hs = seq * heads + h
   const uint32_t seq = hs32 / (uint32_t)a.heads, h = hs32 - seq * (uint32_t)a.heads;
-  const int64_t row0 = (int64_t)seq * a.tokens + (int64_t)blk * B;   // x row of the tile's first token
+  const int64_t row0 = (int64_t)seq * a.in_seq_tokens + (int64_t)blk * B;   // x row of the tile's first token
   const int64_t hs = hs32;                                            // (sequence, head) output stream
-  const int64_t tok0 = hs * a.tokens + (int64_t)blk * B;              // head-major index of that token
+  const int64_t tok0 = hs * a.out_tokens + a.out_tok0 + (int64_t)blk * B;   // head-major index of that token
+  const int64_t sblk = hs * (a.out_tokens / B) + a.out_tok0 / B + blk;     // its scale row
 
   // 1. this wave's B / 4 rows into LDS (instruction k moves 1 KiB; the chunk that lane p fetches
   //    is XOR-swizzled with its row, so slot cc of row r holds chunk cc ^ (r % CPR) and the
@@ -323,7 +324,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
     iv[q] = m > 0.f ? a.q * __builtin_amdgcn_rcpf(m) : 0.f;
     if (q == j) s16 = f32_to_f16(m * a.scale_mul);
   }
-  if (j < LCH) a.scales[(hs * nb + blk) * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
+  if (j < LCH) a.scales[sblk * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
 
   // 6. codes and near-tie flags
   uint32_t pk[ST];

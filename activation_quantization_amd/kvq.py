@@ -42,6 +42,10 @@ _SIGNATURES = {
     "kvq_attention_workspace_bytes": (ctypes.c_int64, [ctypes.POINTER(KvqDesc), ctypes.c_int64]),
     "kvq_attention_decode": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, ctypes.c_int64, _P]),
+    "kvq_append": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
+    "kvq_attention_decode_stream": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, _P, ctypes.c_int64,
+                                                   _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_int64, _P]),
     "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (ctypes.c_int32, []),
@@ -220,6 +224,51 @@ def attention_decode(d: Desc, q: torch.Tensor, k_cache, v_cache, k_signs=None, v
                                     _ptr(vc), _ptr(vn), _ptr(vs), _ptr(v_signs), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "kvq_attention_decode")
+    return out
+
+
+def alloc_residual(d: Desc, device):
+    """The full-precision residual of a streamed cache: [seqs, block_tokens, heads, head_dim]."""
+    return torch.empty((d.seqs, d.block_tokens, d.heads, d.head_dim), dtype=d.dtype, device=device)
+
+
+def append(d: Desc, tokens_cached: int, x_new: torch.Tensor, residual: torch.Tensor, cache, signs=None,
+           stream=None) -> int:
+    """kvq_append: append x_new [seqs, n_new, heads, head_dim] to every sequence of the cache
+    (codes, norms, scales with d.tokens_per_seq the capacity) and its residual.  Returns the new
+    token count tokens_cached + n_new."""
+    codes, norms, scales = cache
+    _need_cuda(x_new, residual, signs, codes, norms, scales)
+    n_new = x_new.shape[1] if x_new.dim() == 4 else 0
+    st = lib().kvq_append(ctypes.byref(d.c()), tokens_cached, _ptr(x_new), n_new, _ptr(residual), _ptr(signs),
+                          _ptr(codes), _ptr(norms), _ptr(scales), _stream(stream))
+    _check(st, "kvq_append")
+    return tokens_cached + n_new
+
+
+def attention_decode_stream(d: Desc, tokens_cached: int, q: torch.Tensor, k_cache, k_residual, v_cache, v_residual,
+                            k_signs=None, v_signs=None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_attention_decode_stream: attention over the first tokens_cached tokens of a streamed
+    cache (whole blocks packed, the rest in the residuals).  Same conventions as attention_decode."""
+    if q.dtype != torch.float16:
+        raise ValueError("q must be fp16")
+    q_heads = q.shape[1]
+    kc, kn, ks = k_cache
+    vc, vn, vs = v_cache
+    if out is None:
+        out = torch.empty((d.seqs, q_heads, d.head_dim), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = attention_workspace_bytes(d, q_heads)
+        if nbytes < 0:
+            _check(lib().kvq_validate(ctypes.byref(d.c())) or ERR_UNSUPPORTED, "kvq_attention_workspace_bytes")
+        workspace = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=q.device)
+    _need_cuda(q, kc, kn, ks, vc, vn, vs, k_signs, v_signs, k_residual, v_residual, out, workspace)
+    st = lib().kvq_attention_decode_stream(ctypes.byref(d.c()), tokens_cached, _ptr(q), q_heads, _ptr(kc), _ptr(kn),
+                                           _ptr(ks), _ptr(k_signs), _ptr(k_residual), _ptr(vc), _ptr(vn), _ptr(vs),
+                                           _ptr(v_signs), _ptr(v_residual), _ptr(out), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "kvq_attention_decode_stream")
     return out
 
 

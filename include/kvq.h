@@ -157,13 +157,52 @@ kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_
                                 const uint16_t* v_scales, const int8_t* v_signs, float* out, void* workspace,
                                 int64_t workspace_bytes, void* stream);
 
+/*
+ * Streaming append with a full-precision residual (NSNQuant summary, "implementation details": the
+ * KV cache is a quantized part plus a full-precision residual; when the residual is full it is
+ * quantized and moved into the quantized part).  Per-channel modes only: a per-channel scale needs
+ * a whole block of block_tokens tokens, so the last tokens_cached mod B tokens of a sequence wait
+ * at full precision (per-token codes need no residual: kvq_quantize on the new tokens appends them).
+ *   d: the cache.  tokens_per_seq is its capacity C (a multiple of block_tokens); codes, norms and
+ *      scales are head-major streams of C tokens, laid out exactly as kvq_quantize writes them.
+ *   tokens_cached: tokens already appended to every sequence (the caller keeps count; the cache
+ *      holds the first floor(tokens_cached / B) B tokens, the residual the rest in its first slots).
+ *   x_new: [seqs, n_new, heads, head_dim] in d->dtype, the tokens to append to every sequence.
+ *   residual: [seqs, block_tokens, heads, head_dim] in d->dtype, read and written.
+ *   signs: as for kvq_quantize.
+ * Afterwards every sequence holds tokens_cached + n_new tokens (must be <= C): each block that
+ * filled has been quantized into the cache exactly as kvq_quantize quantizes it, and the tokens
+ * after the last whole block sit in residual slots 0 .. (tokens_cached + n_new) mod B - 1.
+ * Enqueues up to four launches (residual top-up, its quantization, whole blocks straight from
+ * x_new, the new residual); allocates nothing.  x_new, residual, codes, signs 16-byte aligned.
+ */
+kvq_status kvq_append(const kvq_desc* d, int64_t tokens_cached, const void* x_new, int64_t n_new, void* residual,
+                      const int8_t* signs, uint8_t* codes, uint16_t* norms, uint16_t* scales, void* stream);
+
+/*
+ * Fused decode attention over a streamed cache: kvq_attention_decode over the first tokens_cached
+ * tokens of every sequence, where the whole blocks come from the packed caches (capacity
+ * d->tokens_per_seq) and the last tokens_cached mod B tokens from the full-precision residuals that
+ * kvq_append maintains (k_residual, v_residual: [seqs, block_tokens, heads, head_dim] in d->dtype,
+ * 2-byte aligned; they may be NULL when tokens_cached is a multiple of B).  One softmax spans both
+ * parts (NSNQuant summary, "implementation details").  1 <= tokens_cached <= tokens_per_seq; the
+ * workspace is sized by kvq_attention_workspace_bytes(d, q_heads), as for kvq_attention_decode.
+ */
+kvq_status kvq_attention_decode_stream(const kvq_desc* d, int64_t tokens_cached, const uint16_t* q, int64_t q_heads,
+                                       const uint8_t* k_codes, const uint16_t* k_norms, const uint16_t* k_scales,
+                                       const int8_t* k_signs, const void* k_residual, const uint8_t* v_codes,
+                                       const uint16_t* v_norms, const uint16_t* v_scales, const int8_t* v_signs,
+                                       const void* v_residual, float* out, void* workspace, int64_t workspace_bytes,
+                                       void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_str(kvq_status s);
 
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* kvq_last_error(void);
 
-/* ABI version: 10000 * major + 100 * minor + patch (1.1: fused decode attention). */
+/* ABI version: 10000 * major + 100 * minor + patch (1.1: fused decode attention; 1.2: streaming
+ * append and attention over a streamed cache). */
 int32_t kvq_version(void);
 
 #ifdef __cplusplus

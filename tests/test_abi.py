@@ -152,3 +152,46 @@ def test_attention_validation_before_any_device_call():
     assert _att(d, vs=FAKE + 2) == kvq.ERR_ALIGN          # scales are read as 16-byte vectors
     assert _att(d, out=FAKE + 2) == kvq.ERR_ALIGN
     assert _att(d, ws_bytes=100) == kvq.ERR_SHAPE
+
+
+def _app(d, tokens_cached=0, n_new=8, **ptr):
+    p = dict(x=FAKE, res=FAKE, sg=FAKE, c=FAKE, n=FAKE, s=FAKE)
+    p.update(ptr)
+    return kvq.lib().kvq_append(ctypes.byref(d.c()), tokens_cached, p["x"], n_new, p["res"], p["sg"], p["c"], p["n"],
+                                p["s"], None)
+
+
+def test_append_validation_before_any_device_call():
+    d = kvq.Desc(**GOOD)                                  # capacity 256 tokens, B = 128, NSEP + Hadamard
+    assert _app(kvq.Desc(**{**GOOD, "mode": "nsep", "block_tokens": 0})) == kvq.ERR_UNSUPPORTED   # per-token codes
+    assert _app(d, tokens_cached=250, n_new=7) == kvq.ERR_SHAPE          # past the capacity
+    assert _app(d, tokens_cached=-1) == kvq.ERR_SHAPE
+    assert _app(d, n_new=-1) == kvq.ERR_SHAPE
+    assert _app(d, tokens_cached=250, n_new=6, res=None) == kvq.ERR_NULL  # exactly full passes the size check
+    assert _app(d, n_new=0) == kvq.OK                                    # nothing to append
+    assert _app(d, res=None) == kvq.ERR_NULL
+    assert _app(d, n=None) == kvq.ERR_NULL                               # NSEP needs norms
+    assert _app(d, sg=None) == kvq.ERR_NULL                              # Hadamard needs signs
+    assert _app(d, res=FAKE + 8) == kvq.ERR_ALIGN
+    assert _app(d, x=FAKE + 2) == kvq.ERR_ALIGN
+
+
+def _atts(d, tokens_cached, q_heads=16, ws_bytes=1 << 30, **ptr):
+    p = dict(q=FAKE, kc=FAKE, kn=FAKE, ks=FAKE, ksg=FAKE, kr=FAKE, vc=FAKE, vn=FAKE, vs=FAKE, vsg=FAKE, vr=FAKE,
+             out=FAKE, ws=FAKE)
+    p.update(ptr)
+    return kvq.lib().kvq_attention_decode_stream(ctypes.byref(d.c()), tokens_cached, p["q"], q_heads, p["kc"], p["kn"],
+                                                 p["ks"], p["ksg"], p["kr"], p["vc"], p["vn"], p["vs"], p["vsg"],
+                                                 p["vr"], p["out"], p["ws"], ws_bytes, None)
+
+
+def test_stream_attention_validation_before_any_device_call():
+    d = kvq.Desc(**GOOD)
+    assert _atts(d, 0) == kvq.ERR_SHAPE                                  # nothing cached
+    assert _atts(d, 257) == kvq.ERR_SHAPE                                # past the capacity
+    assert _atts(d, 130, kr=None) == kvq.ERR_NULL                        # 2 tokens wait in the residual
+    assert _atts(d, 130, vr=FAKE + 1) == kvq.ERR_ALIGN
+    # whole blocks only: no residual needed (validation goes on to the workspace size)
+    assert _atts(d, 128, kr=None, vr=None, ws_bytes=100) == kvq.ERR_SHAPE
+    assert _atts(d, 130, kr=None, ws_bytes=100) == kvq.ERR_NULL
+    assert _atts(kvq.Desc(**{**GOOD, "mode": "naive", "block_tokens": 0}), 10) == kvq.ERR_UNSUPPORTED
