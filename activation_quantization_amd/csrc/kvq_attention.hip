@@ -65,8 +65,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   constexpr int R = 128, KS = 4, LB = 16, GM = 4, NGR = U / 16;
   __shared__ __attribute__((aligned(16))) float qr[GM * R];                 // rotated queries
   __shared__ __attribute__((aligned(16))) unsigned char vbuf[4][U * 64];    // per wave: one block of V codes
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[4][64][GM];        // per wave: weight pairs (t, t + 4) x head, high
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf_lo[4][64][GM];     // ... and low 15 bits
+  __shared__ __attribute__((aligned(16))) unsigned char wbuf[4][U / 64][16][64];   // per wave: MFMA A operand (weight planes)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index, in a scalar register
   const int g = lane >> 4, j = lane & 15;
@@ -113,17 +112,14 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   const float zscale = 1.f / sqrtf((float)R);
 
   // per-lane softmax state of the row's heads 2 g, 2 g + 1 (replicated over the row), and the
-  // value sums: lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens t = a (mod 4)
+  // value sums: lane 16 g + b owns channels 8 b .. 8 b + 7 of head g
   float m_row[2] = {-INFINITY, -INFINITY}, l_row[2] = {0.f, 0.f};
-  float o[GM][8];
+  float o[8];
 #pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
-  const int va = lane >> 4, vb = lane & 15;
+  for (int c = 0; c < 8; ++c) o[c] = 0.f;
+  const int vb = lane & 15;
   unsigned char* vw = &vbuf[w][0];
-  uint16_t* pw = (uint16_t*)&pbuf[w][0][0];
-  uint16_t* pwl = (uint16_t*)&pbuf_lo[w][0][0];
+  unsigned char* ww = &wbuf[w][0][0][0];
 
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
@@ -208,12 +204,13 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       }
     }
 
-    // 3. online softmax for the row's two heads.  The value weights p' = p * norm_v go to LDS as
-    //    integers W = rint(p' 2^30 / wmax) against the block's largest weight wmax of the head,
-    //    split into 15-bit halves (fp16 weights, 2^-12 relative, and 15-bit ones, 2^-16 wmax,
-    //    both move a long, nearly cancelling value sum past 2e-3 of the output's rms), in the pair
-    //    order slot(8 k + r) = 8 k + 2 (r % 4) + r / 4, so tokens t and t + 4 sit side by side
-    float alpha_row[2], wf_row[2], ws_row[2], wsl_row[2];
+    // 3. online softmax for the row's two heads.  The value weights p' = p * norm_v become
+    //    28-bit integers W = rint(p' (2^28 - 1) / wmax) against the block's largest weight wmax of
+    //    the head (fp16 weights, 2^-12 relative, move a long, nearly cancelling value sum past 2e-3
+    //    of the output's rms), stored as four 7-bit planes: row 4 h + b of the value MFMA's A
+    //    operand.  Token t sits at K position (lane group t % 4, byte 4 ((t / 4) % 4) + (t / 16) % 4)
+    //    of K step t / 64, so this lane's four tokens of a K step fill one 32-bit word per plane.
+    float alpha_row[2], wf_row[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       float mx = -INFINITY;
@@ -232,117 +229,99 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
         wmax = fmaxf(wmax, z[gr][q2]);
       }
       wmax = row_max16f(wmax);
-      const float wscale = wmax > 0.f ? 0x1p30f / wmax : 0.f;
-      float wsum = 0.f, wsuml = 0.f;                       // sums of the halves (integers < 2^22: exact)
+      const float wscale = wmax > 0.f ? 0x1p28f / wmax : 0.f;
+      if (h < GM) {
 #pragma unroll
-      for (int gr = 0; gr < NGR; ++gr) {
-        const uint32_t wq = (uint32_t)__builtin_rintf(z[gr][q2] * wscale);   // <= 2^30
-        const uint32_t whi = wq >> 15, wlo = wq & 0x7fffu;
-        wsum += (float)whi;
-        wsuml += (float)wlo;
-        const int t = 16 * gr + j;                          // pair (t & ~4) slot 4 (t / 8) + t % 4, half (t / 4) % 2
-        if (h < GM) {
-          const int slot = 2 * GM * (4 * (t >> 3) + (t & 3)) + 2 * h + ((t >> 2) & 1);
-          pw[slot] = (uint16_t)whi;
-          pwl[slot] = (uint16_t)wlo;
+        for (int ks = 0; ks < NGR / 4; ++ks) {
+          uint32_t pk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float wv = __builtin_rintf(z[4 * ks + r][q2] * wscale);
+            const uint32_t wq = wv < 268435455.f ? (uint32_t)wv : 268435455u;        // <= 2^28 - 1
+#pragma unroll
+            for (int b = 0; b < 4; ++b) pk[b] |= ((wq >> (7 * b)) & 127u) << (8 * r);
+          }
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            *(uint32_t*)(ww + ((ks * 16 + 4 * h + b) * 64 + 16 * (j & 3) + 4 * (j >> 2))) = pk[b];
         }
       }
       ps = row_sum16f(ps);
-      ws_row[q2] = row_sum16f(wsum);
-      wsl_row[q2] = row_sum16f(wsuml);
-      wf_row[q2] = wmax * 0x1p-30f;
+      wf_row[q2] = wmax * 0x1p-28f;
       l_row[q2] = l_row[q2] * alpha_row[q2] + ps;
       m_row[q2] = mnew;
     }
-    // alpha, weight unit and weight sum of every head, to every lane (head h lives in row h / 2)
-    float alpha[GM], wf[GM];
-    int wsb[GM], wsbl[GM];
+    // alpha and weight unit of this lane's head g (head h lives in row h / 2)
+    float alpha_g = 0.f, wf_g = 0.f;
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       const int src = 16 * (h >> 1);
-      alpha[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_row[h & 1]), src));
-      wf[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wf_row[h & 1]), src));
-      wsb[h] = 2 * (int)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ws_row[h & 1]), src));
-      wsbl[h] = 2 * (int)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsl_row[h & 1]), src));
+      const float ah = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_row[h & 1]), src));
+      const float fh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wf_row[h & 1]), src));
+      if (g == h) {
+        alpha_g = ah;
+        wf_g = fh;
+      }
     }
 
-    // 4. value sums of the block: tokens t = 8 i + va and t + 4, channels 8 vb ..
+    // 4. value sums of the block on the matrix cores (v_mfma_i32_16x16x64_i8, exact integers):
+    //    D[4 h + b][j] of group m = sum_t W_b(t) (c_t + 8), column j = channel 8 j + m.  Lane
+    //    (kg, j) reads word j (channels 8 j .. 8 j + 7) of its 16 tokens of the K step and takes
+    //    nibble m of each as a byte; a ninth product with B = 8 gives the bias 8 sum_t W_b(t).
     __builtin_amdgcn_s_waitcnt(0x0070);                   // the V codes (and everything else) landed
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    uint32_t acc[GM][8], accl[GM][8];
+    i32x4 acc[9];
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
+    for (int m = 0; m < 9; ++m) acc[m] = i32x4{0, 0, 0, 0};
+    const int kg = lane >> 4;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] = accl[h][c] = 0u;
-#pragma unroll 4
-    for (int i = 0; i < U / 8; ++i) {
-      const int ta = 8 * i + va;
-      const uint32_t x0 = *(const uint32_t*)(vw + ta * 64 + 4 * vb) ^ 0x88888888u;
-      const uint32_t x1 = *(const uint32_t*)(vw + (ta + 4) * 64 + 4 * vb) ^ 0x88888888u;
-      const uint32_t e0 = x0 & 0x0F0F0F0Fu, o0 = (x0 >> 4) & 0x0F0F0F0Fu;
-      const uint32_t e1 = x1 & 0x0F0F0F0Fu, o1 = (x1 >> 4) & 0x0F0F0F0Fu;
-      // channel 2 k: byte k of e0 (token ta) and of e1 (token ta + 4); 2 k + 1 from o0 / o1, as
-      // 16-bit pairs of c + 8 (exact integer products and sums: the +8 is taken out per block)
-      u16x2 cp[8];
+    for (int ks = 0; ks < NGR / 4; ++ks) {
+      uint32_t ev[16], od[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + k) << 16) | (uint32_t)k;   // (b_k of src1) | (b_k of src0) << 16
-        cp[2 * k] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(e1, e0, sel));
-        cp[2 * k + 1] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(o1, o0, sel));
+      for (int e = 0; e < 16; ++e) {
+        const int t = 64 * ks + kg + 4 * (e >> 2) + 16 * (e & 3);
+        const uint32_t x = *(const uint32_t*)(vw + t * 64 + 4 * vb) ^ 0x88888888u;   // nibbles c + 8
+        ev[e] = x & 0x0F0F0F0Fu;                                                        // channels 8 vb + 2 k
+        od[e] = (x >> 4) & 0x0F0F0F0Fu;                                                 // channels 8 vb + 2 k + 1
       }
-      // weight pairs (ta, ta + 4) of the four heads in one 16-byte read per half
-      const u32x4 pq = *(const u32x4*)(pbuf[w][4 * i + va]);
-      const u32x4 pql = *(const u32x4*)(pbuf_lo[w][4 * i + va]);
-      const uint32_t pp4[4] = {pq.x, pq.y, pq.z, pq.w};
-      const uint32_t pl4[4] = {pql.x, pql.y, pql.z, pql.w};
+      const i32x4 av = *(const i32x4*)(ww + ((ks * 16 + (lane & 15)) * 64 + 16 * kg));
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          const u16x2 pp = __builtin_bit_cast(u16x2, pp4[h]);
-          const u16x2 pl = __builtin_bit_cast(u16x2, pl4[h]);
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t* src = (m & 1) ? od : ev;
+        const int k = m >> 1;
+        const uint32_t lo_sel = 0x0C0C0400u | (uint32_t)k | ((uint32_t)k << 8);        // bytes 0, 1: byte k of src1, src0
+        const uint32_t hi_sel = 0x04000C0Cu | ((uint32_t)k << 16) | ((uint32_t)k << 24); // bytes 2, 3
+        int bq[4];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            acc[h][c] = __builtin_amdgcn_udot2(cp[c], pp, acc[h][c], false);
-            accl[h][c] = __builtin_amdgcn_udot2(cp[c], pl, accl[h][c], false);
-          }
-        }
+        for (int q = 0; q < 4; ++q)
+          bq[q] = (int)(__builtin_amdgcn_perm(src[4 * q + 1], src[4 * q], lo_sel) |
+                        __builtin_amdgcn_perm(src[4 * q + 3], src[4 * q + 2], hi_sel));
+        acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{bq[0], bq[1], bq[2], bq[3]}, acc[m], 0, 0, 0);
       }
+      acc[8] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{0x08080808, 0x08080808, 0x08080808, 0x08080808},
+                                                     acc[8], 0, 0, 0);
     }
-    // o = o alpha + scale_v (.) wmax 2^-30 (sum W c); per half sum W (c + 8) - 8 sum W, the +8 bias
-    // split evenly over the four token classes a (2 sum W each, exact in integers: every term
-    // stays below 2^24), whose partial sums are added up at the end
+    // lane (g, j): rows 4 g + b = the planes of head g; sum_t W (c_t) = sum_b 128^b (D_b - bias_b),
+    // every difference below 2^24 (exact in fp32)
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float hi = (float)((int)acc[h][c] - wsb[h]), lo = (float)((int)accl[h][c] - wsbl[h]);
-        o[h][c] = o[h][c] * alpha[h] + vs[c] * (wf[h] * __builtin_fmaf(hi, 32768.f, lo));
-      }
+    for (int m = 0; m < 8; ++m) {
+      float v = (float)(acc[m][3] - acc[8][3]);
+      v = __builtin_fmaf(v, 128.f, (float)(acc[m][2] - acc[8][2]));
+      v = __builtin_fmaf(v, 128.f, (float)(acc[m][1] - acc[8][1]));
+      v = __builtin_fmaf(v, 128.f, (float)(acc[m][0] - acc[8][0]));
+      o[m] = o[m] * alpha_g + vs[m] * (wf_g * v);
+    }
     // every lane of the wave is done with this block's LDS before the next block's copy
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
   }
 
-  // 5. the wave's partial: sum the four token classes a (lanes 0..15 then hold it)
-#pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v = o[h][c];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      o[h][c] = v;
-    }
   // 6. merge the four waves' partials through LDS (each wave's V buffer is free now), then one
   // partial (max, sum, vector) per head for the workgroup
   float* mw = (float*)&vbuf[w][0];                         // [GM][R] sums, [GM] maxima, [GM] sums of p
-  if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) mw[h * R + 8 * lane + c] = o[h][c];
-  }
+  for (int c = 0; c < 8; ++c) mw[g * R + 8 * vb + c] = o[c];
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
     const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_row[h & 1]), 16 * (h >> 1)));
