@@ -107,6 +107,64 @@ def config_bytes(w, bits_mode):
     return q, q
 
 
+def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, stream, dev, steps, warmup):
+    """The decode loop's streaming append and attention over the streamed cache.
+
+    Every sequence of the K and V caches starts at T - B cached tokens (whole blocks); one decode
+    step appends one new token per sequence to each cache, so a cycle of B steps fills the
+    full-precision residual and flushes it (the B-th append quantizes it into the cache).  Then
+    decode attention over T - 1 tokens: T - B from the packed caches and B - 1 from the residuals.
+    New tokens are seeded N(0, 1) fp16 (the append's cost does not depend on their values)."""
+    B, T, S = w.block_tokens, w.tokens, w.seqs
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    xk = torch.randn((S, B, w.heads, w.head_dim), generator=gen).half().to(dev)
+    xv = torch.randn((S, B, w.heads, w.head_dim), generator=gen).half().to(dev)
+    steps_k = [xk[:, i:i + 1].contiguous() for i in range(B)]
+    steps_v = [xv[:, i:i + 1].contiguous() for i in range(B)]
+    rk, rv = kvq.alloc_residual(d, dev), kvq.alloc_residual(d, dev)
+
+    def cycle():
+        n = T - B
+        for i in range(B):
+            kvq.append(d, n, steps_k[i], rk, k_cache, signs, stream=stream)
+            n = kvq.append(d, n, steps_v[i], rv, v_cache, signs, stream=stream)
+        return n
+
+    cycle()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    cycle()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cycle_us = e0.elapsed_time(e1) * 1e3
+    tok_bytes = S * w.heads * w.head_dim * 2                     # one new token per sequence, fp16
+    blk_bytes = S * B * w.heads * w.head_dim * 2                 # a full residual
+    packed = S * B * w.heads * (w.head_dim // 2 + 2) + S * w.heads * w.head_dim * 2
+    cycle_bytes = 2 * (B * 2 * tok_bytes + blk_bytes + packed)   # K and V: copies in/out, one flush
+    rows = {"append_decode_step": {"us_per_step": round(cycle_us / B, 2), "appends_per_step": 2,
+                                   "tokens_per_append": S, "cycle_steps": B, "cycle_us": round(cycle_us, 1),
+                                   "cycle_bytes": cycle_bytes,
+                                   "GB/s": round(cycle_bytes / (cycle_us * 1e-6) / 1e9, 1)}}
+    n = T - 1
+    for _ in range(warmup):
+        kvq.attention_decode_stream(d, n, q, k_cache, rk, v_cache, rv, signs, signs, out=att_out, workspace=ws,
+                                    stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        kvq.attention_decode_stream(d, n, q, k_cache, rk, v_cache, rv, signs, signs, out=att_out, workspace=ws,
+                                    stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nb = algorithmic_bytes(w, w.q_heads)["attention_decode"]
+    rows["attention_decode_stream"] = {"us": round(us, 2), "tokens_cached": n, "residual_tokens": B - 1,
+                                       "GB/s": round(nb / (us * 1e-6) / 1e9, 1),
+                                       "frac_hbm": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return rows
+
+
 def other_configs(torch, kvq, synth, dev, steps, warmup):
     """Quantize and dequantize of the other workloads, each iteration after a 512 MiB read that
     evicts L2 and the MALL (the events bracket the kernel only).  A read, not a write: a written
@@ -273,6 +331,9 @@ def main():
         gbs = b["attention_decode"] / (attn_us * 1e-6) / 1e9
         kernels["attention_decode"] = {"us": round(attn_us, 2), "bytes": b["attention_decode"], "GB/s": round(gbs, 1),
                                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "in_step": False}
+    if attn_us is not None and not args.only:
+        kernels.update(stream_decode(torch, kvq, d, w, q, kc, vcache, signs, att_out, ws, stream, dev,
+                                     args.steps, args.warmup))
     if args.only:
         print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
         return
