@@ -48,6 +48,7 @@ import dataclasses
 import numpy as np
 
 MODES = ("naive", "nsep", "pchan", "nsep_pchan")
+NSN_MODE = "nsn_pchan"        # NSN before the per-channel quantizer (its own entry points)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,7 +69,7 @@ class Spec:
 
     @property
     def per_channel(self) -> bool:
-        return self.mode in ("pchan", "nsep_pchan")
+        return self.mode in ("pchan", "nsep_pchan", "nsn_pchan")
 
 
 def qmax(bits: int) -> int:
@@ -238,6 +239,82 @@ def attention_decode(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, spec: 
     for hq in range(Hq):
         out[:, hq, :] = np.einsum("st,std->sd", p[:, hq, :], vh[:, :, hq // G, :])
     return out
+
+
+# ----------------------------------------------------------------------------- NSN variant
+@dataclasses.dataclass
+class NsnQuantized:
+    codes: np.ndarray        # int8 [N, heads, D]
+    packed: np.ndarray       # uint8 [N, heads, D/2]
+    v: np.ndarray            # float64 quotient before rounding
+    s1: np.ndarray           # float64 [N, heads]: first token scale, ||x|| / sqrt(D)
+    s2: np.ndarray           # float64 [N, heads]: second token scale, ||u1 - o|| / sqrt(D)
+    offset: np.ndarray       # float64 [seqs * T/B, heads, D]: the block's channel mean, original domain
+    scale: np.ndarray        # float64 [seqs * T/B, heads, D]: per-channel absmax / Q of u3
+    s1_16: np.ndarray
+    s2_16: np.ndarray
+    offset16: np.ndarray
+    scales16: np.ndarray
+
+
+def nsn_quantize(x: np.ndarray, spec: Spec, signs: np.ndarray | None = None) -> NsnQuantized:
+    """Normalize-Shift-Normalize before the per-channel scalar quantizer (NSNQuant summary,
+    "Normalize-Shift-Normalize (NSN)": token norms to sqrt(d), subtract the channel means, token
+    norms to sqrt(d) again, keeping s1, o, s2 to reconstruct; "Hadamard transform": combined with a
+    randomized Hadamard rotation).
+
+    Per (token, head): y = R x (C1), s1 = ||y|| / sqrt(D), u1 = y / s1.  Per (sequence, B-token
+    block, head): o = the mean of u1 over the block's tokens.  Per token: u2 = u1 - o,
+    s2 = ||u2|| / sqrt(D), u3 = u2 / s2.  Then per-channel absmax / Q of u3 over the block and
+    c = rne(fp32(u3 / scale)) as in quantize().  The rotation is orthonormal and linear, so it
+    commutes with both normalizations and with the mean; the stored offset is the mean in the
+    original domain, R^T o.  s1 = 0 or s2 = 0 give zero directions (and codes 0); s2 counts as 0
+    when ||u2|| < 2^-16 sqrt(D) (reading: a token equal to its block's mean up to round-off).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    N, Hh, D = x.shape
+    assert spec.mode == "nsn_pchan" and N == spec.seqs * spec.tokens
+    Q = qmax(spec.bits)
+    B = spec.block_tokens
+    nb = spec.tokens // B
+    y = rotate(x, signs, spec.hadamard) if spec.hadamard else x.copy()
+
+    def unit(v):                       # scale to norm sqrt(D); returns (direction, scale)
+        sc = np.sqrt(np.sum(v * v, axis=-1)) / np.sqrt(D)
+        safe = np.where(sc > 0.0, sc, 1.0)
+        return np.where(sc[..., None] > 0.0, v / safe[..., None], 0.0), sc
+
+    u1, s1 = unit(y)
+    o = u1.reshape(spec.seqs, nb, B, Hh, D).mean(axis=2)                                 # [S, nb, H, D]
+    u2 = u1 - np.repeat(o[:, :, None], B, axis=2).reshape(N, Hh, D)
+    # a token equal to its block's mean up to round-off (||u2|| under 2^-16 of ||u1|| = sqrt(D))
+    # has no second direction: s2 = 0, codes 0 (else round-off noise would fill the codes)
+    u2 = np.where((np.sqrt(np.sum(u2 * u2, axis=-1)) < 2.0 ** -16 * np.sqrt(D))[..., None], 0.0, u2)
+    u3, s2 = unit(u2)
+    amax = np.abs(u3).reshape(spec.seqs, nb, B, Hh, D).max(axis=2)
+    scale = (amax / Q).reshape(spec.seqs * nb, Hh, D)
+    scale_full = np.repeat(scale.reshape(spec.seqs, nb, 1, Hh, D), B, axis=2).reshape(N, Hh, D)
+    safe = np.where(scale_full > 0.0, scale_full, 1.0)
+    v = np.where(scale_full > 0.0, u3 / safe, 0.0)
+    c = np.clip(np.rint(v.astype(np.float32)), -Q, Q).astype(np.int8)
+    o = o.reshape(spec.seqs * nb, Hh, D)
+    offset = inverse_rotate(o, signs, spec.hadamard) if spec.hadamard else o
+    return NsnQuantized(codes=c, packed=pack_nibbles(c), v=v, s1=s1, s2=s2, offset=offset, scale=scale,
+                        s1_16=s1.astype(np.float16), s2_16=s2.astype(np.float16),
+                        offset16=offset.astype(np.float16), scales16=scale.astype(np.float16))
+
+
+def nsn_dequantize(packed: np.ndarray, s1_16, s2_16, offset16, scales16, spec: Spec,
+                   signs: np.ndarray | None = None) -> np.ndarray:
+    """x^ = s1 (s2 R^T (c * scale) + offset) in float64 from the stored fp16 byproducts (the
+    inverse of each NSN step, in reverse order)."""
+    c = unpack_nibbles(np.asarray(packed)).astype(np.float64)
+    u3 = c * expand_scales(scales16, spec)
+    back = inverse_rotate(u3, signs, spec.hadamard) if spec.hadamard else u3
+    off = expand_scales(offset16, spec)                 # the same per-block broadcast as the scales
+    s1 = np.asarray(s1_16).astype(np.float64)[..., None]
+    s2 = np.asarray(s2_16).astype(np.float64)[..., None]
+    return s1 * (s2 * back + off)
 
 
 # ----------------------------------------------------------------------------- streaming append
