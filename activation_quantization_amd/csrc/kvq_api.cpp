@@ -36,6 +36,8 @@ int ilog2(int64_t v) {
 }
 bool nsep_mode(int m) { return m == KVQ_NSEP || m == KVQ_NSEP_PCHAN; }
 bool pchan_mode(int m) { return m == KVQ_PCHAN || m == KVQ_NSEP_PCHAN; }
+bool nsn_mode(int m) { return m == KVQ_NSN_PCHAN; }
+bool blocked_mode(int m) { return pchan_mode(m) || nsn_mode(m); }   // per-channel scales over token blocks
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 kvq_status check_desc(const kvq_desc* d) {
@@ -49,7 +51,7 @@ kvq_status check_desc(const kvq_desc* d) {
   if (d->head_dim & 1) return fail(KVQ_ERR_SHAPE, "head_dim %lld is odd", (long long)d->head_dim);
   if (d->reserved != 0) return fail(KVQ_ERR_UNSUPPORTED, "reserved field must be 0");
   if (d->bits < 2 || d->bits > 4) return fail(KVQ_ERR_UNSUPPORTED, "bits %d not in {2, 3, 4}", d->bits);
-  if (d->mode < KVQ_NAIVE || d->mode > KVQ_NSEP_PCHAN) return fail(KVQ_ERR_UNSUPPORTED, "unknown mode %d", d->mode);
+  if (d->mode < KVQ_NAIVE || d->mode > KVQ_NSN_PCHAN) return fail(KVQ_ERR_UNSUPPORTED, "unknown mode %d", d->mode);
   if (d->dtype != KVQ_F16 && d->dtype != KVQ_BF16)
     return fail(KVQ_ERR_UNSUPPORTED, "input dtype %d must be KVQ_F16 or KVQ_BF16", d->dtype);
   const int64_t D = d->head_dim;
@@ -59,7 +61,7 @@ kvq_status check_desc(const kvq_desc* d) {
     if (d->hadamard < 16 || d->hadamard > 128)
       return fail(KVQ_ERR_UNSUPPORTED, "hadamard %d not in {16, 32, 64, 128}", d->hadamard);
   }
-  if (pchan_mode(d->mode)) {
+  if (blocked_mode(d->mode)) {
     if (D != 64 && D != 128) return fail(KVQ_ERR_UNSUPPORTED, "per-channel modes need head_dim 64 or 128 (got %lld)", (long long)D);
     if (d->block_tokens <= 0) return fail(KVQ_ERR_SHAPE, "block_tokens %d must be >= 1", d->block_tokens);
     if (d->block_tokens != 64 && d->block_tokens != 128 && d->block_tokens != 256)
@@ -77,7 +79,7 @@ kvq_status check_desc(const kvq_desc* d) {
   const int64_t rows = d->seqs * d->tokens_per_seq;
   if (rows > (int64_t(1) << 40) || d->heads > (int64_t(1) << 20))
     return fail(KVQ_ERR_UNSUPPORTED, "tensor too large");
-  const int64_t tiles = pchan_mode(d->mode) ? rows / d->block_tokens * d->heads
+  const int64_t tiles = blocked_mode(d->mode) ? rows / d->block_tokens * d->heads
                                             : (rows * d->heads * (D / (D >= 128 ? 128 : 64)) + 63) / 64;
   if (tiles >= (int64_t(1) << 31)) return fail(KVQ_ERR_UNSUPPORTED, "too many tiles (%lld)", (long long)tiles);
   return KVQ_OK;
@@ -117,13 +119,13 @@ int64_t kvq_codes_bytes(const kvq_desc* d) {
 
 int64_t kvq_norms_count(const kvq_desc* d) {
   if (check_desc(d) != KVQ_OK) return -1;
-  return nsep_mode(d->mode) ? d->seqs * d->tokens_per_seq * d->heads : 0;
+  return nsep_mode(d->mode) || nsn_mode(d->mode) ? d->seqs * d->tokens_per_seq * d->heads : 0;
 }
 
 int64_t kvq_scales_count(const kvq_desc* d) {
   if (check_desc(d) != KVQ_OK) return -1;
   const int64_t rows = d->seqs * d->tokens_per_seq;
-  return pchan_mode(d->mode) ? rows / d->block_tokens * d->heads * d->head_dim : rows * d->heads;
+  return blocked_mode(d->mode) ? rows / d->block_tokens * d->heads * d->head_dim : rows * d->heads;
 }
 
 namespace {
@@ -150,6 +152,7 @@ kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs, u
                         uint16_t* norms, uint16_t* scales, void* stream) {
   kvq_status s = check_desc(d);
   if (s != KVQ_OK) return s;
+  if (nsn_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "mode KVQ_NSN_PCHAN has its own entry points (the _nsn calls)");
   if (empty_work(d)) return ok();
   if (!x || !codes || !scales) return fail(KVQ_ERR_NULL, "x, codes and scales are required");
   if (nsep_mode(d->mode) != (norms != nullptr))
@@ -228,6 +231,7 @@ kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_
                           const uint16_t* scales, const int8_t* signs, void* y, int32_t y_dtype, void* stream) {
   kvq_status s = check_desc(d);
   if (s != KVQ_OK) return s;
+  if (nsn_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "mode KVQ_NSN_PCHAN has its own entry points (the _nsn calls)");
   if (y_dtype != KVQ_F16 && y_dtype != KVQ_BF16 && y_dtype != KVQ_F32)
     return fail(KVQ_ERR_UNSUPPORTED, "output dtype %d not in {F16, BF16, F32}", y_dtype);
   if (empty_work(d)) return ok();
@@ -261,6 +265,7 @@ kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_head
                             void* stream) {
   kvq_status s = check_desc(d);
   if (s != KVQ_OK) return s;
+  if (nsn_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "mode KVQ_NSN_PCHAN has its own entry points (the _nsn calls)");
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(KVQ_ERR_UNSUPPORTED, "decode score needs head_dim 64 or 128 (got %lld)", (long long)d->head_dim);
   if (q_heads <= 0 || q_heads % d->heads != 0)
@@ -287,6 +292,94 @@ kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_head
   a.nsep = nsep_mode(d->mode);
   a.per_channel = pchan_mode(d->mode);
   return launched(kvq::launch_score_decode(a, static_cast<hipStream_t>(stream)), "score_decode");
+}
+
+kvq_status kvq_quantize_nsn(const kvq_desc* d, const void* x, const int8_t* signs, uint8_t* codes, uint16_t* s1,
+                            uint16_t* s2, uint16_t* offsets, uint16_t* scales, void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (!nsn_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "the _nsn calls need mode KVQ_NSN_PCHAN");
+  if (empty_work(d)) return ok();
+  if (!x || !codes || !s1 || !s2 || !offsets || !scales)
+    return fail(KVQ_ERR_NULL, "x, codes, s1, s2, offsets and scales are required");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(offsets, 16) || (signs && !aligned(signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "x, codes, offsets and signs must be 16-byte aligned");
+  if (!aligned(s1, 2) || !aligned(s2, 2) || !aligned(scales, 2))
+    return fail(KVQ_ERR_ALIGN, "s1, s2 and scales must be 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+  kvq::NsnArgs a{};
+  a.x = x; a.signs = signs; a.codes = codes; a.s1 = s1; a.s2 = s2; a.offsets = offsets; a.scales = scales;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.q = (1 << (d->bits - 1)) - 1;
+  a.dtype = d->dtype == KVQ_F16 ? kvq::DT_F16 : kvq::DT_BF16;
+  return launched(kvq::launch_quantize_nsn(a, static_cast<hipStream_t>(stream)), "quantize_nsn");
+}
+
+kvq_status kvq_dequantize_nsn(const kvq_desc* d, const uint8_t* codes, const uint16_t* s1, const uint16_t* s2,
+                              const uint16_t* offsets, const uint16_t* scales, const int8_t* signs, void* y,
+                              int32_t y_dtype, void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (!nsn_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "the _nsn calls need mode KVQ_NSN_PCHAN");
+  if (y_dtype != KVQ_F16 && y_dtype != KVQ_BF16 && y_dtype != KVQ_F32)
+    return fail(KVQ_ERR_UNSUPPORTED, "output dtype %d not in {F16, BF16, F32}", y_dtype);
+  if (empty_work(d)) return ok();
+  if (!codes || !s1 || !s2 || !offsets || !scales || !y)
+    return fail(KVQ_ERR_NULL, "codes, s1, s2, offsets, scales and y are required");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(y, 16) || !aligned(codes, 16) || !aligned(offsets, 16) || (signs && !aligned(signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "y, codes, offsets and signs must be 16-byte aligned");
+  if (!aligned(s1, 2) || !aligned(s2, 2) || !aligned(scales, 2))
+    return fail(KVQ_ERR_ALIGN, "s1, s2 and scales must be 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+  kvq::DequantArgs a{};
+  a.codes = codes; a.norms = s1; a.s2 = s2; a.offsets = offsets; a.scales = scales; a.signs = signs; a.y = y;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.nsep = 1;
+  a.per_channel = 1;
+  a.out_dtype = y_dtype == KVQ_F16 ? kvq::DT_F16 : y_dtype == KVQ_BF16 ? kvq::DT_BF16 : kvq::DT_F32;
+  return launched(kvq::launch_dequantize_nsn(a, static_cast<hipStream_t>(stream)), "dequantize_nsn");
+}
+
+kvq_status kvq_score_decode_nsn(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* codes,
+                                const uint16_t* s1, const uint16_t* s2, const uint16_t* offsets,
+                                const uint16_t* scales, const int8_t* signs, float* scores, void* stream) {
+  kvq_status s = check_desc(d);
+  if (s != KVQ_OK) return s;
+  if (!nsn_mode(d->mode)) return fail(KVQ_ERR_UNSUPPORTED, "the _nsn calls need mode KVQ_NSN_PCHAN");
+  if (q_heads <= 0 || q_heads % d->heads != 0)
+    return fail(KVQ_ERR_SHAPE, "q_heads %lld must be a positive multiple of heads %lld", (long long)q_heads,
+                (long long)d->heads);
+  if (q_heads / d->heads > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (empty_work(d)) return ok();
+  if (!q || !codes || !s1 || !s2 || !offsets || !scales || !scores)
+    return fail(KVQ_ERR_NULL, "q, codes, s1, s2, offsets, scales and scores are required");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(codes, 16)) return fail(KVQ_ERR_ALIGN, "codes must be 16-byte aligned");
+  if (!aligned(q, 2) || !aligned(s1, 2) || !aligned(s2, 2) || !aligned(offsets, 2) || !aligned(scales, 2) ||
+      !aligned(scores, 4))
+    return fail(KVQ_ERR_ALIGN, "q, s1, s2, offsets, scales must be 2-byte and scores 4-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+  kvq::ScoreArgs a{};
+  a.q = q; a.codes = codes; a.norms = s1; a.s2 = s2; a.offsets = offsets; a.scales = scales; a.signs = signs;
+  a.scores = scores;
+  a.seqs = d->seqs; a.tokens = d->tokens_per_seq; a.heads = d->heads; a.dim = d->head_dim; a.q_heads = q_heads;
+  a.block = d->block_tokens;
+  a.lg_had = d->hadamard ? ilog2(d->hadamard) : 0;
+  a.inv_sqrt_n = d->hadamard ? float(1.0 / std::sqrt(double(d->hadamard))) : 1.f;
+  a.nsep = 1;
+  a.per_channel = 1;
+  a.nsn = 1;
+  return launched(kvq::launch_score_decode(a, static_cast<hipStream_t>(stream)), "score_decode_nsn");
 }
 
 namespace {
@@ -408,6 +501,6 @@ const char* kvq_status_str(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_version(void) { return 10200; }
+int32_t kvq_version(void) { return 10300; }
 
 }  // extern "C"

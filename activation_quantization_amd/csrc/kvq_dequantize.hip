@@ -73,20 +73,25 @@ __device__ __forceinline__ void stage_row(unsigned char* stage, int row, const f
 // tokens, so the 16 lanes of a row store whole output rows.  The products scale * code are
 // exact in fp32 (11 x 4 bits).
 
-template <int R, bool PT>
+template <int R, bool PT, bool NS>
 struct DqPre {
   static constexpr int KS = R / 32;
   uint32_t wd[KS];          // packed codes of token j, channels (R/4) g ..
   uint32_t nw[2];           // fp16 norms of tokens 4 g + r, r = 0..3
   u32x4 sc[PT ? 1 : KS];    // per-channel: fp16 scales of channels (R/4) g + 8 K + [0, 8);
                             // per-token: sc[0].x, .y = fp16 scales of tokens 4 g + r
+  uint32_t n2[NS ? 2 : 1];  // NSN: fp16 second scales s2 of tokens 4 g + r
+  uint32_t of[NS ? R / 32 : 1];   // NSN: fp16 offsets of channels L j .. L j + L - 1 (pairs)
 };
 
 //
 // Per-token scales (PT) use the same contraction with diag(scale) = I; the token's scale joins
 // its norm in the row factor.  A vector of D = 2^lgL R channels is 2^lgL row segments, each
 // walked as a stream of its own (the rotation is block-diagonal with blocks of at most R).
-template <int ODT, int R, int LG, bool PT, int WPE = 3>
+//
+// NSN (NS): x^ = s1 (s2 R^T (c scale) + offset): the row factor is s1 s2 and s1 times the block's
+// offset (original domain) is added per output channel.
+template <int ODT, int R, int LG, bool PT, bool NS = false, int WPE = 3>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
   constexpr int L = R / 16;                 // I-blocks: output channels per lane and token
@@ -143,7 +148,7 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
     const unsigned char* cstream = a.codes + hs * a.tokens * cstride + seg * (R / 2);
     const uint16_t* nstream = a.nsep ? a.norms + hs * a.tokens : nullptr;
     const uint16_t* sstream = PT ? a.scales + hs * a.tokens : a.scales + hs * nb * R;
-    auto load = [&](int i, DqPre<R, PT>& p) {
+    auto load = [&](int i, DqPre<R, PT, NS>& p) {
       const uint32_t t = (uint32_t)((ch0 + i) * 64) + 16 * w;   // stream token of the wave's first row
       const unsigned char* cp = cstream + (size_t)(t + j) * cstride + LB * g;
       if constexpr (KS == 4) {
@@ -161,6 +166,24 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
         } else {
           p.nw[0] = np[0] | ((uint32_t)np[1] << 16);
           p.nw[1] = np[2] | ((uint32_t)np[3] << 16);
+        }
+      }
+      if constexpr (NS) {
+        const uint16_t* np = a.s2 + hs * a.tokens + t + 4 * g;
+        if (vec) {
+          const u32x2 v = *(const u32x2*)np;
+          p.n2[0] = v.x; p.n2[1] = v.y;
+        } else {
+          p.n2[0] = np[0] | ((uint32_t)np[1] << 16);
+          p.n2[1] = np[2] | ((uint32_t)np[3] << 16);
+        }
+        const uint16_t* op = a.offsets + (hs * nb + (t >> lgb)) * R + L * j;
+        if constexpr (R == 128) {
+          const u32x4 v = *(const u32x4*)op;
+          p.of[0] = v.x; p.of[1] = v.y; p.of[2] = v.z; p.of[3] = v.w;
+        } else {
+          const u32x2 v = *(const u32x2*)op;
+          p.of[0] = v.x; p.of[1] = v.y;
         }
       }
       if constexpr (PT) {
@@ -191,7 +214,7 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
     const size_t orow = (size_t)a.heads * a.dim * OB;          // bytes between x rows
     unsigned char* const ybase =
         (unsigned char*)a.y + ((s * a.tokens) * a.heads + h) * a.dim * OB + (seg * R + L * j) * OB;
-    DqPre<R, PT> cur;
+    DqPre<R, PT, NS> cur;
     for (int i = 0; i < nt; ++i) {
       load(i, cur);
 
@@ -224,15 +247,17 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
         }
         av[K] = u32x4{q4[0], q4[1], q4[2], q4[3]};
       }
-      float nu[4];
+      float nu[4], s1v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-      nu[r] = (a.nsep ? f16_to_f32(cur.nw[r >> 1] >> (16 * (r & 1))) : 1.f) * a.inv_sqrt_n;
-      if constexpr (PT) {
-        const uint32_t sw = r < 2 ? cur.sc[0].x : cur.sc[0].y;
-        nu[r] *= f16_to_f32(sw >> (16 * (r & 1)));
+        s1v[r] = a.nsep ? f16_to_f32(cur.nw[r >> 1] >> (16 * (r & 1))) : 1.f;
+        nu[r] = s1v[r] * a.inv_sqrt_n;
+        if constexpr (PT) {
+          const uint32_t sw = r < 2 ? cur.sc[0].x : cur.sc[0].y;
+          nu[r] *= f16_to_f32(sw >> (16 * (r & 1)));
+        }
+        if constexpr (NS) nu[r] *= f16_to_f32(cur.n2[r >> 1] >> (16 * (r & 1)));
       }
-    }
 
       // results: lane (g, j) owns channels [L j, L j + L) of tokens 4 g + r; f16/bf16 outputs are
       // packed as each pair of I-blocks completes (fp32 outputs keep L floats per token)
@@ -260,7 +285,8 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc[r] * nu[r]) ^ sbit);
+          float v = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc[r] * nu[r]) ^ sbit);
+          if constexpr (NS) v = __builtin_fmaf(s1v[r], f16_to_f32(cur.of[I >> 1] >> (16 * (I & 1))), v);
           if constexpr (ODT == DT_F32)
             ow[r][I] = __builtin_bit_cast(uint32_t, v);
           else if ((I & 1) == 0)
@@ -358,12 +384,13 @@ __global__ void __launch_bounds__(64) dequant_ptok_kernel(DequantArgs a, int64_t
 }
 
 // ---------------------------------------------------------------------------------------
-template <int ODT, int R, int LG, bool PT>
+template <int ODT, int R, int LG, bool PT, bool NS = false>
 static void dq_mfma_k(const DequantArgs& a, hipStream_t st, int lgL) {
   const int64_t nchunks = (a.seqs * a.heads << lgL) * (a.tokens / 64);
-  const int64_t grid = persistent_grid(dequant_mfma<ODT, R, LG, PT>, 256, nchunks);
-  const int vec = ((uintptr_t)a.scales & (PT ? 7u : 15u)) == 0 && (!a.norms || ((uintptr_t)a.norms & 7u) == 0);
-  hipLaunchKernelGGL((dequant_mfma<ODT, R, LG, PT>), dim3((unsigned)grid), dim3(256), 0, st, a, nchunks, lgL, vec);
+  const int64_t grid = persistent_grid(dequant_mfma<ODT, R, LG, PT, NS>, 256, nchunks);
+  const int vec = ((uintptr_t)a.scales & (PT ? 7u : 15u)) == 0 && (!a.norms || ((uintptr_t)a.norms & 7u) == 0) &&
+                  (!NS || ((uintptr_t)a.s2 & 7u) == 0);
+  hipLaunchKernelGGL((dequant_mfma<ODT, R, LG, PT, NS>), dim3((unsigned)grid), dim3(256), 0, st, a, nchunks, lgL, vec);
 }
 
 template <int ODT, int R, int LG>
@@ -386,10 +413,15 @@ static void dq_ptok_k(const DequantArgs& a, hipStream_t st) {
                      nseg, ntiles, lgL);
 }
 
+template <int ODT, int R, int LG>
+static void dq_nsn_k(const DequantArgs& a, hipStream_t st) {
+  dq_mfma_k<ODT, R, LG, false, true>(a, st, 0);
+}
+
 // compile-time Hadamard size: LG = log2(n) in {0 (none), 4, 5, 6, 7}
-template <int ODT, int R, bool PCHAN>
+template <int ODT, int R, int KIND>    // KIND: 0 per-token, 1 per-channel, 2 NSN
 static void dq_by_lg(const DequantArgs& a, hipStream_t st) {
-#define KVQ_DQ(LGV) (PCHAN ? dq_pchan_k<ODT, R, LGV>(a, st) : dq_ptok_k<ODT, R, LGV>(a, st))
+#define KVQ_DQ(LGV) (KIND == 1 ? dq_pchan_k<ODT, R, LGV>(a, st) : KIND == 2 ? dq_nsn_k<ODT, R, LGV>(a, st) : dq_ptok_k<ODT, R, LGV>(a, st))
   switch (a.lg_had) {
     case 0: KVQ_DQ(0); break;
     case 4: KVQ_DQ(4); break;
@@ -400,23 +432,24 @@ static void dq_by_lg(const DequantArgs& a, hipStream_t st) {
 #undef KVQ_DQ
 }
 
-template <int ODT, bool PCHAN>
+template <int ODT, int KIND>
 static void dq_odt(const DequantArgs& a, hipStream_t st) {
-  const bool wide = PCHAN ? a.dim == 128 : a.dim >= 128;
-  if (wide) dq_by_lg<ODT, 128, PCHAN>(a, st); else dq_by_lg<ODT, 64, PCHAN>(a, st);
+  const bool wide = KIND ? a.dim == 128 : a.dim >= 128;
+  if (wide) dq_by_lg<ODT, 128, KIND>(a, st); else dq_by_lg<ODT, 64, KIND>(a, st);
 }
 
-template <bool PCHAN>
+template <int KIND>
 static hipError_t dq_launch(const DequantArgs& a, hipStream_t st) {
   switch (a.out_dtype) {
-    case DT_F16: dq_odt<DT_F16, PCHAN>(a, st); break;
-    case DT_BF16: dq_odt<DT_BF16, PCHAN>(a, st); break;
-    default: dq_odt<DT_F32, PCHAN>(a, st); break;
+    case DT_F16: dq_odt<DT_F16, KIND>(a, st); break;
+    case DT_BF16: dq_odt<DT_BF16, KIND>(a, st); break;
+    default: dq_odt<DT_F32, KIND>(a, st); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t st) { return dq_launch<true>(a, st); }
-hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t st) { return dq_launch<false>(a, st); }
+hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t st) { return dq_launch<1>(a, st); }
+hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t st) { return dq_launch<0>(a, st); }
+hipError_t launch_dequantize_nsn(const DequantArgs& a, hipStream_t st) { return dq_launch<2>(a, st); }
 
 }  // namespace kvq

@@ -28,11 +28,29 @@ struct QuantArgs {
   int64_t out_tok0;         // stream token of the first quantized token (a multiple of B; 0 for a plain call)
 };
 
+// NSN variant (normalize, shift, normalize before the per-channel quantizer)
+struct NsnArgs {
+  const void* x;            // [rows, heads, D] f16/bf16
+  const int8_t* signs;      // [heads, D] or null
+  uint8_t* codes;           // head-major, as for the other modes
+  uint16_t* s1;             // [seqs, heads, tokens] fp16: ||x|| / sqrt(D)
+  uint16_t* s2;             // [seqs, heads, tokens] fp16: ||u1 - o|| / sqrt(D)
+  uint16_t* offsets;        // [seqs, heads, tokens/B, D] fp16: the block's channel mean, original domain
+  uint16_t* scales;         // [seqs, heads, tokens/B, D] fp16
+  int64_t seqs, tokens, heads, dim;
+  int32_t block;
+  int32_t lg_had;
+  int32_t q;                // Q = 2^(bits-1) - 1
+  int32_t dtype;
+};
+
 struct DequantArgs {
   const uint8_t* codes;
-  const uint16_t* norms;
+  const uint16_t* norms;    // NSN: s1
   const uint16_t* scales;
   const int8_t* signs;
+  const uint16_t* s2;       // NSN only
+  const uint16_t* offsets;  // NSN only
   void* y;
   int64_t seqs, tokens, heads, dim;
   int32_t block;
@@ -46,9 +64,11 @@ struct DequantArgs {
 struct ScoreArgs {
   const uint16_t* q;        // [seqs, q_heads, D] fp16
   const uint8_t* codes;
-  const uint16_t* norms;
+  const uint16_t* norms;    // NSN: s1
   const uint16_t* scales;
   const int8_t* signs;
+  const uint16_t* s2;       // NSN only
+  const uint16_t* offsets;  // NSN only
   float* scores;            // [seqs, q_heads, tokens]
   int64_t seqs, tokens, heads, dim, q_heads;
   int32_t block;
@@ -56,6 +76,7 @@ struct ScoreArgs {
   float inv_sqrt_n;
   int32_t nsep;
   int32_t per_channel;
+  int32_t nsn;              // NSN: norms = s1, plus s2 and the block offsets
 };
 
 struct AttnArgs {
@@ -87,6 +108,8 @@ struct AttnArgs {
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_quantize_nsn(const NsnArgs& a, hipStream_t stream);
+hipError_t launch_dequantize_nsn(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t stream);

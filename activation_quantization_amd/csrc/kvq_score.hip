@@ -9,6 +9,10 @@
 //
 // scores[s, hq, t] = sum_d q[s,hq,d] k^[s,t,hq/G,d]
 //                  = norm[t] * sum_d (R q)[d] * scale[blk(t), d] * code[t, d]
+// and for the NSN variant (k^ = s1 (s2 R^T (c scale) + offset); NSNQuant summary, "implementation
+// details": the byproducts folded into the score kernel)
+//                  = s1[t] s2[t] * sum_d (R q)[d] scale[blk(t), d] code[t, d] + s1[t] (q . offset[blk(t)])
+// where q . offset (original domain) is one dot product per unit and query head.
 //
 // Work: a workgroup takes a chunk of one head-major (sequence, KV head) stream; each wave
 // walks units of U tokens (U = the scale block for per-channel modes, 128 otherwise).  Per unit
@@ -43,6 +47,8 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
   constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
   __shared__ __attribute__((aligned(16))) float qr[16 * R];   // rotated queries of this KV head's group
+  __shared__ float qn[16 * R];                                 // NSN: the queries, original domain
+  __shared__ float qob[4][16];                                 // NSN: per wave, q . offset of the unit
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int G = (int)(a.q_heads / a.heads);
@@ -57,6 +63,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   for (int e = tid; e < G * R; e += 256) {
     const int hh = e / R, d = e % R;
     float v = f16_to_f32(a.q[(s * a.q_heads + kvh * G + hh) * R + d]);
+    if (a.nsn) qn[e] = v;
     if (a.lg_had && a.signs[kvh * R + d] < 0) v = -v;
     qr[e] = v;
   }
@@ -110,6 +117,20 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
           for (int e = 0; e < 8; ++e) sc[8 * K + e] = f16_to_f32(srow[8 * K + nib_of(e)]);
       }
     }
+    if (a.nsn) {
+      // q . offset of this unit for every query head of the group (lanes take R / 64 channels)
+      const uint16_t* orow = a.offsets + (sh * nb + un) * R;
+      for (int hh = 0; hh < G; ++hh) {
+        float p = 0.f;
+#pragma unroll
+        for (int d = lane; d < R; d += 64) p = __builtin_fmaf(qn[hh * R + d], f16_to_f32(orow[d]), p);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) p += shfl_xor_f(p, o);
+        if (lane == 0) qob[w][hh] = p;
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    }
     for (int hc = 0; hc < NHC; ++hc) {
       // A operand: row i = lane & 15 -> head hc 8 + i / 2, hi (i even) or lo (i odd) part
       const int hl = hc * 8 + (j >> 1);
@@ -147,7 +168,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
       // 16-token groups, four at a time: every load of the four first, then the products
       for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
         uint32_t wd[4][KS];
-        float f[4];
+        float f[4], f1[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int64_t t = t0 + 16 * (gr0 + b) + j;
@@ -160,12 +181,14 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
               const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
               wd[b][0] = v.x; wd[b][1] = v.y;
             }
-            f[b] = (a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f) * 0x1p24f;
+            f1[b] = a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f;
+            f[b] = f1[b] * 0x1p24f;
             if (!a.per_channel) f[b] *= f16_to_f32(a.scales[tstream + t]);
+            if (a.nsn) f[b] *= f16_to_f32(a.s2[tstream + t]);
           } else {
 #pragma unroll
             for (int k = 0; k < KS; ++k) wd[b][k] = 0u;      // code 0
-            f[b] = 0.f;
+            f[b] = f1[b] = 0.f;
           }
         }
 #pragma unroll
@@ -179,8 +202,10 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
           if (t < T) {
             const int h0 = hc * 8 + 2 * g;
             float* sp = a.scores + (s * a.q_heads + kvh * G + h0) * T + t;
-            if (h0 < G) sp[0] = (acc.x + acc.y) * f[b];
-            if (h0 + 1 < G) sp[T] = (acc.z + acc.w) * f[b];
+            const float add0 = a.nsn && h0 < G ? f1[b] * qob[w][h0] : 0.f;
+            const float add1 = a.nsn && h0 + 1 < G ? f1[b] * qob[w][h0 + 1] : 0.f;
+            if (h0 < G) sp[0] = __builtin_fmaf(acc.x + acc.y, f[b], add0);
+            if (h0 + 1 < G) sp[T] = __builtin_fmaf(acc.z + acc.w, f[b], add1);
           }
         }
       }

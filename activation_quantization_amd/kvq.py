@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP = range(6)
-MODES = {"naive": 0, "nsep": 1, "pchan": 2, "nsep_pchan": 3}
+MODES = {"naive": 0, "nsep": 1, "pchan": 2, "nsep_pchan": 3, "nsn_pchan": 4}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
 DTYPE_NAMES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -46,6 +46,10 @@ _SIGNATURES = {
     "kvq_attention_decode_stream": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, _P, ctypes.c_int64,
                                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                    ctypes.c_int64, _P]),
+    "kvq_quantize_nsn": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kvq_dequantize_nsn": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
+    "kvq_score_decode_nsn": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                            _P]),
     "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (ctypes.c_int32, []),
@@ -100,7 +104,11 @@ class Desc:
 
     @property
     def per_channel(self) -> bool:
-        return self.mode in ("pchan", "nsep_pchan")
+        return self.mode in ("pchan", "nsep_pchan", "nsn_pchan")
+
+    @property
+    def nsn(self) -> bool:
+        return self.mode == "nsn_pchan"
 
     @property
     def rows(self) -> int:
@@ -224,6 +232,54 @@ def attention_decode(d: Desc, q: torch.Tensor, k_cache, v_cache, k_signs=None, v
                                     _ptr(vc), _ptr(vn), _ptr(vs), _ptr(v_signs), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "kvq_attention_decode")
+    return out
+
+
+def alloc_nsn(d: Desc, device):
+    """Outputs of kvq_quantize_nsn: codes, s1, s2 (fp16 per token), offsets, scales (fp16 per block
+    and channel), all head-major."""
+    codes = torch.empty(d.codes_shape(), dtype=torch.uint8, device=device)
+    s1 = torch.empty(d.norms_shape(), dtype=torch.float16, device=device)
+    s2 = torch.empty(d.norms_shape(), dtype=torch.float16, device=device)
+    offsets = torch.empty(d.scales_shape(), dtype=torch.float16, device=device)
+    scales = torch.empty(d.scales_shape(), dtype=torch.float16, device=device)
+    return codes, s1, s2, offsets, scales
+
+
+def quantize_nsn(d: Desc, x: torch.Tensor, signs: torch.Tensor | None = None, out=None, stream=None):
+    """kvq_quantize_nsn.  Returns (codes, s1, s2, offsets, scales)."""
+    codes, s1, s2, offsets, scales = out if out is not None else alloc_nsn(d, x.device)
+    _need_cuda(x, signs, codes, s1, s2, offsets, scales)
+    st = lib().kvq_quantize_nsn(ctypes.byref(d.c()), _ptr(x), _ptr(signs), _ptr(codes), _ptr(s1), _ptr(s2),
+                                _ptr(offsets), _ptr(scales), _stream(stream))
+    _check(st, "kvq_quantize_nsn")
+    return codes, s1, s2, offsets, scales
+
+
+def dequantize_nsn(d: Desc, codes, s1, s2, offsets, scales, signs=None, out_dtype=torch.float16,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_dequantize_nsn: x^ = s1 (s2 R^T (c scale) + offset), [rows, heads, head_dim]."""
+    if out is None:
+        out = torch.empty((d.rows, d.heads, d.head_dim), dtype=out_dtype, device=codes.device)
+    _need_cuda(codes, s1, s2, offsets, scales, signs, out)
+    st = lib().kvq_dequantize_nsn(ctypes.byref(d.c()), _ptr(codes), _ptr(s1), _ptr(s2), _ptr(offsets), _ptr(scales),
+                                  _ptr(signs), _ptr(out), DTYPES[out.dtype], _stream(stream))
+    _check(st, "kvq_dequantize_nsn")
+    return out
+
+
+def score_decode_nsn(d: Desc, q: torch.Tensor, codes, s1, s2, offsets, scales, signs=None,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_score_decode_nsn: scores fp32 [seqs, q_heads, tokens] from an NSN cache."""
+    if q.dtype != torch.float16:
+        raise ValueError("q must be fp16")
+    q_heads = q.shape[1]
+    if out is None:
+        out = torch.empty((d.seqs, q_heads, d.tokens_per_seq), dtype=torch.float32, device=codes.device)
+    _need_cuda(q, codes, s1, s2, offsets, scales, signs, out)
+    st = lib().kvq_score_decode_nsn(ctypes.byref(d.c()), _ptr(q), q_heads, _ptr(codes), _ptr(s1), _ptr(s2),
+                                    _ptr(offsets), _ptr(scales), _ptr(signs), _ptr(out), _stream(stream))
+    _check(st, "kvq_score_decode_nsn")
     return out
 
 

@@ -68,7 +68,8 @@ typedef enum {
   KVQ_NAIVE = 0,      /* per-token absmax of x (after the optional rotation)                 */
   KVQ_NSEP = 1,       /* norm separation, per-token absmax of the unit direction             */
   KVQ_PCHAN = 2,      /* per-channel absmax over a block of tokens, no norm separation       */
-  KVQ_NSEP_PCHAN = 3  /* norm separation, then per-channel scales over the token block       */
+  KVQ_NSEP_PCHAN = 3, /* norm separation, then per-channel scales over the token block       */
+  KVQ_NSN_PCHAN = 4   /* normalize-shift-normalize, then per-channel scales (the _nsn calls)  */
 } kvq_mode;
 
 typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2 } kvq_dtype;
@@ -95,8 +96,9 @@ typedef struct {
 kvq_status kvq_validate(const kvq_desc* d);
 
 /* Buffer sizes for a valid descriptor (-1 if kvq_validate fails):
- *   codes bytes = rows*heads*head_dim/2; norms = rows*heads for NSEP modes, else 0;
- *   scales = rows*heads (per-token) or seqs*(tokens_per_seq/block_tokens)*heads*head_dim.  */
+ *   codes bytes = rows*heads*head_dim/2; norms = rows*heads for NSEP modes and for each of s1 and s2
+ *   of the NSN mode, else 0; scales = rows*heads (per-token) or
+ *   seqs*(tokens_per_seq/block_tokens)*heads*head_dim (per-channel and NSN; also the NSN offsets). */
 int64_t kvq_codes_bytes(const kvq_desc* d);
 int64_t kvq_norms_count(const kvq_desc* d);
 int64_t kvq_scales_count(const kvq_desc* d);
@@ -195,6 +197,31 @@ kvq_status kvq_attention_decode_stream(const kvq_desc* d, int64_t tokens_cached,
                                        const void* v_residual, float* out, void* workspace, int64_t workspace_bytes,
                                        void* stream);
 
+/*
+ * The NSN variant (mode KVQ_NSN_PCHAN; NSNQuant summary, "Normalize-Shift-Normalize (NSN)" and
+ * "Hadamard transform", "implementation details"): after the optional rotation y = R x, per token
+ * s1 = ||y|| / sqrt(D) and u1 = y / s1; per block of block_tokens tokens the channel mean o of u1;
+ * u2 = u1 - o, s2 = ||u2|| / sqrt(D) (0 when ||u2|| < 2^-16 sqrt(D)), u3 = u2 / s2; then per-channel
+ * absmax scales of u3 over the block and rounded codes as for KVQ_NSEP_PCHAN.  Stored (head-major):
+ *   codes  as for the other modes;
+ *   s1, s2 fp16 [seqs, heads, tokens_per_seq];
+ *   offsets fp16 [seqs, heads, tokens_per_seq / B, head_dim]: R^T o, the mean in the original domain;
+ *   scales fp16 [seqs, heads, tokens_per_seq / B, head_dim].
+ * Dequantization: x^ = s1 (s2 R^T (c * scale) + offset).  Decode score: q . x^ =
+ * s1 s2 (R q) . (c * scale) + s1 (q . offset), the byproducts folded in.  Same shapes, dtypes,
+ * head_dim (64, 128) and block sizes as the per-channel modes; x, codes, offsets and signs 16-byte
+ * aligned; the other arrays 2-byte (scores 4-byte).  The plain quantize / dequantize / score calls
+ * refuse this mode; attention and the streaming append do not support it.
+ */
+kvq_status kvq_quantize_nsn(const kvq_desc* d, const void* x, const int8_t* signs, uint8_t* codes, uint16_t* s1,
+                            uint16_t* s2, uint16_t* offsets, uint16_t* scales, void* stream);
+kvq_status kvq_dequantize_nsn(const kvq_desc* d, const uint8_t* codes, const uint16_t* s1, const uint16_t* s2,
+                              const uint16_t* offsets, const uint16_t* scales, const int8_t* signs, void* y,
+                              int32_t y_dtype, void* stream);
+kvq_status kvq_score_decode_nsn(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* codes,
+                                const uint16_t* s1, const uint16_t* s2, const uint16_t* offsets,
+                                const uint16_t* scales, const int8_t* signs, float* scores, void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_str(kvq_status s);
 
@@ -202,7 +229,7 @@ const char* kvq_status_str(kvq_status s);
 const char* kvq_last_error(void);
 
 /* ABI version: 10000 * major + 100 * minor + patch (1.1: fused decode attention; 1.2: streaming
- * append and attention over a streamed cache). */
+ * append and attention over a streamed cache; 1.3: the NSN variant). */
 int32_t kvq_version(void);
 
 #ifdef __cplusplus

@@ -102,8 +102,9 @@ def check_scores(gpu: np.ndarray, ref: np.ndarray, q: np.ndarray, k_hat: np.ndar
     tol = REL_SCORE * np.maximum(np.abs(ref), scale)
     err = np.abs(np.asarray(gpu, np.float64) - ref)
     bad = err > tol
-    assert not np.any(bad), f"scores: {int(bad.sum())} outside tolerance, worst {np.max(err / tol):.3g}x"
-    return float(np.max(err / tol))
+    ratio = np.divide(err, tol, out=np.where(err > 0, np.inf, 0.0), where=tol > 0)   # 0 / 0: exact zero
+    assert not np.any(bad), f"scores: {int(bad.sum())} outside tolerance, worst {np.max(ratio):.3g}x"
+    return float(np.max(ratio))
 
 
 REL_ATTN = 2e-3

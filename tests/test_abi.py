@@ -195,3 +195,35 @@ def test_stream_attention_validation_before_any_device_call():
     assert _atts(d, 128, kr=None, vr=None, ws_bytes=100) == kvq.ERR_SHAPE
     assert _atts(d, 130, kr=None, ws_bytes=100) == kvq.ERR_NULL
     assert _atts(kvq.Desc(**{**GOOD, "mode": "naive", "block_tokens": 0}), 10) == kvq.ERR_UNSUPPORTED
+
+
+NSN = dict(GOOD, mode="nsn_pchan")
+
+
+def test_nsn_sizes_and_mode_checks():
+    d = kvq.Desc(**NSN)
+    assert d.validate() == kvq.OK
+    rows = d.seqs * d.tokens_per_seq
+    assert d.norms_count() == rows * d.heads                             # each of s1 and s2
+    assert d.scales_count() == rows // d.block_tokens * d.heads * d.head_dim   # also the offsets
+    L = kvq.lib()
+    c = ctypes.byref(d.c())
+    # the plain calls refuse the NSN mode, the _nsn calls refuse the others
+    assert L.kvq_quantize(c, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_dequantize(c, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_score_decode(c, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    g = ctypes.byref(kvq.Desc(**GOOD).c())
+    assert L.kvq_quantize_nsn(g, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_dequantize_nsn(g, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_score_decode_nsn(g, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    # missing byproducts, signs, alignment
+    assert L.kvq_quantize_nsn(c, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == kvq.ERR_NULL
+    assert L.kvq_quantize_nsn(c, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_NULL   # Hadamard on
+    assert L.kvq_quantize_nsn(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, None) == kvq.ERR_ALIGN
+    assert L.kvq_dequantize_nsn(c, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, 0, None) == kvq.ERR_ALIGN
+    assert L.kvq_dequantize_nsn(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 7, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_score_decode_nsn(c, FAKE, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_SHAPE
+    assert L.kvq_score_decode_nsn(c, FAKE, 16, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == kvq.ERR_NULL
+    # attention and the streaming append do not take the NSN mode
+    assert _att(d) == kvq.ERR_UNSUPPORTED
+    assert _app(d) == kvq.ERR_UNSUPPORTED
