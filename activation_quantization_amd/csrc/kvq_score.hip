@@ -41,14 +41,14 @@ __device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
 
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
 
-template <int R>
+template <int R, bool NS>
 __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
                                                     int vec_scales) {
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
   constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
   __shared__ __attribute__((aligned(16))) float qr[16 * R];   // rotated queries of this KV head's group
-  __shared__ float qn[16 * R];                                 // NSN: the queries, original domain
-  __shared__ float qob[4][16];                                 // NSN: per wave, q . offset of the unit
+  __shared__ float qn[NS ? 16 * R : 1];                        // NSN: the queries, original domain
+  __shared__ float qob[4][NS ? 16 : 1];                        // NSN: per wave, q . offset of the unit
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int G = (int)(a.q_heads / a.heads);
@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   for (int e = tid; e < G * R; e += 256) {
     const int hh = e / R, d = e % R;
     float v = f16_to_f32(a.q[(s * a.q_heads + kvh * G + hh) * R + d]);
-    if (a.nsn) qn[e] = v;
+    if constexpr (NS) qn[e] = v;
     if (a.lg_had && a.signs[kvh * R + d] < 0) v = -v;
     qr[e] = v;
   }
@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
           for (int e = 0; e < 8; ++e) sc[8 * K + e] = f16_to_f32(srow[8 * K + nib_of(e)]);
       }
     }
-    if (a.nsn) {
+    if constexpr (NS) {
       // q . offset of this unit for every query head of the group (lanes take R / 64 channels)
       const uint16_t* orow = a.offsets + (sh * nb + un) * R;
       for (int hh = 0; hh < G; ++hh) {
@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
             f1[b] = a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f;
             f[b] = f1[b] * 0x1p24f;
             if (!a.per_channel) f[b] *= f16_to_f32(a.scales[tstream + t]);
-            if (a.nsn) f[b] *= f16_to_f32(a.s2[tstream + t]);
+            if constexpr (NS) f[b] *= f16_to_f32(a.s2[tstream + t]);
           } else {
 #pragma unroll
             for (int k = 0; k < KS; ++k) wd[b][k] = 0u;      // code 0
@@ -202,10 +202,13 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
           if (t < T) {
             const int h0 = hc * 8 + 2 * g;
             float* sp = a.scores + (s * a.q_heads + kvh * G + h0) * T + t;
-            const float add0 = a.nsn && h0 < G ? f1[b] * qob[w][h0] : 0.f;
-            const float add1 = a.nsn && h0 + 1 < G ? f1[b] * qob[w][h0 + 1] : 0.f;
-            if (h0 < G) sp[0] = __builtin_fmaf(acc.x + acc.y, f[b], add0);
-            if (h0 + 1 < G) sp[T] = __builtin_fmaf(acc.z + acc.w, f[b], add1);
+            if constexpr (NS) {
+              if (h0 < G) sp[0] = __builtin_fmaf(acc.x + acc.y, f[b], f1[b] * qob[w][h0]);
+              if (h0 + 1 < G) sp[T] = __builtin_fmaf(acc.z + acc.w, f[b], f1[b] * qob[w][h0 + 1]);
+            } else {
+              if (h0 < G) sp[0] = (acc.x + acc.y) * f[b];
+              if (h0 + 1 < G) sp[T] = (acc.z + acc.w) * f[b];
+            }
           }
         }
       }
@@ -219,10 +222,14 @@ hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t st) {
   const int64_t nchunks = (nunits + SCORE_UNITS_PER_BLOCK - 1) / SCORE_UNITS_PER_BLOCK;
   const int64_t ntiles = a.seqs * a.heads * nchunks;
   const int vec_scales = ((uintptr_t)a.scales & 15u) == 0;
-  if (a.dim == 128)
-    hipLaunchKernelGGL((score_kernel<128>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
-  else
-    hipLaunchKernelGGL((score_kernel<64>), dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
+  };
+  if (a.nsn) {
+    if (a.dim == 128) go(score_kernel<128, true>); else go(score_kernel<64, true>);
+  } else {
+    if (a.dim == 128) go(score_kernel<128, false>); else go(score_kernel<64, false>);
+  }
   return hipGetLastError();
 }
 

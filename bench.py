@@ -165,6 +165,43 @@ def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, str
     return rows
 
 
+def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup):
+    """The NSN variant (normalize, shift, normalize before the per-channel quantizer) on the same
+    cache: quantize, dequantize to fp16, decode score, each timed with HIP events on the stream."""
+    d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, 4, "nsn_pchan", w.block_tokens, w.hadamard, torch.float16)
+    out = kvq.alloc_nsn(d, dev)
+    scores = torch.empty((w.seqs, w.q_heads, w.tokens), dtype=torch.float32, device=dev)
+    n = w.seqs * w.tokens * w.heads * w.head_dim
+    tok = w.seqs * w.tokens * w.heads
+    blk = w.seqs * (w.tokens // w.block_tokens) * w.heads * w.head_dim
+    side = 2 * 2 * tok + 2 * 2 * blk                      # s1, s2; offsets, scales (fp16)
+    signs_b = w.heads * w.head_dim
+    nbytes = {"quantize_nsn": 2 * n + signs_b + n // 2 + side,
+              "dequantize_nsn": n // 2 + side + signs_b + 2 * n,
+              "score_decode_nsn": 2 * w.seqs * w.q_heads * w.head_dim + signs_b + n // 2 + side
+                                  + 4 * w.seqs * w.q_heads * w.tokens}
+    calls = {"quantize_nsn": lambda: kvq.quantize_nsn(d, x, signs, out=out, stream=stream),
+             "dequantize_nsn": lambda: kvq.dequantize_nsn(d, *out, signs, out=y, stream=stream),
+             "score_decode_nsn": lambda: kvq.score_decode_nsn(d, q, *out, signs, out=scores, stream=stream)}
+    rows = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        rows[name] = {"us": round(us, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "in_step": False}
+    del out, scores
+    return rows
+
+
 def other_configs(torch, kvq, synth, dev, steps, warmup):
     """Quantize and dequantize of the other workloads, each iteration after a 512 MiB read that
     evicts L2 and the MALL (the events bracket the kernel only).  A read, not a write: a written
@@ -334,6 +371,8 @@ def main():
     if attn_us is not None and not args.only:
         kernels.update(stream_decode(torch, kvq, d, w, q, kc, vcache, signs, att_out, ws, stream, dev,
                                      args.steps, args.warmup))
+        kernels.update(nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, min(args.steps, 10),
+                                   min(args.warmup, 2)))
     if args.only:
         print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
         return
