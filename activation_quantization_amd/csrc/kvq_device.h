@@ -100,6 +100,24 @@ __device__ __forceinline__ float shfl_f(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
 }
 
+// ------------------------------------------------------------------ code packing
+// Codes by one fma into [128, 256), where the fp32 ulp is 2^-16: b = bits(v + 136.5) has code + 8
+// in byte 2 (v rounded half up), and b & 0xffff == 0 marks a value within 2^-17 of a tie.
+constexpr float CODE_MAGIC = 136.5f;
+
+__device__ __forceinline__ uint32_t min3_u16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_min3_u16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// 8 magic-biased codes (channels 8d .. 8d + 7) -> one packed word
+__device__ __forceinline__ uint32_t pack8(const uint32_t (&b)[8]) {
+  const uint32_t ev = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0602u) | __builtin_amdgcn_perm(b[6], b[4], 0x06020C0Cu);
+  const uint32_t od = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0602u) | __builtin_amdgcn_perm(b[7], b[5], 0x06020C0Cu);
+  return ((od << 4) | ev) ^ 0x88888888u;   // byte k = nibble(c_2k) | nibble(c_2k+1) << 4
+}
+
 // ------------------------------------------------------------------ Walsh-Hadamard
 // In-register fast Walsh-Hadamard transform (unnormalized, natural Sylvester order) on
 // independent blocks of n = 2^lg consecutive elements of v[R]; lg is wave-uniform.

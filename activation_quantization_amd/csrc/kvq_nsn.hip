@@ -10,16 +10,25 @@
 //   u2 = u1 - o,  s2 = ||u2|| / sqrt(D),  u3 = u2 / s2,  scale = max over the block |u3| / Q,
 //   c = rne(fp32(u3 / scale));  stored: codes, s1, s2, R^T o (the offset, original domain), scale.
 //
-// The statistics (two token norms, the block's channel means and maxima) are taken in fp64, so the
-// codes are the same rounding decisions as the fp64 definition without a near-tie path: fp16 inputs
-// rotate exactly in fp64, and what differs is summation order at the 2^-53 level.
+// Everything after the fp16/bf16 load is fp64, so every code is the rounding decision of the fp64
+// definition (what differs is summation order at the 2^-53 level) and no near-tie path over the
+// statistics is needed.  fp64 adds and fmas issue at the fp32 rate on this chip, so the cost is
+// the instruction count per element, which the layout keeps low:
 //
-// Layout: one workgroup of 2 B threads per tile (one sequence, one head, B tokens); thread
-// 2 t + half holds channels [half D/2, half D/2 + D/2) of token t in registers.  When the rotation
-// spans the whole row, its top butterfly stage pairs channel c with c + D/2: each thread reads the
-// whole row and forms its half of that stage directly (the stages commute), so no exchange is
-// needed.  Column statistics over the block's tokens reduce across the lanes of equal parity,
-// then across waves through LDS.
+//   row phase    thread 2 t + h holds channels [h D/2, h D/2 + D/2) of token t: the butterflies
+//                over the low channel bits are in registers, the top one (when the rotation spans
+//                the row) is a DPP exchange with the neighbouring lane; the token norm is a
+//                register sum plus that exchange.
+//   transpose    two v_permlane32_swap / v_permlane16_swap steps turn the wave's 32 tokens x D
+//                channels into lanes holding D/8 consecutive channels of 4 tokens (tokens
+//                differing in bits 3 and 4), with no arithmetic.
+//   block phase  the column sums and maxima over the block are 4-token register reductions,
+//                then one LDS partial per (lane group, wave), reduced by all threads; the second
+//                token norm is a register sum plus three lane exchanges.
+//
+// Input rows are staged in LDS by global_load_lds (1 KiB per wave instruction, XOR-swizzled
+// 16-byte chunks, so the half-row reads are free of bank conflicts); the partials reuse that
+// buffer.  Codes leave as D/16-byte pieces, eight lanes completing each token's row.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -44,156 +53,306 @@ __device__ __forceinline__ void fwht64(double (&v)[N], int stages) {
   }
 }
 
-// sum (MAX = false) or maximum over the lanes of equal parity (the threads holding the same
-// channels of different tokens) of one wave
-template <bool MAX>
-__device__ __forceinline__ double parity_reduce(double x) {
-#pragma unroll
-  for (int m = 2; m < 64; m <<= 1) {
-    const double y = __shfl_xor(x, m);
-    x = MAX ? fmax(x, y) : x + y;
-  }
-  return x;
+// the value of lane ^ 1 (DPP quad_perm [1, 0, 3, 2] on both halves)
+__device__ __forceinline__ double xor1(double x) {
+  const u32x2 b = __builtin_bit_cast(u32x2, x);
+  u32x2 r;
+  r.x = (uint32_t)__builtin_amdgcn_mov_dpp((int)b.x, 0xB1, 0xF, 0xF, false);
+  r.y = (uint32_t)__builtin_amdgcn_mov_dpp((int)b.y, 0xB1, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+
+// v_permlane32_swap on a pair of doubles: lanes 32..63 of p trade places with lanes 0..31 of q
+__device__ __forceinline__ void swap32(double& p, double& q) {
+  const u32x2 a = __builtin_bit_cast(u32x2, p), b = __builtin_bit_cast(u32x2, q);
+  const auto lo = __builtin_amdgcn_permlane32_swap(a.x, b.x, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(a.y, b.y, false, false);
+  p = __builtin_bit_cast(double, u32x2{lo[0], hi[0]});
+  q = __builtin_bit_cast(double, u32x2{lo[1], hi[1]});
+}
+// v_permlane16_swap on a pair of doubles: the odd 16-lane rows of p trade places with the even
+// rows of q
+__device__ __forceinline__ void swap16(double& p, double& q) {
+  const u32x2 a = __builtin_bit_cast(u32x2, p), b = __builtin_bit_cast(u32x2, q);
+  const auto lo = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+  p = __builtin_bit_cast(double, u32x2{lo[0], hi[0]});
+  q = __builtin_bit_cast(double, u32x2{lo[1], hi[1]});
+}
+// x + (x of lane ^ 16), x + (x of lane ^ 32): a swap of x with a copy of itself puts both terms in
+// every lane
+__device__ __forceinline__ double add_xor16(double x) {
+  double y = x;
+  swap16(x, y);
+  return x + y;
+}
+__device__ __forceinline__ double add_xor32(double x) {
+  double y = x;
+  swap32(x, y);
+  return x + y;
+}
+
+// fp64 -> fp16 bits through fp32 (the opaque step keeps the compiler from replacing the two hardware
+// conversions by a bitwise fp64 -> fp16 routine)
+__device__ __forceinline__ uint16_t f64_to_f16(double x) {
+  float f = (float)x;
+  asm volatile("" : "+v"(f));
+  return (uint16_t)f32_to_f16(f);
+}
+
+// byte offset of the double (p, c) in the partials: rows of D doubles, 16-byte chunks XOR-swizzled
+// with the row so that both the lanes' row-pair writes and the reducers' column reads spread over
+// the banks
+template <int D> __device__ __forceinline__ int part_off(int p, int c) {
+  return p * (8 * D) + 16 * ((c >> 1) ^ (p & 15)) + 8 * (c & 1);
 }
 
 template <int DT, int D, int LG, int B>
 __global__ void __launch_bounds__(2 * B) quant_nsn_tile(NsnArgs a, int64_t ntiles) {
-  constexpr int RH = D / 2, NW = 2 * B / 64, LGD = D == 128 ? 7 : 6;
+  constexpr int RH = D / 2;                            // row phase: channels per thread
+  constexpr int CQ = D / 8;                            // block phase: channels per lane (x 4 tokens)
+  constexpr int NW = 2 * B / 64;                       // waves (32 tokens each)
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16;         // input row bytes, 16-byte chunks per row
+  constexpr int WSTAGE = B * ROWB / NW, NLD = WSTAGE / 1024;
+  constexpr int LGD = D == 128 ? 7 : 6;
   constexpr bool CROSS = LG == LGD;                    // the rotation's top stage crosses the halves
-  __shared__ double part[NW][D];                       // per-wave column sums / maxima
-  __shared__ double mean[D];                           // the block's column mean of u1
-  __shared__ double col[D];                            // the block's column scale
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = tid & 1, t = tid >> 1;
+  constexpr int P = 8 * NW;                            // partial rows: (wave, lane group)
+  constexpr int TPC = 2 * B / D, RPT = P / TPC;        // reducers per channel, rows each
+  static_assert(B * ROWB == P * 8 * D && NLD >= 1, "tile shape");
+  // the staged input rows; once every thread holds its row, the column partials
+  __shared__ __attribute__((aligned(16))) unsigned char stage[B * ROWB];
+  __shared__ __attribute__((aligned(16))) double omean[D];   // the block's column mean o
+  __shared__ __attribute__((aligned(16))) double oinv[D];    // Q / the column's max |u3|
+  __shared__ __attribute__((aligned(16))) uint32_t smask[D / 2];   // sign bits of the channel pairs
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tile = xcd_tile(blockIdx.x, ntiles);
   const int64_t nb = a.tokens / B, hs = tile / nb, blk = tile - hs * nb;
   const int64_t seq = hs / a.heads, h = hs - seq * a.heads;
-  const uint16_t* xr = (const uint16_t*)a.x + ((seq * a.tokens + blk * B + t) * a.heads + h) * D;
-  const int8_t* sg = LG ? a.signs + h * D : nullptr;
-  const int c0 = half * RH;
-  auto ld = [&](int c) -> double {
-    const uint32_t b = xr[c];
-    double v = DT == DT_F16 ? (double)f16_to_f32(b) : (double)bf16_to_f32(b);
-    if (LG != 0 && sg[c] < 0) v = -v;
-    return v;
-  };
+  const int64_t row0 = seq * a.tokens + blk * B;       // x row of the tile's first token
+  const int64_t tok0 = hs * a.tokens + blk * B;        // head-major index of that token
+  const int64_t sblk = hs * nb + blk;                  // the block's scale and offset row
+  const double rd = sqrt((double)D), qd = (double)a.q;
 
-  // 1. y = R x on this thread's half row (exact for fp16 inputs), then / sqrt(n)
+  // 1. this wave's B / NW rows into LDS (slot cc of row r holds chunk cc ^ (r % CPR)); the sign
+  //    masks of the head's channel pairs
+  {
+    const unsigned char* xw = (const unsigned char*)a.x + ((row0 + (B / NW) * w) * a.heads + h) * ROWB;
+    const uint32_t tok_bytes = (uint32_t)(a.heads * ROWB);
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int p = 64 * k + lane, r = p / CPR, cc = p % CPR;
+      const uint32_t off = (uint32_t)r * tok_bytes + 16u * (uint32_t)(cc ^ ((r + (B / NW) * w) % CPR));
+      __builtin_amdgcn_global_load_lds((const void*)(xw + off),
+                                       (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, 0);
+    }
+    if constexpr (LG != 0) {
+      if (tid < D / 2) {
+        const int8_t* sg = a.signs + h * D + 2 * tid;
+        smask[tid] = (sg[0] < 0 ? 0x8000u : 0u) | (sg[1] < 0 ? 0x80000000u : 0u);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0): this wave's rows have landed
+  asm volatile("" ::: "memory");
+  lds_barrier();
+
+  // 2. row phase: y = H diag(sigma) x on this thread's half row in fp64 (left unnormalized)
+  const int half = lane & 1, tau = lane >> 1, t = 32 * w + tau;
   double v[RH];
 #pragma unroll
-  for (int i = 0; i < RH; ++i) {
-    if constexpr (CROSS) {
-      const double own = ld(c0 + i), oth = ld((c0 ^ RH) + i);
-      v[i] = half == 0 ? own + oth : oth - own;
-    } else {
-      v[i] = ld(c0 + i);
+  for (int k = 0; k < CPR / 2; ++k) {
+    const int cc = half * (CPR / 2) + k;
+    u32x4 xv = *(const u32x4*)(stage + t * ROWB + 16 * (cc ^ (t % CPR)));
+    if constexpr (LG != 0) xv ^= *(const u32x4*)(smask + half * (RH / 2) + 4 * k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * k + 2 * e] = (double)lo_f32<DT>(xv[e]);
+      v[8 * k + 2 * e + 1] = (double)hi_f32<DT>(xv[e]);
     }
   }
   fwht64<RH>(v, CROSS ? LG - 1 : LG);
-  if (LG) {
-    const double rn = sqrt((double)(1 << LG));
+  if constexpr (CROSS) {
+    const double sgn = half ? -1.0 : 1.0;              // (a, b) -> (a + b, a - b) across the pair
 #pragma unroll
-    for (int i = 0; i < RH; ++i) v[i] /= rn;
+    for (int i = 0; i < RH; ++i) v[i] = __builtin_fma(v[i], sgn, xor1(v[i]));
   }
-  const double rd = sqrt((double)D);
+  double k1;                                           // sqrt(D) / ||y||: u1 = k1 y
+  {
+    double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < RH; ++i) s4[i & 3] = __builtin_fma(v[i], v[i], s4[i & 3]);
+    double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    ss += xor1(ss);
+    const double nrm = sqrt(ss);
+    k1 = nrm > 0.0 ? rd / nrm : 0.0;
+    if (half == 0) a.s1[tok0 + t] = f64_to_f16(nrm / (sqrt((double)(1 << LG)) * rd));
+  }
+  lds_barrier();                                       // every row has been read: stage -> partials
 
-  // 2. s1 = ||y|| / sqrt(D), u1 = y / s1
-  double ss = 0.0;
+  // 3. transpose: register q CQ + i (q = 2 s + r) becomes channel cb + i of token tq(q) =
+  //    (tau & 7) + 8 r + 16 s; the token scale k1 follows the same swaps
 #pragma unroll
-  for (int i = 0; i < RH; ++i) ss = __builtin_fma(v[i], v[i], ss);
-  ss += __shfl_xor(ss, 1);
-  const double s1 = sqrt(ss) / rd;
+  for (int i = 0; i < RH / 2; ++i) swap32(v[i], v[i + RH / 2]);
 #pragma unroll
-  for (int i = 0; i < RH; ++i) v[i] = s1 > 0.0 ? v[i] / s1 : 0.0;
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < RH / 4; ++i) swap16(v[s * (RH / 2) + i], v[s * (RH / 2) + i + RH / 4]);
+  double kk[4] = {k1, k1, k1, k1};
+  swap32(kk[0], kk[2]);
+  swap32(kk[1], kk[3]);
+  swap16(kk[0], kk[1]);
+  swap16(kk[2], kk[3]);
+  const int cb = half * RH + ((lane >> 5) & 1) * (RH / 2) + ((lane >> 4) & 1) * (RH / 4);
+  const int prow = 8 * w + (tau & 7);
+  auto tq = [&](int q) { return (tau & 7) + 8 * (q & 1) + 16 * (q >> 1); };
 
-  // 3. o = the block's channel means of u1
+  // block-wide column reduction of this lane's CQ values through the partials: the reducers
+  // (TPC threads per channel, RPT rows each) leave the result of `fin` in dst[c]
+  auto column_reduce = [&](const double (&val)[CQ], auto op, auto fin, double* dst) {
 #pragma unroll
-  for (int i = 0; i < RH; ++i) {
-    const double r = parity_reduce<false>(v[i]);
-    if (lane < 2) part[w][c0 + i] = r;
-  }
-  __syncthreads();
-  if (tid < D) {
-    double sum = 0.0;
+    for (int m = 0; m < CQ / 2; ++m) {
+      typedef double d2 __attribute__((ext_vector_type(2)));
+      *(d2*)(stage + part_off<D>(prow, cb + 2 * m)) = d2{val[2 * m], val[2 * m + 1]};
+    }
+    lds_barrier();
+    const int c = tid / TPC, j = tid % TPC;
+    double r = *(const double*)(stage + part_off<D>(j * RPT, c));
 #pragma unroll
-    for (int k = 0; k < NW; ++k) sum += part[k][tid];
-    mean[tid] = sum / (double)B;
-  }
-  __syncthreads();
+    for (int k = 1; k < RPT; ++k) r = op(r, *(const double*)(stage + part_off<D>(j * RPT + k, c)));
+#pragma unroll
+    for (int m = 1; m < TPC; m <<= 1) r = op(r, __shfl_xor(r, m));
+    if (j == 0) dst[c] = fin(r, c);
+    lds_barrier();
+  };
 
-  // 4. u2 = u1 - o, s2 = ||u2|| / sqrt(D) (0 when ||u2|| < 2^-16 sqrt(D)), u3 = u2 / s2
-  double ss2 = 0.0;
+  // 4. o: column sums of u1 = k y over the block
+  {
+    double cs[CQ];
 #pragma unroll
-  for (int i = 0; i < RH; ++i) {
-    v[i] -= mean[c0 + i];
-    ss2 = __builtin_fma(v[i], v[i], ss2);
-  }
-  ss2 += __shfl_xor(ss2, 1);
-  const double n2 = sqrt(ss2);
-  const double s2 = n2 < 0x1p-16 * rd ? 0.0 : n2 / rd;
-#pragma unroll
-  for (int i = 0; i < RH; ++i) v[i] = s2 > 0.0 ? v[i] / s2 : 0.0;
-
-  // 5. per-channel absmax of u3 over the block, scale = amax / Q
-#pragma unroll
-  for (int i = 0; i < RH; ++i) {
-    const double r = parity_reduce<true>(fabs(v[i]));
-    if (lane < 2) part[w][c0 + i] = r;
-  }
-  __syncthreads();
-  if (tid < D) {
-    double m = 0.0;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) m = fmax(m, part[k][tid]);
-    const double sc = m / (double)a.q;
-    col[tid] = sc;
-    a.scales[(hs * nb + blk) * D + tid] = (uint16_t)f32_to_f16((float)sc);
-  }
-  __syncthreads();
-
-  // 6. codes c = rne(fp32(u3 / scale)), packed two per byte; the token scales
-  uint32_t cw[RH / 8];
-#pragma unroll
-  for (int k = 0; k < RH / 8; ++k) cw[k] = 0u;
-#pragma unroll
-  for (int i = 0; i < RH; ++i) {
-    const double sc = col[c0 + i];
-    int c = sc > 0.0 ? (int)__builtin_rintf((float)(v[i] / sc)) : 0;
-    c = c > a.q ? a.q : (c < -a.q ? -a.q : c);
-    cw[i >> 3] |= ((uint32_t)c & 0xFu) << (4 * (i & 7));
-  }
-  const int64_t tok = hs * a.tokens + blk * B + t;     // head-major token index
-  uint32_t* cp = (uint32_t*)(a.codes + tok * (D / 2) + c0 / 2);
-#pragma unroll
-  for (int k = 0; k < RH / 8; ++k) cp[k] = cw[k];
-  if (half == 0) {
-    a.s1[tok] = (uint16_t)f32_to_f16((float)s1);
-    a.s2[tok] = (uint16_t)f32_to_f16((float)s2);
+    for (int i = 0; i < CQ; ++i)
+      cs[i] = __builtin_fma(v[i], kk[0], __builtin_fma(v[CQ + i], kk[1], __builtin_fma(v[2 * CQ + i], kk[2], v[3 * CQ + i] * kk[3])));
+    column_reduce(cs, [](double x, double y) { return x + y; },
+                  [](double r, int) { return r * (1.0 / (double)B); }, omean);
   }
 
-  // 7. the offset R^T o (original domain) of this block: threads 0 and 1 (token 0), from mean[]
-  if (t == 0) {
-    double of[RH];
+  // 5. the stored offset R^T o = diag(sigma) H o / sqrt(n), by the last wave (D / 64 channels a lane)
+  if (w == NW - 1) {
+    constexpr int PL = D / 64;
+    double of[PL];
 #pragma unroll
-    for (int i = 0; i < RH; ++i) {
-      if constexpr (CROSS) {
-        const double own = mean[c0 + i], oth = mean[(c0 ^ RH) + i];
-        of[i] = half == 0 ? own + oth : oth - own;
-      } else {
-        of[i] = mean[c0 + i];
+    for (int e = 0; e < PL; ++e) of[e] = omean[lane + 64 * e];
+    if constexpr (PL == 2 && LG == 7) {
+      const double x0 = of[0], x1 = of[1];
+      of[0] = x0 + x1;
+      of[1] = x0 - x1;
+    }
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+      if (s < LG) {
+        const int m = 1 << s;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          const double pv = __shfl_xor(of[e], m);
+          of[e] = (lane & m) ? pv - of[e] : of[e] + pv;
+        }
       }
     }
-    fwht64<RH>(of, CROSS ? LG - 1 : LG);
-    uint16_t* op = a.offsets + (hs * nb + blk) * D + c0;
-    const double rn = sqrt((double)(1 << LG));
+    const double rn = 1.0 / sqrt((double)(1 << LG));
 #pragma unroll
-    for (int i = 0; i < RH; ++i) {
-      double x = of[i];
-      if (LG) {
-        x /= rn;
-        if (sg[c0 + i] < 0) x = -x;
-      }
-      op[i] = (uint16_t)f32_to_f16((float)x);
+    for (int e = 0; e < PL; ++e) {
+      const int c = lane + 64 * e;
+      double x = of[e] * rn;
+      if (LG != 0 && a.signs[h * D + c] < 0) x = -x;
+      a.offsets[sblk * D + c] = f64_to_f16(x);
     }
+  }
+
+  // 6. u2 = k y - o, s2 = ||u2|| / sqrt(D) (0 under 2^-16 sqrt(D)), u3 = u2 / s2; column maxima
+  {
+    double ss[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < CQ; ++i) {
+      const double o = omean[cb + i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q * CQ + i] = __builtin_fma(v[q * CQ + i], kk[q], -o);
+        ss[q] = __builtin_fma(v[q * CQ + i], v[q * CQ + i], ss[q]);
+      }
+    }
+    double a2[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double x = ss[q] + xor1(ss[q]);                  // the lanes holding token tq(q): lane bits 0, 4, 5
+      x = add_xor16(x);
+      x = add_xor32(x);
+      const double n2 = sqrt(x);
+      const bool zero = n2 < 0x1p-16 * rd;
+      a2[q] = zero ? 0.0 : rd / n2;
+      if ((lane & 0x31) == 0) a.s2[tok0 + 32 * w + tq(q)] = zero ? (uint16_t)0 : f64_to_f16(n2 / rd);
+    }
+    double mx[CQ];
+#pragma unroll
+    for (int i = 0; i < CQ; ++i) {
+      double m = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q * CQ + i] *= a2[q];
+        m = fmax(m, fabs(v[q * CQ + i]));
+      }
+      mx[i] = m;
+    }
+    column_reduce(mx, [](double x, double y) { return fmax(x, y); },
+                  [&](double r, int c) {
+                    a.scales[sblk * D + c] = f64_to_f16(r / qd);
+                    return r > 0.0 ? qd / r : 0.0;
+                  },
+                  oinv);
+  }
+
+  // 7. codes c = rne(fp32(u3 / scale)): one magic add per value; a value within 2^-17 of a tie
+  //    (rare) is rounded again with rint
+  constexpr int NG = CQ / 8;                           // packed words per token
+  uint32_t pk[4][NG];
+  uint32_t fl = 0xffffffffu;
+  double iv[CQ];
+#pragma unroll
+  for (int i = 0; i < CQ; ++i) iv[i] = oinv[cb + i];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(uint32_t, (float)(v[q * CQ + 8 * g + e] * iv[8 * g + e]) + CODE_MAGIC);
+      fl = min3_u16(fl, b[0], b[1]);
+      fl = min3_u16(fl, b[2], b[3]);
+      fl = min3_u16(fl, b[4], b[5]);
+      fl = min3_u16(fl, b[6], b[7]);
+      pk[q][g] = pack8(b);
+    }
+  if ((fl & 0xffffu) == 0u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = (int)__builtin_rintf((float)(v[q * CQ + 8 * g + e] * iv[8 * g + e]));
+          word |= ((uint32_t)c & 0xFu) << (4 * e);
+        }
+        pk[q][g] = word;
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    unsigned char* cp = a.codes + (tok0 + 32 * w + tq(q)) * (D / 2) + cb / 2;
+    if constexpr (NG == 2)
+      *(u32x2*)cp = u32x2{pk[q][0], pk[q][1]};
+    else
+      *(uint32_t*)cp = pk[q][0];
   }
 }
 

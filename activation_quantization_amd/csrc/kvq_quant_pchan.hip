@@ -41,27 +41,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr float CODE_MAGIC = 136.5f;   // 128 + 8 + 1/2: [128, 256) has ulp 2^-16
-
 template <int DT> __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (DT == DT_F16)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
                                                    0);
-}
-
-__device__ __forceinline__ uint32_t min3_u16(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t r;
-  asm("v_min3_u16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// 8 codes (fma results of channels 8d .. 8d + 7 of the lane) -> one packed word
-__device__ __forceinline__ uint32_t pack8(const uint32_t (&b)[8]) {
-  const uint32_t ev = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0602u) | __builtin_amdgcn_perm(b[6], b[4], 0x06020C0Cu);
-  const uint32_t od = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0602u) | __builtin_amdgcn_perm(b[7], b[5], 0x06020C0Cu);
-  return ((od << 4) | ev) ^ 0x88888888u;   // byte k = nibble(c_2k) | nibble(c_2k+1) << 4
 }
 
 template <int DT> __device__ __forceinline__ double widen64(uint32_t h) {
