@@ -165,9 +165,13 @@ def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, str
     return rows
 
 
-def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup):
+NSN_KERNELS = ("quantize_nsn", "dequantize_nsn", "score_decode_nsn")
+
+
+def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup, only=None):
     """The NSN variant (normalize, shift, normalize before the per-channel quantizer) on the same
-    cache: quantize, dequantize to fp16, decode score, each timed with HIP events on the stream."""
+    cache: quantize, dequantize to fp16, decode score, each timed with HIP events on the stream
+    (`only`: just that one, after an untimed quantize that fills the cache it reads)."""
     d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, 4, "nsn_pchan", w.block_tokens, w.hadamard, torch.float16)
     out = kvq.alloc_nsn(d, dev)
     scores = torch.empty((w.seqs, w.q_heads, w.tokens), dtype=torch.float32, device=dev)
@@ -184,6 +188,9 @@ def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup):
              "dequantize_nsn": lambda: kvq.dequantize_nsn(d, *out, signs, out=y, stream=stream),
              "score_decode_nsn": lambda: kvq.score_decode_nsn(d, q, *out, signs, out=scores, stream=stream)}
     rows = {}
+    if only is not None:
+        calls["quantize_nsn"]()
+        calls = {only: calls[only]}
     for name, fn in calls.items():
         for _ in range(warmup):
             fn()
@@ -246,7 +253,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seqs", type=int, default=10, help="sequences in the oracle baseline sample (0 = skip)")
-    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode"), default=None,
+    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode") + NSN_KERNELS,
+                    default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
     ap.add_argument("--other-configs", type=int, default=1,
                     help="also time quantize / dequantize of the other workloads (1 = yes), after an L2/MALL flush")
@@ -279,6 +287,10 @@ def main():
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    if args.only in NSN_KERNELS:
+        kernels = nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, args.steps, args.warmup, only=args.only)
+        print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
+        return
     if args.calibrate_copy:
         del y
         y = torch.empty_like(x)
