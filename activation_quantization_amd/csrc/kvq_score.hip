@@ -41,14 +41,18 @@ __device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
 
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
 
+// fp16 1.0: the norm or token scale of a mode that has none, read like a real one (no branch)
+__device__ const uint16_t kF16One[1] = {0x3C00u};
+
 template <int R, bool NS>
-__global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
                                                     int vec_scales) {
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
   constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
   __shared__ __attribute__((aligned(16))) float qr[16 * R];   // rotated queries of this KV head's group
-  __shared__ float qn[NS ? 16 * R : 1];                        // NSN: the queries, original domain
-  __shared__ float qob[4][NS ? 16 : 1];                        // NSN: per wave, q . offset of the unit
+  __shared__ float qob[NS ? SCORE_UNITS_PER_BLOCK : 1][16];  // NSN: q . offset per (unit, query head)
+  __shared__ __attribute__((aligned(16))) uint16_t qh[NS ? 16 * R : 8];   // NSN: fp16 queries (zero rows past G)
+  __shared__ float tokf[4][2][256];   // per wave, the unit's tokens: norm 2^24 token-scale s2, and norm
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int G = (int)(a.q_heads / a.heads);
@@ -63,7 +67,6 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   for (int e = tid; e < G * R; e += 256) {
     const int hh = e / R, d = e % R;
     float v = f16_to_f32(a.q[(s * a.q_heads + kvh * G + hh) * R + d]);
-    if constexpr (NS) qn[e] = v;
     if (a.lg_had && a.signs[kvh * R + d] < 0) v = -v;
     qr[e] = v;
   }
@@ -84,6 +87,13 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
     __syncthreads();
   }
 
+  // NSN: the original-domain fp16 queries, the A operand of q . offset on the matrix cores (row i =
+  // query head i of the group, zero rows past G)
+  if constexpr (NS) {
+    for (int e = tid; e < 16 * R; e += 256) qh[e] = e / R < G ? a.q[(s * a.q_heads + kvh * G) * R + e] : (uint16_t)0;
+    __syncthreads();
+  }
+
   const int NHC = (G + 7) / 8;                              // passes of 8 query heads
   const int64_t nunits = (T + U - 1) / U;
   const int64_t u_begin = ci * SCORE_UNITS_PER_BLOCK;
@@ -92,9 +102,61 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
   const int64_t tstream = sh * T;                           // index of the stream's first token
   const int64_t nb = a.per_channel ? T / a.block : 0;
   const int ngr = U / 16;                                   // 16-token groups per unit
+  const uint16_t* nrm_p = a.nsep ? a.norms + tstream : kF16One;              // per-token norms
+  const uint16_t* tsc_p = a.per_channel ? kF16One : a.scales + tstream;      // per-token scales
+
+  // NSN: q . offset for every (unit, query head) of the workgroup, all offset loads in flight at
+  // once: B holds a unit's offset vector in every column (lane 16 g + j: channels 32 K + 8 g +
+  // [0, 8)), so D[i][*] = q_i . offset and lane 16 g (column 0) holds heads 4 g .. 4 g + 3 (exact
+  // fp16 products, fp32 sums).  Wave w takes the units it walks below.
+  if constexpr (NS) {
+    constexpr int UW = SCORE_UNITS_PER_BLOCK / 4;           // units per wave
+    u32x4 ov[UW][KS];
+#pragma unroll
+    for (int i = 0; i < UW; ++i) {
+      const int64_t un = u_begin + w + 4 * i;
+      const uint16_t* orow = a.offsets + (sh * nb + (un < u_end ? un : u_begin)) * R + 8 * g;
+#pragma unroll
+      for (int K = 0; K < KS; ++K) {
+        if (vec_scales) {                                   // scales and offsets 16-byte aligned
+          ov[i][K] = *(const u32x4*)(orow + 32 * K);
+        } else {
+          uint32_t o4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (uint32_t)orow[32 * K + 2 * e] | ((uint32_t)orow[32 * K + 2 * e + 1] << 16);
+          ov[i][K] = u32x4{o4[0], o4[1], o4[2], o4[3]};
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UW; ++i) {
+      f32x4 qo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < KS; ++K) {
+        const f16x8 qa = __builtin_bit_cast(f16x8, *(const u32x4*)(qh + j * R + 32 * K + 8 * g));
+        qo = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, __builtin_bit_cast(f16x8, ov[i][K]), qo, 0, 0, 0);
+      }
+      if (j == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qob[w + 4 * i][4 * g + r] = qo[r];
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  }
 
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
+    // the unit's per-token factors: coalesced 2-byte loads by all lanes (token t0 + lane + 64 k,
+    // clamped to the last token), issued before the scale loads, into this wave's LDS table
+    uint16_t nv[4], sv[4], s2v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t tt = t0 + lane + 64 * k;
+      const int64_t tc = tt < T ? tt : T - 1;
+      nv[k] = nrm_p[a.nsep ? tc : 0];
+      sv[k] = tsc_p[a.per_channel ? 0 : tc];
+      if constexpr (NS) s2v[k] = a.s2[tstream + tc];
+    }
     // scales of this lane's channels (LB g .. as fp16), loaded with the unit
     float sc[KS * 8];
     if (a.per_channel) {
@@ -117,20 +179,19 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
           for (int e = 0; e < 8; ++e) sc[8 * K + e] = f16_to_f32(srow[8 * K + nib_of(e)]);
       }
     }
-    if constexpr (NS) {
-      // q . offset of this unit for every query head of the group (lanes take R / 64 channels)
-      const uint16_t* orow = a.offsets + (sh * nb + un) * R;
-      for (int hh = 0; hh < G; ++hh) {
-        float p = 0.f;
+    // f = norm 2^24 token-scale (s2), f1 = norm (a mode without the value reads the constant 1.0)
 #pragma unroll
-        for (int d = lane; d < R; d += 64) p = __builtin_fmaf(qn[hh * R + d], f16_to_f32(orow[d]), p);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) p += shfl_xor_f(p, o);
-        if (lane == 0) qob[w][hh] = p;
+    for (int k = 0; k < 4; ++k) {
+      if (64 * k < U) {
+        const float n1 = f16_to_f32(nv[k]);
+        float fk = n1 * 0x1p24f * f16_to_f32(sv[k]);
+        if constexpr (NS) fk *= f16_to_f32(s2v[k]);
+        tokf[w][0][lane + 64 * k] = fk;
+        tokf[w][1][lane + 64 * k] = n1;
       }
-      __builtin_amdgcn_wave_barrier();
-      asm volatile("" ::: "memory");
     }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
     for (int hc = 0; hc < NHC; ++hc) {
       // A operand: row i = lane & 15 -> head hc 8 + i / 2, hi (i even) or lo (i odd) part
       const int hl = hc * 8 + (j >> 1);
@@ -157,6 +218,13 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
           av[K][e + 1] = pv[1];
         }
       }
+      // NSN: q . offset of this lane's two heads for the unit
+      float qo0 = 0.f, qo1 = 0.f;
+      if constexpr (NS) {
+        const int h0 = hc * 8 + 2 * g;
+        qo0 = qob[un - u_begin][h0 < 16 ? h0 : 15];
+        qo1 = qob[un - u_begin][h0 + 1 < 16 ? h0 + 1 : 15];
+      }
       // accumulator start: -8 2^-24 sum_k A[i][k], from one more product with B = ones (lane (g, j)
       // receives rows 4 g + r)
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
@@ -169,27 +237,26 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
       for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
         uint32_t wd[4][KS];
         float f[4], f1[4];
+        // the four groups' code loads are all issued before any is used (a token past the end
+        // reads the last token; its scores are not stored)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int64_t t = t0 + 16 * (gr0 + b) + j;
-          if (t < T) {
-            const unsigned char* cp = cstream + t * (R / 2) + LB * g;
-            if constexpr (KS == 4) {
-              const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
-              wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
-            } else {
-              const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
-              wd[b][0] = v.x; wd[b][1] = v.y;
-            }
-            f1[b] = a.nsep ? f16_to_f32(a.norms[tstream + t]) : 1.f;
-            f[b] = f1[b] * 0x1p24f;
-            if (!a.per_channel) f[b] *= f16_to_f32(a.scales[tstream + t]);
-            if constexpr (NS) f[b] *= f16_to_f32(a.s2[tstream + t]);
+          const int64_t tc = t < T ? t : T - 1;
+          const unsigned char* cp = cstream + tc * (R / 2) + LB * g;
+          if constexpr (KS == 4) {
+            const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
+            wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
           } else {
-#pragma unroll
-            for (int k = 0; k < KS; ++k) wd[b][k] = 0u;      // code 0
-            f[b] = f1[b] = 0.f;
+            const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
+            wd[b][0] = v.x; wd[b][1] = v.y;
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          f[b] = tokf[w][0][16 * (gr0 + b) + j];
+          f1[b] = tokf[w][1][16 * (gr0 + b) + j];
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -203,8 +270,8 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a, int64_t ntiles,
             const int h0 = hc * 8 + 2 * g;
             float* sp = a.scores + (s * a.q_heads + kvh * G + h0) * T + t;
             if constexpr (NS) {
-              if (h0 < G) sp[0] = __builtin_fmaf(acc.x + acc.y, f[b], f1[b] * qob[w][h0]);
-              if (h0 + 1 < G) sp[T] = __builtin_fmaf(acc.z + acc.w, f[b], f1[b] * qob[w][h0 + 1]);
+              if (h0 < G) sp[0] = __builtin_fmaf(acc.x + acc.y, f[b], f1[b] * qo0);
+              if (h0 + 1 < G) sp[T] = __builtin_fmaf(acc.z + acc.w, f[b], f1[b] * qo1);
             } else {
               if (h0 < G) sp[0] = (acc.x + acc.y) * f[b];
               if (h0 + 1 < G) sp[T] = (acc.z + acc.w) * f[b];
@@ -221,7 +288,7 @@ hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t st) {
   const int64_t nunits = (a.tokens + U - 1) / U;
   const int64_t nchunks = (nunits + SCORE_UNITS_PER_BLOCK - 1) / SCORE_UNITS_PER_BLOCK;
   const int64_t ntiles = a.seqs * a.heads * nchunks;
-  const int vec_scales = ((uintptr_t)a.scales & 15u) == 0;
+  const int vec_scales = ((uintptr_t)a.scales & 15u) == 0 && (!a.nsn || ((uintptr_t)a.offsets & 15u) == 0);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
   };
