@@ -66,6 +66,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   __shared__ __attribute__((aligned(16))) float qr[GM * R];                 // rotated queries
   __shared__ __attribute__((aligned(16))) unsigned char vbuf[4][U * 64];    // per wave: one block of V codes
   __shared__ __attribute__((aligned(16))) unsigned char wbuf[4][U / 64][16][64];   // per wave: MFMA A operand (weight planes)
+  __shared__ float tokf[4][2][U];   // per wave, the block's tokens: K norm 2^24 / sqrt(D) (log2 e), V norm
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index, in a scalar register
   const int g = lane >> 4, j = lane & 15;
@@ -121,6 +122,8 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   unsigned char* vw = &vbuf[w][0];
   unsigned char* ww = &wbuf[w][0][0][0];
 
+  const uint16_t* knp = a.nsep ? a.k_norms + tstream : kF16One;      // per-token norms (1.0 without)
+  const uint16_t* vnp = a.nsep ? a.v_norms + tstream : kF16One;
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
     // the block's V codes into LDS (U * 64 bytes, 1 KiB per instruction, linear)
@@ -128,6 +131,15 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     for (int k = 0; k < NGR; ++k)
       __builtin_amdgcn_global_load_lds((const void*)(vstream + t0 * (R / 2) + k * 1024 + 16 * lane),
                                        (__attribute__((address_space(3))) void*)(vw + k * 1024), 16, 0, 0);
+    // the block's K and V norms: coalesced 2-byte loads by all lanes (token t0 + lane + 64 k),
+    // issued with the scale loads, then kept in this wave's LDS table
+    uint16_t kn[U / 64], vn[U / 64];
+#pragma unroll
+    for (int k = 0; k < U / 64; ++k) {
+      const int64_t tt = t0 + lane + 64 * k;
+      kn[k] = knp[a.nsep ? tt : 0];
+      vn[k] = vnp[a.nsep ? tt : 0];
+    }
     // K scales of this lane's channels (R/4) g + 8 K + nib(e); V scales of channels 8 vb ..
     // (scale rows are 16-byte aligned: the entry point requires it)
     const uint16_t* ksrow = a.k_scales + (sh * nb + un) * R + (R / 4) * g;
@@ -149,6 +161,14 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) vs[c] = f16_to_f32((c & 1) ? wv[c >> 1] >> 16 : wv[c >> 1] & 0xffffu);
     }
+
+#pragma unroll
+    for (int k = 0; k < U / 64; ++k) {
+      tokf[w][0][lane + 64 * k] = f16_to_f32(kn[k]) * (0x1p24f * zscale);
+      tokf[w][1][lane + 64 * k] = f16_to_f32(vn[k]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
 
     // 2. scores of the block: A = (R q) * K scale as fp16 hi/lo rows (row i = lane & 15 -> head
     //    i / 2), B = K codes as fp16 subnormals (c + 8) 2^-24
@@ -190,8 +210,12 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
         const int64_t t = t0 + 16 * (gr0 + b) + j;
         const u32x4 v = __builtin_nontemporal_load((const u32x4*)(kstream + t * (R / 2) + LB * g));
         wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
-        fk[b] = (a.nsep ? f16_to_f32(a.k_norms[tstream + t]) : 1.f) * (0x1p24f * zscale);
-        nvv[gr0 + b] = a.nsep ? f16_to_f32(a.v_norms[tstream + t]) : 1.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        fk[b] = tokf[w][0][16 * (gr0 + b) + j];
+        nvv[gr0 + b] = tokf[w][1][16 * (gr0 + b) + j];
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {

@@ -100,6 +100,10 @@ __device__ __forceinline__ float shfl_f(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
 }
 
+// fp16 1.0: the per-token norm or scale of a mode that has none, read like a real one (no branch
+// between the load and its use)
+static __device__ const uint16_t kF16One[1] = {0x3C00u};
+
 // ------------------------------------------------------------------ code packing
 // Codes by one fma into [128, 256), where the fp32 ulp is 2^-16: b = bits(v + 136.5) has code + 8
 // in byte 2 (v rounded half up), and b & 0xffff == 0 marks a value within 2^-17 of a tie.

@@ -41,8 +41,6 @@ __device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
 
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
 
-// fp16 1.0: the norm or token scale of a mode that has none, read like a real one (no branch)
-__device__ const uint16_t kF16One[1] = {0x3C00u};
 
 template <int R, bool NS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
