@@ -41,6 +41,10 @@ def algorithmic_bytes(w, q_heads):
             "score_decode": q + signs + codes + norms + scales + scores,
             # fused decode attention (a "next" row, outside the step): K and V caches in, fp32 out
             "attention_decode": q + 2 * (signs + codes + norms + scales) + out,
+            # the NSN variant: s1 and s2 per token, offsets shaped like the per-channel scales
+            "quantize_nsn": x + signs + codes + 2 * norms + 2 * scales,
+            "dequantize_nsn": codes + 2 * norms + 2 * scales + signs + x,
+            "score_decode_nsn": q + signs + codes + 2 * norms + 2 * scales + scores,
             "elements": n}
 
 
@@ -175,15 +179,7 @@ def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup, only=
     d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, 4, "nsn_pchan", w.block_tokens, w.hadamard, torch.float16)
     out = kvq.alloc_nsn(d, dev)
     scores = torch.empty((w.seqs, w.q_heads, w.tokens), dtype=torch.float32, device=dev)
-    n = w.seqs * w.tokens * w.heads * w.head_dim
-    tok = w.seqs * w.tokens * w.heads
-    blk = w.seqs * (w.tokens // w.block_tokens) * w.heads * w.head_dim
-    side = 2 * 2 * tok + 2 * 2 * blk                      # s1, s2; offsets, scales (fp16)
-    signs_b = w.heads * w.head_dim
-    nbytes = {"quantize_nsn": 2 * n + signs_b + n // 2 + side,
-              "dequantize_nsn": n // 2 + side + signs_b + 2 * n,
-              "score_decode_nsn": 2 * w.seqs * w.q_heads * w.head_dim + signs_b + n // 2 + side
-                                  + 4 * w.seqs * w.q_heads * w.tokens}
+    nbytes = algorithmic_bytes(w, w.q_heads)
     calls = {"quantize_nsn": lambda: kvq.quantize_nsn(d, x, signs, out=out, stream=stream),
              "dequantize_nsn": lambda: kvq.dequantize_nsn(d, *out, signs, out=y, stream=stream),
              "score_decode_nsn": lambda: kvq.score_decode_nsn(d, q, *out, signs, out=scores, stream=stream)}
