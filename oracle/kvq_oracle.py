@@ -369,6 +369,77 @@ def attention_decode_stream(q: np.ndarray, k_hat: np.ndarray | None, v_hat: np.n
 
 
 # ----------------------------------------------------------------------------- error report
+# ----------------------------------------------------------------------------- RRS INT4 GEMM
+RRS_GROUP = 128     # channels per runtime-smoothing group = the GEMM's K block (Figure 4)
+
+
+@dataclasses.dataclass
+class RrsActivations:
+    codes: np.ndarray      # int8 [N, K] in [-Q, Q]
+    packed: np.ndarray     # uint8 [N, K/2]
+    v: np.ndarray          # float64 quotient before rounding [N, K]
+    scale: np.ndarray      # float64 per-token scale a_t [N]
+    scales16: np.ndarray   # float16 stored a_t
+
+
+def rrs_smooth_scales(x: np.ndarray, signs: np.ndarray | None, hadamard: int, group: int = RRS_GROUP) -> np.ndarray:
+    """Runtime smoothing scales (Rotated Runtime Smooth analysis, "master equation" and
+    "term-by-term": s_j = the largest |(X R)_tj| over the N tokens of column j; Figure 4: the
+    group of `group` channels takes its largest s_j).  x: [N, K]; returns s [K / group] float64."""
+    x = np.asarray(x, dtype=np.float64)
+    N, K = x.shape
+    y = rotate(x[:, None, :], signs[None, :], hadamard)[:, 0, :] if hadamard else x
+    col = np.abs(y).max(axis=0) if N else np.zeros(K)
+    return col.reshape(K // group, group).max(axis=1)
+
+
+def rrs_quantize_act(x: np.ndarray, signs: np.ndarray | None, hadamard: int, s: np.ndarray, bits: int = 4,
+                     group: int = RRS_GROUP) -> RrsActivations:
+    """X'_quant = Quantize(X R diag(s)^-1) ("master equation"): every column of the rotated
+    activations divided by its group's smoothing scale, then symmetric per-token INT-b with
+    round-to-nearest (the per-token absmax reading of the activation quantizer), the rounding
+    decision on the fp32 quotient as for the cache modes."""
+    x = np.asarray(x, dtype=np.float64)
+    N, K = x.shape
+    Q = qmax(bits)
+    y = rotate(x[:, None, :], signs[None, :], hadamard)[:, 0, :] if hadamard else x
+    sc = np.repeat(np.asarray(s, dtype=np.float64), group)
+    u = np.where(sc[None, :] > 0.0, y / np.where(sc > 0.0, sc, 1.0)[None, :], 0.0)
+    a = np.abs(u).max(axis=1) / Q if K else np.zeros(N)
+    safe = np.where(a > 0.0, a, 1.0)
+    v = np.where(a[:, None] > 0.0, u / safe[:, None], 0.0)
+    c = np.clip(np.rint(v.astype(np.float32)), -Q, Q).astype(np.int8)
+    return RrsActivations(codes=c, packed=pack_nibbles(c), v=v, scale=a, scales16=a.astype(np.float16))
+
+
+def rrs_quantize_weights(w: np.ndarray, signs: np.ndarray | None, hadamard: int, bits: int = 4) -> Quantized:
+    """W'_quant = Quantize(W_rot): every weight row rotated as the activation rows are (W_rot =
+    W R keeps X W^T = X_rot W_rot^T; the page's R^-1 W does not type-check for an M x K weight),
+    then symmetric per-output-channel INT-b with round-to-nearest: the per-token NAIVE mode
+    with each of the M rows as one token."""
+    w = np.asarray(w, dtype=np.float64)
+    M, K = w.shape
+    spec = Spec(1, M, 1, K, bits, "naive", M, hadamard)
+    return quantize(w[:, None, :], spec, None if signs is None else signs[None, :])
+
+
+def rrs_gemm(x_codes: np.ndarray, a16: np.ndarray, w_codes: np.ndarray, b16: np.ndarray, s: np.ndarray,
+             group: int = RRS_GROUP) -> np.ndarray:
+    """Y = sum_j (X'_quant)_j (W'_quant)_j^T s_j ("master equation", the channel sum of the
+    term-by-term analysis): with X'_quant = a_t c_tj and W'_quant = b_m d_mj and s_j shared by
+    a group, Y_tm = a_t b_m sum_g s_g sum_{j in g} c_tj d_mj; each group's integer product is
+    exact and the scale is applied to it (Figure 4: scales on the interim results).  float64."""
+    c = np.asarray(x_codes, dtype=np.int64)
+    d = np.asarray(w_codes, dtype=np.int64)
+    N, K = c.shape
+    M = d.shape[0]
+    acc = np.zeros((N, M))
+    for g in range(K // group):
+        part = c[:, g * group:(g + 1) * group] @ d[:, g * group:(g + 1) * group].T     # exact integers
+        acc += part.astype(np.float64) * float(s[g])
+    return acc * np.asarray(a16, dtype=np.float64)[:, None] * np.asarray(b16, dtype=np.float64)[None, :]
+
+
 def reconstruction_errors(x: np.ndarray, x_hat: np.ndarray, outlier_mask: np.ndarray) -> dict:
     """Four relative-error measures of a reconstruction (for the mode ordering check).
 
