@@ -487,6 +487,100 @@ kvq_status kvq_attention_decode_stream(const kvq_desc* d, int64_t tokens_cached,
                         "attention_decode_stream");
 }
 
+// ----------------------------------------------------------------------------- RRS INT4 GEMM path
+}  // extern "C"
+
+namespace {
+
+// the per-token descriptor of an [n, k] activation (or weight) matrix: one sequence of n tokens,
+// one head of k channels, NAIVE mode
+kvq_status rrs_desc(kvq_desc* d, int64_t n, int64_t k, int32_t dtype, int32_t hadamard, int32_t bits, const char* what) {
+  if (n < 0) return fail(KVQ_ERR_SHAPE, "%s: row count %lld must be >= 0", what, (long long)n);
+  if (k < 128 || k > 8192 || (k & (k - 1)) != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: k %lld must be a power of two in [128, 8192] (groups of 128 channels)", what,
+                (long long)k);
+  *d = kvq_desc{};
+  d->seqs = 1; d->tokens_per_seq = n; d->heads = 1; d->head_dim = k;
+  d->bits = bits; d->mode = KVQ_NAIVE; d->block_tokens = 0; d->hadamard = hadamard; d->dtype = dtype;
+  return check_desc(d);
+}
+
+kvq_status rrs_inputs(const kvq_desc* d, const void* x, const int8_t* signs) {
+  if (!x) return fail(KVQ_ERR_NULL, "the input matrix is required");
+  if ((d->hadamard != 0) != (signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
+  if (!aligned(x, 16) || (signs && !aligned(signs, 16))) return fail(KVQ_ERR_ALIGN, "x and signs must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_rrs_smooth_scales(const void* x, int64_t n_tokens, int64_t k, int32_t dtype, const int8_t* signs,
+                                 int32_t hadamard, float* scales, void* stream) {
+  kvq_desc d;
+  kvq_status s = rrs_desc(&d, n_tokens, k, dtype, hadamard, 4, "rrs_smooth_scales");
+  if (s != KVQ_OK) return s;
+  if (!scales) return fail(KVQ_ERR_NULL, "scales is required");
+  if (!aligned(scales, 4)) return fail(KVQ_ERR_ALIGN, "scales must be 4-byte aligned");
+  if (n_tokens > 0 && (s = rrs_inputs(&d, x, signs)) != KVQ_OK) return s;
+  if ((s = device_ready()) != KVQ_OK) return s;
+  const kvq::QuantArgs a = quant_args(&d, x, signs, nullptr, nullptr, nullptr);
+  return launched(kvq::launch_rrs_colmax(a, scales, static_cast<hipStream_t>(stream)), "rrs_smooth_scales");
+}
+
+kvq_status kvq_rrs_quantize_act(const void* x, int64_t n_tokens, int64_t k, int32_t dtype, const int8_t* signs,
+                                int32_t hadamard, const float* scales, int32_t bits, uint8_t* codes,
+                                uint16_t* act_scales, void* stream) {
+  kvq_desc d;
+  kvq_status s = rrs_desc(&d, n_tokens, k, dtype, hadamard, bits, "rrs_quantize_act");
+  if (s != KVQ_OK) return s;
+  if (n_tokens == 0) return ok();
+  if ((s = rrs_inputs(&d, x, signs)) != KVQ_OK) return s;
+  if (!scales || !codes || !act_scales) return fail(KVQ_ERR_NULL, "scales, codes and act_scales are required");
+  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(act_scales, 2))
+    return fail(KVQ_ERR_ALIGN, "codes must be 16-byte, scales 4-byte and act_scales 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+  kvq::QuantArgs a = quant_args(&d, x, signs, codes, nullptr, act_scales);
+  a.seg_div = scales;
+  return launched(kvq::launch_quantize_ptok(a, static_cast<hipStream_t>(stream)), "rrs_quantize_act");
+}
+
+kvq_status kvq_rrs_quantize_weights(const void* w, int64_t m, int64_t k, int32_t dtype, const int8_t* signs,
+                                    int32_t hadamard, int32_t bits, uint8_t* codes, uint16_t* w_scales, void* stream) {
+  kvq_desc d;
+  kvq_status s = rrs_desc(&d, m, k, dtype, hadamard, bits, "rrs_quantize_weights");
+  if (s != KVQ_OK) return s;
+  if (m == 0) return ok();
+  if ((s = rrs_inputs(&d, w, signs)) != KVQ_OK) return s;
+  if (!codes || !w_scales) return fail(KVQ_ERR_NULL, "codes and w_scales are required");
+  if (!aligned(codes, 16) || !aligned(w_scales, 2)) return fail(KVQ_ERR_ALIGN, "codes must be 16-byte and w_scales 2-byte aligned");
+  if ((s = device_ready()) != KVQ_OK) return s;
+  const kvq::QuantArgs a = quant_args(&d, w, signs, codes, nullptr, w_scales);
+  return launched(kvq::launch_quantize_ptok(a, static_cast<hipStream_t>(stream)), "rrs_quantize_weights");
+}
+
+kvq_status kvq_rrs_gemm(const uint8_t* x_codes, const uint16_t* act_scales, int64_t n_tokens, const uint8_t* w_codes,
+                        const uint16_t* w_scales, int64_t m, int64_t k, const float* scales, float* y, void* stream) {
+  if (n_tokens < 0 || m < 0) return fail(KVQ_ERR_SHAPE, "n_tokens %lld and m %lld must be >= 0", (long long)n_tokens, (long long)m);
+  if (k < 128 || k % 128 != 0 || k > (int64_t(1) << 20))
+    return fail(KVQ_ERR_UNSUPPORTED, "k %lld must be a multiple of 128 in [128, 2^20]", (long long)k);
+  if (n_tokens == 0 || m == 0) return ok();
+  if ((n_tokens + 127) / 128 * ((m + 127) / 128) >= (int64_t(1) << 31)) return fail(KVQ_ERR_UNSUPPORTED, "too many output tiles");
+  if (!x_codes || !act_scales || !w_codes || !w_scales || !scales || !y)
+    return fail(KVQ_ERR_NULL, "x_codes, act_scales, w_codes, w_scales, scales and y are required");
+  if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(act_scales, 2) || !aligned(w_scales, 2) ||
+      !aligned(scales, 4) || !aligned(y, 4))
+    return fail(KVQ_ERR_ALIGN, "codes must be 16-byte, scales and y 4-byte, act_scales and w_scales 2-byte aligned");
+  kvq_status s;
+  if ((s = device_ready()) != KVQ_OK) return s;
+  kvq::RrsGemmArgs a{};
+  a.x_codes = x_codes; a.x_scales = act_scales; a.w_codes = w_codes; a.w_scales = w_scales;
+  a.s = scales; a.y = y; a.n = n_tokens; a.m = m; a.k = k;
+  return launched(kvq::launch_rrs_gemm(a, static_cast<hipStream_t>(stream)), "rrs_gemm");
+}
+
 const char* kvq_status_str(kvq_status s) {
   switch (s) {
     case KVQ_OK: return "KVQ_OK";
@@ -501,6 +595,6 @@ const char* kvq_status_str(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_version(void) { return 10300; }
+int32_t kvq_version(void) { return 10400; }
 
 }  // extern "C"

@@ -26,6 +26,20 @@ struct QuantArgs {
   int64_t in_seq_tokens;    // x rows (tokens) from one sequence to the next (= tokens for a plain call)
   int64_t out_tokens;       // tokens per head-major output stream (= tokens for a plain call)
   int64_t out_tok0;         // stream token of the first quantized token (a multiple of B; 0 for a plain call)
+  // per-token kernel only (RRS activations): every 128-channel segment k of a row is divided by
+  // seg_div[k] (a divisor of 0 gives 0) after the rotation, before the per-token absmax; null = 1
+  const float* seg_div;
+};
+
+// RRS INT4 GEMM: y[t, m] = a_t b_m sum_g s_g sum_{j in g} cx[t, j] cw[m, j], groups of 128 channels
+struct RrsGemmArgs {
+  const uint8_t* x_codes;   // [n, k/2] packed INT4, channel 2i in the low nibble
+  const uint16_t* x_scales; // [n] fp16 a_t
+  const uint8_t* w_codes;   // [m, k/2]
+  const uint16_t* w_scales; // [m] fp16 b_m
+  const float* s;           // [k/128] group smoothing scales
+  float* y;                 // [n, m] fp32
+  int64_t n, m, k;
 };
 
 // NSN variant (normalize, shift, normalize before the per-channel quantizer)
@@ -107,6 +121,10 @@ struct AttnArgs {
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);
+// RRS: s[k] = max over the rows of |(x R)| over 128-channel segment k (fp32, orthonormal units), for
+// a per-token QuantArgs with heads = 1 and dim a power of two >= 128
+hipError_t launch_rrs_colmax(const QuantArgs& a, float* s, hipStream_t stream);
+hipError_t launch_rrs_gemm(const RrsGemmArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_pchan(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_nsn(const NsnArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_nsn(const DequantArgs& a, hipStream_t stream);

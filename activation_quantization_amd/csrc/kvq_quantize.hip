@@ -243,10 +243,12 @@ __device__ __forceinline__ double wave_exact_y(const unsigned char* tile, int r,
 // near-tie and with a candidate; channels with either are queued in LDS, and each (lane,
 // channel) item is then computed exactly by the whole wave: first the candidates (exact max
 // per lane, reduced over the vector's L lanes), then the near-ties, patched into the staged
-// codes.  tile: the staged input tile, signs applied; queue: 5 R words of LDS.
+// codes.  tile: the staged input tile, signs applied; queue: 5 R words of LDS.  sdiv (RRS
+// activations, else null): lane l's segment is divided by sdiv[l mod L] (the tile starts a vector).
 template <int DT, int R, int LG>
 __device__ __forceinline__ void ptok_fix(const float (&y)[R], float m, float inv_scale, float q, int L, uint64_t ball,
-                                         const unsigned char* tile, unsigned char* stage_codes, uint32_t* queue) {
+                                         const unsigned char* tile, unsigned char* stage_codes, uint32_t* queue,
+                                         const float* sdiv) {
   constexpr int CRB = R / 2;
   const int lane = threadIdx.x;
   const uint64_t gm = (L == 64 ? ~0ull : ((1ull << L) - 1ull)) << (lane & ~(L - 1));
@@ -275,12 +277,21 @@ __device__ __forceinline__ void ptok_fix(const float (&y)[R], float m, float inv
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)queue[5 * k + w + 1]);
     return ((uint64_t)hi << 32) | lo;
   };
+  // the exact value of lane l's channel c (divided by the segment's divisor for RRS activations)
+  auto exact = [&](int l, int c) {
+    double v = wave_exact_y<DT, R, LG>(tile, l, c);
+    if (sdiv) {
+      const float d = sdiv[l & (L - 1)];
+      v = d > 0.f ? v / (double)d : 0.0;
+    }
+    return v;
+  };
   double mxl = 0.0;
   for (int k = 0; k < nq; ++k) {
     const int c = __builtin_amdgcn_readfirstlane((int)queue[5 * k]);
     for (uint64_t cb = entry(k, 3); cb; cb &= cb - 1ull) {
       const int l = __builtin_ctzll(cb);
-      const double v = fabs(wave_exact_y<DT, R, LG>(tile, l, c));
+      const double v = fabs(exact(l, c));
       if (lane == l) mxl = fmax(mxl, v);
     }
   }
@@ -289,7 +300,7 @@ __device__ __forceinline__ void ptok_fix(const float (&y)[R], float m, float inv
     const int c = __builtin_amdgcn_readfirstlane((int)queue[5 * k]);
     for (uint64_t fb = entry(k, 1); fb; fb &= fb - 1ull) {
       const int l = __builtin_ctzll(fb);
-      const double v = wave_exact_y<DT, R, LG>(tile, l, c);
+      const double v = exact(l, c);
       const double mx = __shfl(mxl, l);
       if (lane == l) patch_nibble(stage_codes, l, CRB, c, mx > 0.0 ? exact_code((double)q * v / mx) : 0u);
     }
@@ -387,6 +398,12 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
       widen_stage1<DT, R>(y, wv, nullptr, false);
     }
     fwht_rest<R, LG>(y);
+    if (a.seg_div) {                                    // RRS: the segment's smoothing divisor
+      const float d = a.seg_div[part];
+      const float di = d > 0.f ? 1.f / d : 0.f;
+#pragma unroll
+      for (int i = 0; i < R; ++i) y[i] *= di;
+    }
     float m = 0.f;
     {
       float mm[4] = {0.f, 0.f, 0.f, 0.f};
@@ -408,7 +425,7 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
 
     // rare path: re-decide the near-ties exactly
     const uint64_t ball = __ballot(lane < nvalid && flagged);
-    if (ball) ptok_fix<DT, R, LG>(y, m, inv_scale, a.q, L, ball, tile, stage_codes, queue);
+    if (ball) ptok_fix<DT, R, LG>(y, m, inv_scale, a.q, L, ball, tile, stage_codes, queue, a.seg_div);
     if (part == 0 && lane < nvalid) {
       const float nu = sqrtf(ss);
       const int64_t vh = head_major(a.heads, a.tokens, vec);
@@ -421,6 +438,94 @@ __global__ void __launch_bounds__(64) quant_ptok_kernel(QuantArgs a, int64_t nse
     pvalid = nvalid;
   }
   if (pseg0 >= 0) store_codes(pseg0, pvalid);
+}
+
+// ---------------------------------------------------------------------------------------
+// RRS runtime smoothing scales (Rotated Runtime Smooth analysis, "master equation" and
+// "term-by-term": s_j = the largest |(X R)_tj| over the tokens; Figure 4: one scale per group of
+// 128 channels, the group's largest).  Rows of x are [n, K] with K = L 128: a tile is 64
+// consecutive 128-channel segments (lane l: segment seg0 + l, part l mod L), rotated like the
+// per-token kernel does; the largest |y| of each part is reduced over the tile's lanes and
+// merged into the fp32 bits of smax[part] with an integer atomic max (every value is >= 0).
+template <int DT, int LG>
+__global__ void __launch_bounds__(64) rrs_colmax_kernel(QuantArgs a, uint32_t* smax, int64_t nseg, int64_t ntiles,
+                                                        int lgL) {
+  constexpr int R = 128, ROWB = 2 * R, CPR = ROWB / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[64 * ROWB];
+  const int lane = threadIdx.x, L = 1 << lgL;
+  float mpart = 0.f;                                    // this lane's part, over all its tiles
+  for (int64_t v = blockIdx.x; v < ntiles; v += gridDim.x) {
+    const int64_t seg0 = v * 64;
+    const int nvalid = (int)(nseg - seg0 < 64 ? nseg - seg0 : 64);
+    const unsigned char* xb = (const unsigned char*)a.x + seg0 * ROWB;
+#pragma unroll
+    for (int k = 0; k < CPR; ++k) {
+      const int q = lane + k * 64;
+      const int row = q / CPR, cc = q % CPR;
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (row < nvalid) t = __builtin_nontemporal_load((const u32x4*)(xb + row * ROWB + cc * 16));
+      *(u32x4*)(tile + row * ROWB + swz_chunk(row, cc, ROWB) * 16) = t;
+    }
+    wave_lds_sync();
+    uint32_t wv[R / 2];
+#pragma unroll
+    for (int cc = 0; cc < CPR; ++cc) {
+      const u32x4 t = *(const u32x4*)(tile + lane * ROWB + swz_chunk(lane, cc, ROWB) * 16);
+      wv[4 * cc] = t.x; wv[4 * cc + 1] = t.y; wv[4 * cc + 2] = t.z; wv[4 * cc + 3] = t.w;
+    }
+    wave_lds_sync();
+    const int part = lane & (L - 1);
+    float y[R];
+    if constexpr (LG != 0) {
+      apply_signs_packed<R>(wv, a.signs + part * R);
+      stage1_unsigned<DT, R>(y, wv);
+    } else {
+      widen_stage1<DT, R>(y, wv, nullptr, false);
+    }
+    fwht_rest<R, LG>(y);
+    float mm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < R; ++i) mm[i & 3] = fmaxf(mm[i & 3], fabsf(y[i]));
+    if (lane < nvalid) mpart = fmaxf(mpart, fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3])));
+  }
+  // lanes l and l' hold the same part when l = l' mod L
+  for (int o = L; o < 64; o <<= 1) mpart = fmaxf(mpart, shfl_xor_f(mpart, o));
+  if (lane < L) atomicMax(smax + lane, __builtin_bit_cast(uint32_t, mpart * a.inv_sqrt_n));
+}
+
+__global__ void __launch_bounds__(64) rrs_fill_zero(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
+template <int DT, int LG> struct ColmaxK {
+  static void run(const QuantArgs& a, uint32_t* smax, hipStream_t st, int64_t nseg, int lgL) {
+    const int64_t ntiles = (nseg + 63) / 64;
+    const int64_t grid = persistent_grid(rrs_colmax_kernel<DT, LG>, 64, ntiles);
+    hipLaunchKernelGGL((rrs_colmax_kernel<DT, LG>), dim3((unsigned)grid), dim3(64), 0, st, a, smax, nseg, ntiles, lgL);
+  }
+};
+
+template <int DT>
+static void colmax_dt(const QuantArgs& a, uint32_t* smax, hipStream_t st, int64_t nseg, int lgL) {
+  switch (a.lg_had) {
+    case 0: ColmaxK<DT, 0>::run(a, smax, st, nseg, lgL); break;
+    case 4: ColmaxK<DT, 4>::run(a, smax, st, nseg, lgL); break;
+    case 5: ColmaxK<DT, 5>::run(a, smax, st, nseg, lgL); break;
+    case 6: ColmaxK<DT, 6>::run(a, smax, st, nseg, lgL); break;
+    default: ColmaxK<DT, 7>::run(a, smax, st, nseg, lgL); break;
+  }
+}
+
+hipError_t launch_rrs_colmax(const QuantArgs& a, float* s, hipStream_t st) {
+  int lgL = 0;
+  while ((128 << lgL) < a.dim) ++lgL;
+  const int64_t nseg = a.seqs * a.tokens * (a.dim / 128);
+  uint32_t* smax = reinterpret_cast<uint32_t*>(s);
+  hipLaunchKernelGGL(rrs_fill_zero, dim3(1), dim3(64), 0, st, smax, (int)(a.dim / 128));
+  if (nseg > 0) {
+    if (a.dtype == DT_F16) colmax_dt<DT_F16>(a, smax, st, nseg, lgL); else colmax_dt<DT_BF16>(a, smax, st, nseg, lgL);
+  }
+  return hipGetLastError();
 }
 
 template <int DT, int R, int LG>

@@ -1,0 +1,145 @@
+// RRS INT4 GEMM for gfx950: Y = sum over channel groups of the group's smoothing scale times the
+// group's integer product of INT4 activations and INT4 weights.
+//
+// Method source (page title, section): Rotated Runtime Smooth analysis, "master equation"
+// (Y = sum_j (X'_quant)_j (W'_quant)_j^T s_j), "step-by-step flow" (the per-channel partial products
+// scaled by s_j, then summed) and Figure 4 (channels grouped to the matrix multiplication's block
+// size, one runtime scale per group, applied to the interim result of each block).  With the
+// per-token activation scale a_t and the per-output-channel weight scale b_m,
+//   y[t, m] = a_t b_m sum_g s_g P_g[t, m],   P_g[t, m] = sum_{j in group g} cx[t, j] cw[m, j],
+// each P_g an exact int32 from the int8 matrix cores, scaled and summed in fp32.
+//
+// Work split: a workgroup (4 waves) owns a 128 x 128 output tile, wave (wr, wc) its 64 x 64
+// quarter as 4 x 4 blocks of v_mfma_i32_16x16x64_i8.  Per group of 128 channels the two operand
+// tiles (128 rows x 64 packed bytes each) stream into LDS with global_load_lds, one group ahead
+// (double-buffered); in LDS, 16-byte chunk c of row r sits in slot c ^ ((r / 4) mod 4), so the 16
+// lanes reading 8 bytes of 16 consecutive rows hit 32 different banks.  A lane's 8 packed bytes
+// (16 codes) become 16 int8 operand bytes with four ALU operations per 4 codes: the even and
+// the odd nibbles of each byte go to separate words (the same channel order in both operands, so
+// the dot product is unchanged) and ((d ^ 0x88) - 0x08) ^ 0x80 sign-extends every byte of d at
+// once (no borrow crosses a byte).  The int32 group products are scaled by s_g into fp32
+// accumulators; the epilogue applies a_t b_m.  Rows or columns past n or m read the last row
+// (addresses stay inside the operands) and are not stored.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int TT = 128;        // output tile rows (tokens) and columns (output channels)
+constexpr int KG = 128;        // channels per smoothing group = the K block
+constexpr int GB = KG / 2;     // packed bytes of one row in one group
+
+// 4 code bytes d (each a 4-bit two's-complement value in its low nibble) -> 4 int8
+__device__ __forceinline__ uint32_t sext4(uint32_t d) { return ((d ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u; }
+
+// 16 packed codes (8 bytes) -> the 16 int8 bytes of one MFMA operand lane
+__device__ __forceinline__ i32x4 unpack16(u32x2 p) {
+  return i32x4{(int)sext4(p.x & 0x0F0F0F0Fu), (int)sext4((p.x >> 4) & 0x0F0F0F0Fu), (int)sext4(p.y & 0x0F0F0F0Fu),
+               (int)sext4((p.y >> 4) & 0x0F0F0F0Fu)};
+}
+
+__global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t tiles_m, int64_t ntiles) {
+  __shared__ __attribute__((aligned(16))) unsigned char sa[2][TT * GB];   // activation codes of a group
+  __shared__ __attribute__((aligned(16))) unsigned char sb[2][TT * GB];   // weight codes of a group
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w >> 1, wc = w & 1;
+  const int64_t tile = xcd_tile(blockIdx.x, ntiles);
+  const int64_t tn = tile / tiles_m, tm = tile - tn * tiles_m;
+  const int64_t r0 = tn * TT, c0 = tm * TT;
+  const int64_t kb = a.k / 2;                                   // packed bytes per row
+  const int ng = (int)(a.k / KG);
+
+  // group g's operand tiles into buffer buf: 512 16-byte pieces each, wave w issuing pieces
+  // 64 (2 w + i) + lane (row p / 4, chunk p mod 4 of the row's group slice)
+  auto issue = [&](int g, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = 64 * (2 * w + i) + lane, row = p >> 2, ch = p & 3;
+      const int phys = ch ^ ((row >> 2) & 3);
+      const int64_t xr = r0 + row < a.n ? r0 + row : a.n - 1;
+      const int64_t mr = c0 + row < a.m ? c0 + row : a.m - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(a.x_codes + xr * kb + (int64_t)g * GB + 16 * phys),
+                                       (__attribute__((address_space(3))) void*)(sa[buf] + 1024 * (2 * w + i)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(a.w_codes + mr * kb + (int64_t)g * GB + 16 * phys),
+                                       (__attribute__((address_space(3))) void*)(sb[buf] + 1024 * (2 * w + i)), 16, 0, 0);
+    }
+  };
+  // 8 packed bytes of row r at byte offset o of its group slice (o a multiple of 8)
+  auto frag = [&](const unsigned char* t, int r, int o) {
+    return *(const u32x2*)(t + r * GB + 16 * ((o >> 4) ^ ((r >> 2) & 3)) + (o & 8));
+  };
+
+  f32x4 accf[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) accf[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  for (int g = 0; g < ng; ++g) {
+    const int buf = g & 1;
+    __builtin_amdgcn_s_waitcnt(0x0070);                       // vmcnt(0): group g has landed
+    asm volatile("" ::: "memory");
+    lds_barrier();                                            // and every wave is done with buf ^ 1
+    if (g + 1 < ng) issue(g + 1, buf ^ 1);
+    i32x4 acc[4][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int o = 32 * ks + 8 * (lane >> 4);               // K position of this lane's 16 codes
+      i32x4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = unpack16(frag(sa[buf], 64 * wr + 16 * i + (lane & 15), o));
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) bf[jj] = unpack16(frag(sb[buf], 64 * wc + 16 * jj + (lane & 15), o));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[jj], ks == 0 ? i32x4{0, 0, 0, 0} : acc[i][jj], 0, 0, 0);
+    }
+    const float sg = a.s[g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accf[i][jj][r] = __builtin_fmaf((float)acc[i][jj][r], sg, accf[i][jj][r]);
+  }
+
+  // epilogue: lane (q, j) holds rows 4 q + r, column j of every 16 x 16 block
+  const int q4 = lane >> 4, j = lane & 15;
+  float bsc[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int64_t m = c0 + 64 * wc + 16 * jj + j;
+    bsc[jj] = m < a.m ? f16_to_f32(a.w_scales[m]) : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = r0 + 64 * wr + 16 * i + 4 * q4 + r;
+      if (t >= a.n) continue;
+      const float at = f16_to_f32(a.x_scales[t]);
+      float* yr = a.y + t * a.m;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t m = c0 + 64 * wc + 16 * jj + j;
+        if (m < a.m) yr[m] = accf[i][jj][r] * at * bsc[jj];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rrs_gemm(const RrsGemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = (a.n + TT - 1) / TT, tiles_m = (a.m + TT - 1) / TT;
+  const int64_t ntiles = tiles_n * tiles_m;
+  if (ntiles > 0)
+    hipLaunchKernelGGL(rrs_gemm_kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, tiles_m, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

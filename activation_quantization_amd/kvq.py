@@ -50,6 +50,13 @@ _SIGNATURES = {
     "kvq_dequantize_nsn": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "kvq_score_decode_nsn": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
                                             _P]),
+    "kvq_rrs_smooth_scales": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32,
+                                             _P, _P]),
+    "kvq_rrs_quantize_act": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32,
+                                            _P, ctypes.c_int32, _P, _P, _P]),
+    "kvq_rrs_quantize_weights": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _P,
+                                                ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "kvq_rrs_gemm": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
     "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (ctypes.c_int32, []),
@@ -326,6 +333,57 @@ def attention_decode_stream(d: Desc, tokens_cached: int, q: torch.Tensor, k_cach
                                            workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "kvq_attention_decode_stream")
     return out
+
+
+# ----------------------------------------------------------------------------- RRS INT4 GEMM path
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x and w must be float16 or bfloat16")
+    return DTYPES[t.dtype]
+
+
+def rrs_smooth_scales(x: torch.Tensor, signs: torch.Tensor | None, hadamard: int, out=None, stream=None):
+    """kvq_rrs_smooth_scales: fp32 [k/128], the group maxima of |x R| over all rows of x [n, k]."""
+    n, k = x.shape
+    s = out if out is not None else torch.empty(k // 128, dtype=torch.float32, device=x.device)
+    _need_cuda(x, signs, s)
+    _check(lib().kvq_rrs_smooth_scales(_ptr(x), n, k, _dtype_code(x), _ptr(signs), hadamard, _ptr(s), _stream(stream)),
+           "kvq_rrs_smooth_scales")
+    return s
+
+
+def rrs_quantize_act(x: torch.Tensor, signs: torch.Tensor | None, hadamard: int, scales: torch.Tensor, bits: int = 4,
+                     out=None, stream=None):
+    """kvq_rrs_quantize_act: (codes uint8 [n, k/2], act_scales fp16 [n])."""
+    n, k = x.shape
+    codes, a = out if out is not None else (torch.empty((n, k // 2), dtype=torch.uint8, device=x.device),
+                                            torch.empty(n, dtype=torch.float16, device=x.device))
+    _need_cuda(x, signs, scales, codes, a)
+    _check(lib().kvq_rrs_quantize_act(_ptr(x), n, k, _dtype_code(x), _ptr(signs), hadamard, _ptr(scales), bits,
+                                      _ptr(codes), _ptr(a), _stream(stream)), "kvq_rrs_quantize_act")
+    return codes, a
+
+
+def rrs_quantize_weights(w: torch.Tensor, signs: torch.Tensor | None, hadamard: int, bits: int = 4, out=None,
+                         stream=None):
+    """kvq_rrs_quantize_weights: (codes uint8 [m, k/2], w_scales fp16 [m])."""
+    m, k = w.shape
+    codes, b = out if out is not None else (torch.empty((m, k // 2), dtype=torch.uint8, device=w.device),
+                                            torch.empty(m, dtype=torch.float16, device=w.device))
+    _need_cuda(w, signs, codes, b)
+    _check(lib().kvq_rrs_quantize_weights(_ptr(w), m, k, _dtype_code(w), _ptr(signs), hadamard, bits, _ptr(codes),
+                                          _ptr(b), _stream(stream)), "kvq_rrs_quantize_weights")
+    return codes, b
+
+
+def rrs_gemm(x_codes, act_scales, w_codes, w_scales, scales, out=None, stream=None) -> torch.Tensor:
+    """kvq_rrs_gemm: y fp32 [n, m] = a_t b_m sum_g s_g (integer product of group g)."""
+    n, m, k = x_codes.shape[0], w_codes.shape[0], 2 * x_codes.shape[1]
+    y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=x_codes.device)
+    _need_cuda(x_codes, act_scales, w_codes, w_scales, scales, y)
+    _check(lib().kvq_rrs_gemm(_ptr(x_codes), _ptr(act_scales), n, _ptr(w_codes), _ptr(w_scales), m, k, _ptr(scales),
+                              _ptr(y), _stream(stream)), "kvq_rrs_gemm")
+    return y
 
 
 def token_major(d: Desc, codes=None, norms=None, scales=None):

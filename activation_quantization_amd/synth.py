@@ -189,6 +189,18 @@ def make_q(w: Workload | str, seed: int = 0, seq_range=None) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(q)).to(torch.float16)
 
 
+WEIGHT_STREAM = 1 << 20     # chunk id of the synthetic weight stream (disjoint from the sequences)
+
+
+def make_weights(m: int, k: int, seed: int = 0, dtype: str = "bf16", std: float = 0.02) -> torch.Tensor:
+    """Synthetic linear-layer weights [m, k] (no trained weights are available): N(0, std^2),
+    with every 64th output row scaled x8 (a few large rows, as in trained layers), in dtype."""
+    rng = _rng(seed, 99, 7, WEIGHT_STREAM)
+    wt = rng.standard_normal((m, k), dtype=np.float32) * np.float32(std)
+    wt[::64] *= np.float32(8.0)
+    return torch.from_numpy(wt).to(torch_dtype(dtype))
+
+
 def scaled(w: Workload | str, **changes) -> Workload:
     """The same statistics at another size (e.g. fewer sequences for CPU-sized parity)."""
     if isinstance(w, str):

@@ -222,6 +222,40 @@ kvq_status kvq_score_decode_nsn(const kvq_desc* d, const uint16_t* q, int64_t q_
                                 const uint16_t* s1, const uint16_t* s2, const uint16_t* offsets,
                                 const uint16_t* scales, const int8_t* signs, float* scores, void* stream);
 
+/*
+ * The RRS activation path into an INT4 GEMM (Rotated Runtime Smooth analysis, "master equation",
+ * "term-by-term", "step-by-step flow" and Figure 4).  Activations x [n_tokens, k] and weights
+ * w [m, k] (dtype KVQ_F16 or KVQ_BF16, row-major, 16-byte aligned) are rotated alike, row by row:
+ * x_rot = x R, w_rot = w R with R the block Hadamard of the other calls (signs [k] int8 then the
+ * orthonormal n-point Hadamard, n = hadamard; signs NULL iff hadamard == 0), so x w^T = x_rot w_rot^T.
+ * Channels form groups of 128 (the GEMM's K block); k must be a power of two in [128, 8192] for the
+ * three quantizer calls and a multiple of 128 for the GEMM.
+ *
+ * kvq_rrs_smooth_scales: s[g] = max over all n_tokens rows and the 128 channels of group g of
+ *   |x_rot| (the runtime smoothing scale s_j = the column max, shared by the group), fp32 [k/128]
+ *   (4-byte aligned); n_tokens = 0 gives zeros.
+ * kvq_rrs_quantize_act: u = x_rot / s (each column divided by its group's scale; s = 0 gives 0),
+ *   then per-token symmetric INT-b: a_t = max_j |u_tj| / Q, code = clamp(rne(u / a_t), -Q, Q)
+ *   decided as for the other modes (from the unrounded fp32 a_t; near-ties exact in fp64).
+ *   codes [n_tokens, k/2] packed like the cache codes (16-byte aligned); act_scales fp16 [n_tokens]
+ *   (2-byte aligned) = a_t.  scales is the fp32 array of kvq_rrs_smooth_scales (any positive values
+ *   are accepted).
+ * kvq_rrs_quantize_weights: per-output-channel symmetric INT-b of w_rot, b_m = max_j |w_rot_mj| / Q:
+ *   codes [m, k/2] and w_scales fp16 [m] (the NAIVE per-token quantizer with each row one token).
+ * kvq_rrs_gemm: y[t, m] = a_t b_m sum_g s_g sum_{j in g} cx[t, j] cw[m, j] in fp32 [n_tokens, m]
+ *   (4-byte aligned), from the stored fp16 a_t, b_m and the fp32 s: each group's integer product is
+ *   exact (int8 matrix cores) and scaled by s_g as an interim result, the groups summed in fp32.
+ */
+kvq_status kvq_rrs_smooth_scales(const void* x, int64_t n_tokens, int64_t k, int32_t dtype, const int8_t* signs,
+                                 int32_t hadamard, float* scales, void* stream);
+kvq_status kvq_rrs_quantize_act(const void* x, int64_t n_tokens, int64_t k, int32_t dtype, const int8_t* signs,
+                                int32_t hadamard, const float* scales, int32_t bits, uint8_t* codes,
+                                uint16_t* act_scales, void* stream);
+kvq_status kvq_rrs_quantize_weights(const void* w, int64_t m, int64_t k, int32_t dtype, const int8_t* signs,
+                                    int32_t hadamard, int32_t bits, uint8_t* codes, uint16_t* w_scales, void* stream);
+kvq_status kvq_rrs_gemm(const uint8_t* x_codes, const uint16_t* act_scales, int64_t n_tokens, const uint8_t* w_codes,
+                        const uint16_t* w_scales, int64_t m, int64_t k, const float* scales, float* y, void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_str(kvq_status s);
 
@@ -229,7 +263,7 @@ const char* kvq_status_str(kvq_status s);
 const char* kvq_last_error(void);
 
 /* ABI version: 10000 * major + 100 * minor + patch (1.1: fused decode attention; 1.2: streaming
- * append and attention over a streamed cache; 1.3: the NSN variant). */
+ * append and attention over a streamed cache; 1.3: the NSN variant; 1.4: the RRS INT4 GEMM path). */
 int32_t kvq_version(void);
 
 #ifdef __cplusplus

@@ -227,3 +227,38 @@ def test_nsn_sizes_and_mode_checks():
     # attention and the streaming append do not take the NSN mode
     assert _att(d) == kvq.ERR_UNSUPPORTED
     assert _app(d) == kvq.ERR_UNSUPPORTED
+
+
+def test_rrs_validation_before_any_device_call():
+    L = kvq.lib()
+    F16, BF16 = 0, 1
+    # shapes: k a power of two in [128, 8192] for the quantizers, a multiple of 128 for the GEMM
+    assert L.kvq_rrs_smooth_scales(FAKE, 16, 384, F16, FAKE, 128, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_smooth_scales(FAKE, 16, 64, F16, FAKE, 64, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_smooth_scales(FAKE, -1, 256, F16, FAKE, 128, FAKE, None) == kvq.ERR_SHAPE
+    assert L.kvq_rrs_quantize_act(FAKE, 16, 16384, BF16, FAKE, 128, FAKE, 4, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_quantize_weights(FAKE, 8, 200, F16, FAKE, 128, 4, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_gemm(FAKE, FAKE, 16, FAKE, FAKE, 8, 200, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_gemm(FAKE, FAKE, -1, FAKE, FAKE, 8, 256, FAKE, FAKE, None) == kvq.ERR_SHAPE
+    # bits, dtype, Hadamard size
+    assert L.kvq_rrs_quantize_act(FAKE, 16, 256, F16, FAKE, 128, FAKE, 5, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_quantize_weights(FAKE, 8, 256, 2, FAKE, 128, 4, FAKE, FAKE, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_rrs_smooth_scales(FAKE, 16, 256, F16, FAKE, 256, FAKE, None) == kvq.ERR_UNSUPPORTED
+    # pointers: required buffers, signs iff Hadamard
+    assert L.kvq_rrs_smooth_scales(FAKE, 16, 256, F16, FAKE, 128, None, None) == kvq.ERR_NULL
+    assert L.kvq_rrs_smooth_scales(None, 16, 256, F16, FAKE, 128, FAKE, None) == kvq.ERR_NULL
+    assert L.kvq_rrs_smooth_scales(FAKE, 16, 256, F16, None, 128, FAKE, None) == kvq.ERR_NULL
+    assert L.kvq_rrs_quantize_act(FAKE, 16, 256, F16, FAKE, 0, FAKE, 4, FAKE, FAKE, None) == kvq.ERR_NULL
+    assert L.kvq_rrs_quantize_act(FAKE, 16, 256, F16, FAKE, 128, None, 4, FAKE, FAKE, None) == kvq.ERR_NULL
+    assert L.kvq_rrs_quantize_weights(FAKE, 8, 256, F16, FAKE, 128, 4, FAKE, None, None) == kvq.ERR_NULL
+    assert L.kvq_rrs_gemm(FAKE, FAKE, 16, None, FAKE, 8, 256, FAKE, FAKE, None) == kvq.ERR_NULL
+    # alignment
+    assert L.kvq_rrs_smooth_scales(FAKE + 8, 16, 256, F16, FAKE, 128, FAKE, None) == kvq.ERR_ALIGN
+    assert L.kvq_rrs_smooth_scales(FAKE, 16, 256, F16, FAKE, 128, FAKE + 2, None) == kvq.ERR_ALIGN
+    assert L.kvq_rrs_quantize_act(FAKE, 16, 256, F16, FAKE, 128, FAKE, 4, FAKE + 4, FAKE, None) == kvq.ERR_ALIGN
+    assert L.kvq_rrs_quantize_weights(FAKE, 8, 256, F16, FAKE, 128, 4, FAKE, FAKE + 1, None) == kvq.ERR_ALIGN
+    assert L.kvq_rrs_gemm(FAKE, FAKE, 16, FAKE + 8, FAKE, 8, 256, FAKE, FAKE, None) == kvq.ERR_ALIGN
+    assert L.kvq_rrs_gemm(FAKE, FAKE, 16, FAKE, FAKE, 8, 256, FAKE, FAKE + 2, None) == kvq.ERR_ALIGN
+    # empty work enqueues nothing (the quantizers and the GEMM return before any pointer is used)
+    assert L.kvq_rrs_quantize_act(None, 0, 256, F16, None, 0, None, 4, None, None, None) == kvq.OK
+    assert L.kvq_rrs_gemm(None, None, 0, None, None, 8, 256, None, None, None) == kvq.OK
