@@ -11,14 +11,16 @@
 //
 // Work split: a workgroup (4 waves) owns a 128 x 128 output tile, wave (wr, wc) its 64 x 64
 // quarter as 4 x 4 blocks of v_mfma_i32_16x16x64_i8.  Per group of 128 channels the two operand
-// tiles (128 rows x 64 packed bytes each) stream into LDS with global_load_lds, one group ahead
-// (double-buffered); in LDS, 16-byte chunk c of row r sits in slot c ^ ((r / 4) mod 4), so the 16
+// tiles (128 rows x 64 packed bytes each) stream into a ring of four LDS stages with
+// global_load_lds, three groups ahead of the one computed; in LDS, 16-byte chunk c of row r sits in slot c ^ ((r / 4) mod 4), so the 16
 // lanes reading 8 bytes of 16 consecutive rows hit 32 different banks.  A lane's 8 packed bytes
-// (16 codes) become 16 int8 operand bytes with four ALU operations per 4 codes: the even and
-// the odd nibbles of each byte go to separate words (the same channel order in both operands, so
-// the dot product is unchanged) and ((d ^ 0x88) - 0x08) ^ 0x80 sign-extends every byte of d at
-// once (no borrow crosses a byte).  The int32 group products are scaled by s_g into fp32
-// accumulators; the epilogue applies a_t b_m.  Rows or columns past n or m read the last row
+// (16 codes) become the 16 int8 operand bytes without sign extension: a code byte's high nibble
+// masked in place, w & 0xF0, is 16 times that two's-complement nibble as an int8, and the low
+// nibble shifted up, (w << 4) & 0xF0, likewise; the odd and even codes go to separate words (the
+// same channel order in both operands, so the dot product is unchanged).  Three ALU operations per
+// 8 codes; every product carries 16 x 16 = 256, exact in int32 (|P| <= 128 49 256 < 2^21) and in
+// its fp32 conversion, and removed with the group scale (s_g / 256, a power-of-two factor).  The
+// int32 group products are scaled into fp32 accumulators; the epilogue applies a_t b_m.  Rows or columns past n or m read the last row
 // (addresses stay inside the operands) and are not stored.
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -29,19 +31,18 @@ namespace {
 constexpr int TT = 128;        // output tile rows (tokens) and columns (output channels)
 constexpr int KG = 128;        // channels per smoothing group = the K block
 constexpr int GB = KG / 2;     // packed bytes of one row in one group
+constexpr int NST = 4;         // LDS stages: the group computed and three in flight
+constexpr int LPG = 4;         // global_load_lds instructions per wave and group
 
-// 4 code bytes d (each a 4-bit two's-complement value in its low nibble) -> 4 int8
-__device__ __forceinline__ uint32_t sext4(uint32_t d) { return ((d ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u; }
-
-// 16 packed codes (8 bytes) -> the 16 int8 bytes of one MFMA operand lane
-__device__ __forceinline__ i32x4 unpack16(u32x2 p) {
-  return i32x4{(int)sext4(p.x & 0x0F0F0F0Fu), (int)sext4((p.x >> 4) & 0x0F0F0F0Fu), (int)sext4(p.y & 0x0F0F0F0Fu),
-               (int)sext4((p.y >> 4) & 0x0F0F0F0Fu)};
+// 16 packed codes (8 bytes) -> the 16 int8 bytes of one MFMA operand lane, each 16 times its code
+__device__ __forceinline__ i32x4 unpack16x16(u32x2 p) {
+  return i32x4{(int)((p.x << 4) & 0xF0F0F0F0u), (int)(p.x & 0xF0F0F0F0u), (int)((p.y << 4) & 0xF0F0F0F0u),
+               (int)(p.y & 0xF0F0F0F0u)};
 }
 
 __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t tiles_m, int64_t ntiles) {
-  __shared__ __attribute__((aligned(16))) unsigned char sa[2][TT * GB];   // activation codes of a group
-  __shared__ __attribute__((aligned(16))) unsigned char sb[2][TT * GB];   // weight codes of a group
+  __shared__ __attribute__((aligned(16))) unsigned char sa[NST][TT * GB];   // activation codes of a group
+  __shared__ __attribute__((aligned(16))) unsigned char sb[NST][TT * GB];   // weight codes of a group
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = w >> 1, wc = w & 1;
@@ -52,17 +53,25 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
   const int ng = (int)(a.k / KG);
 
   // group g's operand tiles into buffer buf: 512 16-byte pieces each, wave w issuing pieces
-  // 64 (2 w + i) + lane (row p / 4, chunk p mod 4 of the row's group slice)
+  // 64 (2 w + i) + lane (row p / 4, chunk p mod 4 of the row's group slice); the per-lane source
+  // addresses of group 0, computed once
+  const unsigned char* xsrc[2];
+  const unsigned char* wsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = 64 * (2 * w + i) + lane, row = p >> 2, ch = p & 3;
+    const int phys = ch ^ ((row >> 2) & 3);
+    const int64_t xr = r0 + row < a.n ? r0 + row : a.n - 1;
+    const int64_t mr = c0 + row < a.m ? c0 + row : a.m - 1;
+    xsrc[i] = a.x_codes + xr * kb + 16 * phys;
+    wsrc[i] = a.w_codes + mr * kb + 16 * phys;
+  }
   auto issue = [&](int g, int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int p = 64 * (2 * w + i) + lane, row = p >> 2, ch = p & 3;
-      const int phys = ch ^ ((row >> 2) & 3);
-      const int64_t xr = r0 + row < a.n ? r0 + row : a.n - 1;
-      const int64_t mr = c0 + row < a.m ? c0 + row : a.m - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(a.x_codes + xr * kb + (int64_t)g * GB + 16 * phys),
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + g * GB),
                                        (__attribute__((address_space(3))) void*)(sa[buf] + 1024 * (2 * w + i)), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(a.w_codes + mr * kb + (int64_t)g * GB + 16 * phys),
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + g * GB),
                                        (__attribute__((address_space(3))) void*)(sb[buf] + 1024 * (2 * w + i)), 16, 0, 0);
     }
   };
@@ -77,29 +86,34 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) accf[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
+  for (int p = 0; p < NST - 1 && p < ng; ++p) issue(p, p);
   for (int g = 0; g < ng; ++g) {
-    const int buf = g & 1;
-    __builtin_amdgcn_s_waitcnt(0x0070);                       // vmcnt(0): group g has landed
+    const int buf = g % NST;
+    // group g has landed once at most the loads of the groups issued after it are in flight
+    // (LPG per group; vmcnt(n) immediates: expcnt and lgkmcnt left unconstrained)
+    const int later = ng - 1 - g < NST - 2 ? ng - 1 - g : NST - 2;
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPG));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LPG);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
     asm volatile("" ::: "memory");
-    lds_barrier();                                            // and every wave is done with buf ^ 1
-    if (g + 1 < ng) issue(g + 1, buf ^ 1);
+    lds_barrier();                                            // and every wave is done with group g - 1's stage
+    if (g + NST - 1 < ng) issue(g + NST - 1, (g + NST - 1) % NST);
     i32x4 acc[4][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int o = 32 * ks + 8 * (lane >> 4);               // K position of this lane's 16 codes
       i32x4 af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = unpack16(frag(sa[buf], 64 * wr + 16 * i + (lane & 15), o));
+      for (int i = 0; i < 4; ++i) af[i] = unpack16x16(frag(sa[buf], 64 * wr + 16 * i + (lane & 15), o));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bf[jj] = unpack16(frag(sb[buf], 64 * wc + 16 * jj + (lane & 15), o));
+      for (int jj = 0; jj < 4; ++jj) bf[jj] = unpack16x16(frag(sb[buf], 64 * wc + 16 * jj + (lane & 15), o));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[jj], ks == 0 ? i32x4{0, 0, 0, 0} : acc[i][jj], 0, 0, 0);
     }
-    const float sg = a.s[g];
+    const float sg = a.s[g] * (1.f / 256.f);                  // the operands carry 16 x 16
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -108,26 +122,34 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
         for (int r = 0; r < 4; ++r) accf[i][jj][r] = __builtin_fmaf((float)acc[i][jj][r], sg, accf[i][jj][r]);
   }
 
-  // epilogue: lane (q, j) holds rows 4 q + r, column j of every 16 x 16 block
+  // epilogue: lane (q, j) holds rows 4 q + r, column j of every 16 x 16 block.  Every scale load is
+  // issued first, at clamped indices (a row or column past the end is loaded, not stored), so none
+  // waits for another.
   const int q4 = lane >> 4, j = lane & 15;
-  float bsc[4];
+  uint16_t bh[4], ah[4][4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int64_t m = c0 + 64 * wc + 16 * jj + j;
-    bsc[jj] = m < a.m ? f16_to_f32(a.w_scales[m]) : 0.f;
+    bh[jj] = a.w_scales[m < a.m ? m : a.m - 1];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t t = r0 + 64 * wr + 16 * i + 4 * q4 + r;
-      if (t >= a.n) continue;
-      const float at = f16_to_f32(a.x_scales[t]);
+      ah[i][r] = a.x_scales[t < a.n ? t : a.n - 1];
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = r0 + 64 * wr + 16 * i + 4 * q4 + r;
+      const float at = f16_to_f32(ah[i][r]);
       float* yr = a.y + t * a.m;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int64_t m = c0 + 64 * wc + 16 * jj + j;
-        if (m < a.m) yr[m] = accf[i][jj][r] * at * bsc[jj];
+        if (t < a.n && m < a.m) yr[m] = accf[i][jj][r] * at * f16_to_f32(bh[jj]);
       }
     }
 }

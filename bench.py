@@ -205,6 +205,59 @@ def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup, only=
     return rows
 
 
+RRS_KERNELS = ("rrs_smooth_scales", "rrs_quantize_act", "rrs_quantize_weights", "rrs_gemm")
+INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix throughput, TOP/s
+
+
+def rrs_kernels(torch, kvq, synth, dev, steps, warmup, only=None):
+    """The RRS activation path into an INT4 GEMM on the activation workload: X [8192, 4096] bf16
+    (the activation generator) times synthetic weights W [4096, 4096] bf16, Hadamard 128 with the
+    workload's signs, INT4.  Each kernel timed with HIP events on the stream; the GEMM against the
+    int8 matrix-core peak (2 N M K integer operations), the others against HBM."""
+    wa = synth.WORKLOADS["activation_4096"]
+    n, k = wa.tokens, wa.head_dim
+    m = 4096
+    x = synth.make_x(wa).reshape(n, k).to(dev)
+    w = synth.make_weights(m, k, seed=11, dtype="bf16").to(dev)
+    sg = synth.make_signs(wa).reshape(k).to(dev)
+    stream = torch.cuda.current_stream()
+    s = kvq.rrs_smooth_scales(x, sg, 128, stream=stream)
+    xq = kvq.rrs_quantize_act(x, sg, 128, s, 4, stream=stream)
+    wq = kvq.rrs_quantize_weights(w, sg, 128, 4, stream=stream)
+    y = kvq.rrs_gemm(*xq, *wq, s, stream=stream)
+    calls = {"rrs_smooth_scales": lambda: kvq.rrs_smooth_scales(x, sg, 128, out=s, stream=stream),
+             "rrs_quantize_act": lambda: kvq.rrs_quantize_act(x, sg, 128, s, 4, out=xq, stream=stream),
+             "rrs_quantize_weights": lambda: kvq.rrs_quantize_weights(w, sg, 128, 4, out=wq, stream=stream),
+             "rrs_gemm": lambda: kvq.rrs_gemm(*xq, *wq, s, out=y, stream=stream)}
+    nbytes = {"rrs_smooth_scales": 2 * n * k + k + 4 * (k // 128),
+              "rrs_quantize_act": 2 * n * k + k + 4 * (k // 128) + n * k // 2 + 2 * n,
+              "rrs_quantize_weights": 2 * m * k + k + m * k // 2 + 2 * m,
+              "rrs_gemm": n * k // 2 + 2 * n + m * k // 2 + 2 * m + 4 * (k // 128) + 4 * n * m}
+    if only is not None:
+        calls = {only: calls[only]}
+    rows = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        row = {"us": round(us, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+               "shape": [n, m, k], "in_step": False}
+        if name == "rrs_gemm":
+            tops = 2.0 * n * m * k / (us * 1e-6) / 1e12
+            row.update({"TOP/s": round(tops, 1), "frac_int8_mfma": round(tops / INT8_MFMA_PEAK_TOPS, 4)})
+        rows[name] = row
+    del x, w, y, xq, wq, s
+    return rows
+
+
 def other_configs(torch, kvq, synth, dev, steps, warmup):
     """Quantize and dequantize of the other workloads, each iteration after a 512 MiB read that
     evicts L2 and the MALL (the events bracket the kernel only).  A read, not a write: a written
@@ -249,7 +302,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seqs", type=int, default=10, help="sequences in the oracle baseline sample (0 = skip)")
-    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode") + NSN_KERNELS,
+    ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode") + NSN_KERNELS
+                    + RRS_KERNELS,
                     default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
     ap.add_argument("--other-configs", type=int, default=1,
@@ -283,6 +337,10 @@ def main():
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    if args.only in RRS_KERNELS:
+        kernels = rrs_kernels(torch, kvq, synth, dev, args.steps, args.warmup, only=args.only)
+        print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
+        return
     if args.only in NSN_KERNELS:
         kernels = nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, args.steps, args.warmup, only=args.only)
         print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
@@ -407,6 +465,8 @@ def main():
         del y
         out["other_configs"] = other_configs(torch, kvq, synth, dev, min(args.steps, 10), min(args.warmup, 2))
         y = None
+    # the RRS activation path into an INT4 GEMM (a "next" row, outside the step)
+    out["kernels"].update(rrs_kernels(torch, kvq, synth, dev, min(args.steps, 10), min(args.warmup, 2)))
     if args.cpu_seqs > 0:
         del x, y
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
