@@ -89,6 +89,9 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
   for (int p = 0; p < NST - 1 && p < ng; ++p) issue(p, p);
   for (int g = 0; g < ng; ++g) {
     const int buf = g % NST;
+    // the group's scale (the operands carry 16 x 16), read through the scalar unit: a vector load
+    // here would be waited for with vmcnt(0), which also drains the operand loads in flight
+    const float sg = ((const __attribute__((address_space(4))) float*)a.s)[g] * (1.f / 256.f);
     // group g has landed once at most the loads of the groups issued after it are in flight
     // (LPG per group; vmcnt(n) immediates: expcnt and lgkmcnt left unconstrained)
     const int later = ng - 1 - g < NST - 2 ? ng - 1 - g : NST - 2;
@@ -113,7 +116,6 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
         for (int jj = 0; jj < 4; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[jj], ks == 0 ? i32x4{0, 0, 0, 0} : acc[i][jj], 0, 0, 0);
     }
-    const float sg = a.s[g] * (1.f / 256.f);                  // the operands carry 16 x 16
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
