@@ -58,6 +58,9 @@ def _chain(x, w, sg, had, bits):
     (64, 96, 128, 0, torch.float16, 4),           # one group, no rotation
     (300, 200, 4096, 128, torch.bfloat16, 4),     # the activation width: 32 groups
     (17, 33, 2048, 16, torch.float16, 2),
+    (1, 1, 128, 0, torch.bfloat16, 4),            # one token, one output channel, one group
+    (300, 1, 256, 32, torch.float16, 4),          # a single output channel
+    (33, 40, 8192, 128, torch.float16, 4),        # the widest activations: 64 groups
 ])
 def test_rrs_parity(n, m, k, had, dtype, bits):
     x = _acts(n + k, n, k, dtype)
