@@ -171,8 +171,39 @@ kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs, u
                   "quantize");
 }
 
-kvq_status kvq_append(const kvq_desc* d, int64_t tokens_cached, const void* x_new, int64_t n_new, void* residual,
-                      const int8_t* signs, uint8_t* codes, uint16_t* norms, uint16_t* scales, void* stream) {
+namespace {
+
+// one cache side of a streaming append
+struct AppendSide {
+  const void* x_new;
+  void* residual;
+  const int8_t* signs;
+  uint8_t* codes;
+  uint16_t* norms;
+  uint16_t* scales;
+};
+
+kvq_status check_append_side(const kvq_desc* d, const AppendSide& c, const char* which) {
+  if (!c.x_new || !c.residual || !c.codes || !c.scales)
+    return fail(KVQ_ERR_NULL, "%sx_new, residual, codes and scales are required", which);
+  if (nsep_mode(d->mode) != (c.norms != nullptr))
+    return fail(KVQ_ERR_NULL, nsep_mode(d->mode) ? "%sNSEP modes need a norms buffer" : "%snorms must be NULL without NSEP",
+                which);
+  if ((d->hadamard != 0) != (c.signs != nullptr))
+    return fail(KVQ_ERR_NULL, d->hadamard ? "%shadamard needs a signs buffer" : "%ssigns must be NULL when hadamard == 0",
+                which);
+  if (!aligned(c.x_new, 16) || !aligned(c.residual, 16) || !aligned(c.codes, 16) || (c.signs && !aligned(c.signs, 16)))
+    return fail(KVQ_ERR_ALIGN, "%sx_new, residual, codes and signs must be 16-byte aligned", which);
+  if (!aligned(c.scales, 2) || (c.norms && !aligned(c.norms, 2)))
+    return fail(KVQ_ERR_ALIGN, "%snorms and scales must be 2-byte aligned", which);
+  return KVQ_OK;
+}
+
+// the streaming append of n_new tokens to nc (1 or 2) caches of the same shape: the residual
+// top-ups and the new residuals of all caches are one copy launch each; a block that fills is
+// quantized per cache
+kvq_status append_impl(const kvq_desc* d, int64_t tokens_cached, int64_t n_new, const AppendSide* cs, int nc,
+                       void* stream) {
   kvq_status s = check_desc(d);
   if (s != KVQ_OK) return s;
   if (!pchan_mode(d->mode))
@@ -181,50 +212,69 @@ kvq_status kvq_append(const kvq_desc* d, int64_t tokens_cached, const void* x_ne
     return fail(KVQ_ERR_SHAPE, "tokens_cached %lld + n_new %lld must stay within the capacity tokens_per_seq %lld",
                 (long long)tokens_cached, (long long)n_new, (long long)d->tokens_per_seq);
   if (d->seqs == 0 || n_new == 0) return ok();
-  if (!x_new || !residual || !codes || !scales) return fail(KVQ_ERR_NULL, "x_new, residual, codes and scales are required");
-  if (nsep_mode(d->mode) != (norms != nullptr))
-    return fail(KVQ_ERR_NULL, nsep_mode(d->mode) ? "NSEP modes need a norms buffer" : "norms must be NULL without NSEP");
-  if ((d->hadamard != 0) != (signs != nullptr))
-    return fail(KVQ_ERR_NULL, d->hadamard ? "hadamard needs a signs buffer" : "signs must be NULL when hadamard == 0");
-  if (!aligned(x_new, 16) || !aligned(residual, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)))
-    return fail(KVQ_ERR_ALIGN, "x_new, residual, codes and signs must be 16-byte aligned");
-  if (!aligned(scales, 2) || (norms && !aligned(norms, 2)))
-    return fail(KVQ_ERR_ALIGN, "norms and scales must be 2-byte aligned");
+  for (int i = 0; i < nc; ++i)
+    if ((s = check_append_side(d, cs[i], nc == 1 ? "" : i == 0 ? "K side: " : "V side: ")) != KVQ_OK) return s;
   if ((s = device_ready()) != KVQ_OK) return s;
 
   // the residual holds tokens [whole, tokens_cached) of every sequence in its first slots
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t B = d->block_tokens, S = d->seqs;
   const int64_t rowb = d->heads * d->head_dim * 2;              // bytes per token (fp16 / bf16)
-  const unsigned char* xn = static_cast<const unsigned char*>(x_new);
-  unsigned char* res = static_cast<unsigned char*>(residual);
-  const kvq::QuantArgs base = quant_args(d, nullptr, signs, codes, norms, scales);
-  auto quantize_blocks = [&](const void* x, int64_t tokens, int64_t in_seq_tokens, int64_t out_tok0) {
-    kvq::QuantArgs a = base;
-    a.x = x; a.tokens = tokens; a.in_seq_tokens = in_seq_tokens; a.out_tok0 = out_tok0;
+  auto quantize_blocks = [&](const AppendSide& c, const void* x, int64_t tokens, int64_t in_seq_tokens, int64_t out_tok0) {
+    kvq::QuantArgs a = quant_args(d, x, c.signs, c.codes, c.norms, c.scales);
+    a.tokens = tokens; a.in_seq_tokens = in_seq_tokens; a.out_tok0 = out_tok0;
     return kvq::launch_quantize_pchan(a, st);
   };
+  const void* src[2];
+  void* dst[2];
   int64_t whole = tokens_cached - tokens_cached % B, r = tokens_cached % B, used = 0;
   hipError_t e = hipSuccess;
-  if (r > 0) {                                                   // top up the residual
+  if (r > 0) {                                                   // top up the residuals
     const int64_t k = n_new < B - r ? n_new : B - r;
-    e = kvq::launch_copy_tokens(xn, res + r * rowb, S, k, rowb, n_new, B, st);
+    for (int i = 0; i < nc; ++i) {
+      src[i] = cs[i].x_new;
+      dst[i] = static_cast<unsigned char*>(cs[i].residual) + r * rowb;
+    }
+    e = kvq::launch_copy_tokens(src, dst, nc, S, k, rowb, n_new, B, st);
     used = k;
     r += k;
-    if (e == hipSuccess && r == B) {                             // it filled: quantize it into the cache
-      e = quantize_blocks(res, B, B, whole);
+    if (r == B) {                                                // they filled: quantize them into the caches
+      for (int i = 0; i < nc && e == hipSuccess; ++i) e = quantize_blocks(cs[i], cs[i].residual, B, B, whole);
       whole += B;
       r = 0;
     }
   }
   const int64_t full = (n_new - used) / B * B;                   // whole blocks straight from x_new
-  if (e == hipSuccess && full > 0) {
-    e = quantize_blocks(xn + used * rowb, full, n_new, whole);
+  if (full > 0) {
+    for (int i = 0; i < nc && e == hipSuccess; ++i)
+      e = quantize_blocks(cs[i], static_cast<const unsigned char*>(cs[i].x_new) + used * rowb, full, n_new, whole);
     used += full;
   }
-  if (e == hipSuccess && used < n_new)                           // the tail starts a new residual
-    e = kvq::launch_copy_tokens(xn + used * rowb, res, S, n_new - used, rowb, n_new, B, st);
+  if (e == hipSuccess && used < n_new) {                         // the tails start new residuals
+    for (int i = 0; i < nc; ++i) {
+      src[i] = static_cast<const unsigned char*>(cs[i].x_new) + used * rowb;
+      dst[i] = cs[i].residual;
+    }
+    e = kvq::launch_copy_tokens(src, dst, nc, S, n_new - used, rowb, n_new, B, st);
+  }
   return launched(e, "append");
+}
+
+}  // namespace
+
+kvq_status kvq_append(const kvq_desc* d, int64_t tokens_cached, const void* x_new, int64_t n_new, void* residual,
+                      const int8_t* signs, uint8_t* codes, uint16_t* norms, uint16_t* scales, void* stream) {
+  const AppendSide c{x_new, residual, signs, codes, norms, scales};
+  return append_impl(d, tokens_cached, n_new, &c, 1, stream);
+}
+
+kvq_status kvq_append_kv(const kvq_desc* d, int64_t tokens_cached, int64_t n_new, const void* k_new, void* k_residual,
+                         const int8_t* k_signs, uint8_t* k_codes, uint16_t* k_norms, uint16_t* k_scales,
+                         const void* v_new, void* v_residual, const int8_t* v_signs, uint8_t* v_codes,
+                         uint16_t* v_norms, uint16_t* v_scales, void* stream) {
+  const AppendSide c[2] = {{k_new, k_residual, k_signs, k_codes, k_norms, k_scales},
+                           {v_new, v_residual, v_signs, v_codes, v_norms, v_scales}};
+  return append_impl(d, tokens_cached, n_new, c, 2, stream);
 }
 
 kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_t* norms,
@@ -595,6 +645,6 @@ const char* kvq_status_str(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_version(void) { return 10400; }
+int32_t kvq_version(void) { return 10500; }
 
 }  // extern "C"

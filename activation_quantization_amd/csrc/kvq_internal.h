@@ -131,9 +131,10 @@ hipError_t launch_dequantize_nsn(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize_ptok(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t stream);
-// k tokens of rowb bytes per sequence, token-major runs: src sequences src_seq tokens apart, dst dst_seq
-hipError_t launch_copy_tokens(const void* src, void* dst, int64_t seqs, int64_t k, int64_t rowb, int64_t src_seq,
-                              int64_t dst_seq, hipStream_t stream);
+// k tokens of rowb bytes per sequence, token-major runs: src sequences src_seq tokens apart, dst dst_seq;
+// npairs (1 or 2) such (src[i], dst[i]) copies of the same shape in one launch
+hipError_t launch_copy_tokens(const void* const* src, void* const* dst, int npairs, int64_t seqs, int64_t k, int64_t rowb,
+                              int64_t src_seq, int64_t dst_seq, hipStream_t stream);
 int64_t attention_partials(const AttnArgs& a);   // partials per (sequence, query head)
 
 }  // namespace kvq

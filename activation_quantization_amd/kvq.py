@@ -43,6 +43,8 @@ _SIGNATURES = {
     "kvq_attention_decode": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, ctypes.c_int64, _P]),
     "kvq_append": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
+    "kvq_append_kv": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, _P, _P, _P, _P, _P]),
     "kvq_attention_decode_stream": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, _P, ctypes.c_int64,
                                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                    ctypes.c_int64, _P]),
@@ -306,6 +308,24 @@ def append(d: Desc, tokens_cached: int, x_new: torch.Tensor, residual: torch.Ten
     st = lib().kvq_append(ctypes.byref(d.c()), tokens_cached, _ptr(x_new), n_new, _ptr(residual), _ptr(signs),
                           _ptr(codes), _ptr(norms), _ptr(scales), _stream(stream))
     _check(st, "kvq_append")
+    return tokens_cached + n_new
+
+
+def append_kv(d: Desc, tokens_cached: int, k_new: torch.Tensor, v_new: torch.Tensor, k_residual: torch.Tensor,
+              v_residual: torch.Tensor, k_cache, v_cache, k_signs=None, v_signs=None, stream=None) -> int:
+    """kvq_append_kv: append k_new and v_new [seqs, n_new, heads, head_dim] to the K and V caches
+    and their residuals in one call (the same results as append on each).  Returns tokens_cached +
+    n_new."""
+    kc, kn, ks = k_cache
+    vc, vn, vs = v_cache
+    _need_cuda(k_new, v_new, k_residual, v_residual, k_signs, v_signs, kc, kn, ks, vc, vn, vs)
+    n_new = k_new.shape[1] if k_new.dim() == 4 else 0
+    if tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError(f"k_new {tuple(k_new.shape)} and v_new {tuple(v_new.shape)} differ")
+    st = lib().kvq_append_kv(ctypes.byref(d.c()), tokens_cached, n_new, _ptr(k_new), _ptr(k_residual), _ptr(k_signs),
+                             _ptr(kc), _ptr(kn), _ptr(ks), _ptr(v_new), _ptr(v_residual), _ptr(v_signs), _ptr(vc),
+                             _ptr(vn), _ptr(vs), _stream(stream))
+    _check(st, "kvq_append_kv")
     return tokens_cached + n_new
 
 

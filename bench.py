@@ -115,7 +115,7 @@ def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, str
     """The decode loop's streaming append and attention over the streamed cache.
 
     Every sequence of the K and V caches starts at T - B cached tokens (whole blocks); one decode
-    step appends one new token per sequence to each cache, so a cycle of B steps fills the
+    step appends one new token per sequence to each cache (one kvq_append_kv call), so a cycle of B steps fills the
     full-precision residual and flushes it (the B-th append quantizes it into the cache).  Then
     decode attention over T - 1 tokens: T - B from the packed caches and B - 1 from the residuals.
     New tokens are seeded N(0, 1) fp16 (the append's cost does not depend on their values)."""
@@ -130,8 +130,7 @@ def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, str
     def cycle():
         n = T - B
         for i in range(B):
-            kvq.append(d, n, steps_k[i], rk, k_cache, signs, stream=stream)
-            n = kvq.append(d, n, steps_v[i], rv, v_cache, signs, stream=stream)
+            n = kvq.append_kv(d, n, steps_k[i], steps_v[i], rk, rv, k_cache, v_cache, signs, signs, stream=stream)
         return n
 
     cycle()
@@ -146,7 +145,7 @@ def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, str
     blk_bytes = S * B * w.heads * w.head_dim * 2                 # a full residual
     packed = S * B * w.heads * (w.head_dim // 2 + 2) + S * w.heads * w.head_dim * 2
     cycle_bytes = 2 * (B * 2 * tok_bytes + blk_bytes + packed)   # K and V: copies in/out, one flush
-    rows = {"append_decode_step": {"us_per_step": round(cycle_us / B, 2), "appends_per_step": 2,
+    rows = {"append_decode_step": {"us_per_step": round(cycle_us / B, 2), "appends_per_step": 2, "calls_per_step": 1,
                                    "tokens_per_append": S, "cycle_steps": B, "cycle_us": round(cycle_us, 1),
                                    "cycle_bytes": cycle_bytes,
                                    "GB/s": round(cycle_bytes / (cycle_us * 1e-6) / 1e9, 1)}}

@@ -182,6 +182,21 @@ kvq_status kvq_append(const kvq_desc* d, int64_t tokens_cached, const void* x_ne
                       const int8_t* signs, uint8_t* codes, uint16_t* norms, uint16_t* scales, void* stream);
 
 /*
+ * The streaming append of one decode step's keys and values in one call: exactly kvq_append on the
+ * K cache (k_new, k_residual, k_signs, k_codes, k_norms, k_scales) followed by kvq_append on the V
+ * cache (v_...), both described by d and holding the same tokens_cached, with the same results
+ * (NSNQuant summary, "implementation details": the quantized part plus a full-precision residual,
+ * for each of K and V).  The residual top-ups of both caches are one copy launch, and so are the new
+ * residuals, so a decode step that appends one token enqueues one launch instead of two; a block
+ * that fills is quantized per cache.  Arguments, layouts, alignment and ownership as for kvq_append,
+ * per side; a check that fails names its side ("K side: ", "V side: ") and nothing is enqueued.
+ */
+kvq_status kvq_append_kv(const kvq_desc* d, int64_t tokens_cached, int64_t n_new, const void* k_new, void* k_residual,
+                         const int8_t* k_signs, uint8_t* k_codes, uint16_t* k_norms, uint16_t* k_scales,
+                         const void* v_new, void* v_residual, const int8_t* v_signs, uint8_t* v_codes,
+                         uint16_t* v_norms, uint16_t* v_scales, void* stream);
+
+/*
  * Fused decode attention over a streamed cache: kvq_attention_decode over the first tokens_cached
  * tokens of every sequence, where the whole blocks come from the packed caches (capacity
  * d->tokens_per_seq) and the last tokens_cached mod B tokens from the full-precision residuals that
@@ -263,7 +278,8 @@ const char* kvq_status_str(kvq_status s);
 const char* kvq_last_error(void);
 
 /* ABI version: 10000 * major + 100 * minor + patch (1.1: fused decode attention; 1.2: streaming
- * append and attention over a streamed cache; 1.3: the NSN variant; 1.4: the RRS INT4 GEMM path). */
+ * append and attention over a streamed cache; 1.3: the NSN variant; 1.4: the RRS INT4 GEMM path;
+ * 1.5: the K and V streaming append in one call). */
 int32_t kvq_version(void);
 
 #ifdef __cplusplus

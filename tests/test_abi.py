@@ -176,6 +176,27 @@ def test_append_validation_before_any_device_call():
     assert _app(d, x=FAKE + 2) == kvq.ERR_ALIGN
 
 
+def _appkv(d, tokens_cached=0, n_new=8, **ptr):
+    p = dict(kx=FAKE, kr=FAKE, ksg=FAKE, kc=FAKE, kn=FAKE, ks=FAKE, vx=FAKE, vr=FAKE, vsg=FAKE, vc=FAKE, vn=FAKE, vs=FAKE)
+    p.update(ptr)
+    return kvq.lib().kvq_append_kv(ctypes.byref(d.c()), tokens_cached, n_new, p["kx"], p["kr"], p["ksg"], p["kc"],
+                                   p["kn"], p["ks"], p["vx"], p["vr"], p["vsg"], p["vc"], p["vn"], p["vs"], None)
+
+
+def test_append_kv_validation_before_any_device_call():
+    # every case fails (or returns OK for an empty append) before any device is touched
+    d = kvq.Desc(**GOOD)
+    assert _appkv(kvq.Desc(**{**GOOD, "mode": "nsep", "block_tokens": 0})) == kvq.ERR_UNSUPPORTED
+    assert _appkv(d, tokens_cached=250, n_new=7) == kvq.ERR_SHAPE
+    assert _appkv(d, n_new=0) == kvq.OK
+    for side, name in (("k", b"K side"), ("v", b"V side")):
+        for change, want in ((dict(r=None), kvq.ERR_NULL), (dict(c=None), kvq.ERR_NULL), (dict(n=None), kvq.ERR_NULL),
+                             (dict(sg=None), kvq.ERR_NULL), (dict(x=FAKE + 2), kvq.ERR_ALIGN),
+                             (dict(s=FAKE + 1), kvq.ERR_ALIGN)):
+            assert _appkv(d, **{side + k: v for k, v in change.items()}) == want
+            assert kvq.lib().kvq_last_error().startswith(name)
+
+
 def _atts(d, tokens_cached, q_heads=16, ws_bytes=1 << 30, **ptr):
     p = dict(q=FAKE, kc=FAKE, kn=FAKE, ks=FAKE, ksg=FAKE, kr=FAKE, vc=FAKE, vn=FAKE, vs=FAKE, vsg=FAKE, vr=FAKE,
              out=FAKE, ws=FAKE)

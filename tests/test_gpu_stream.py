@@ -172,3 +172,43 @@ def test_stream_attention_equals_cache_attention_on_whole_blocks():
                                 kvq.quantize(dn, xv.reshape(S * n, H, D).to(DEV), sv), sk, sv)
     torch.cuda.synchronize()
     np.testing.assert_allclose(got.cpu().numpy(), want.cpu().numpy(), rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("S,H,D,B,mode,had,dtype,chunks", CASES)
+def test_append_kv_equals_two_appends(S, H, D, B, mode, had, dtype, chunks):
+    # kvq_append_kv must leave both caches and residuals byte for byte as kvq_append on K and then V
+    n_tot = sum(chunks)
+    C = ((n_tot + B - 1) // B + 1) * B
+    d = kvq.Desc(S, C, H, D, 4, mode, B, had, dtype)
+    xk, sk = _history(S + n_tot, S, n_tot, H, D, dtype)
+    xv, sv = _history(S + n_tot + 1, S, n_tot, H, D, dtype)
+    sgk = sk.to(DEV) if had else None
+    sgv = sv.to(DEV) if had else None
+    ref_k, ref_rk = _append_all(d, xk, chunks, sgk)
+    ref_v, ref_rv = _append_all(d, xv, chunks, sgv)
+
+    caches = []
+    for _ in range(2):
+        cache = kvq.alloc_outputs(d, DEV)
+        for t in cache:
+            if t is not None:
+                t.view(torch.uint8).fill_(0xAB)
+        caches.append(cache)
+    rk, rv = kvq.alloc_residual(d, DEV), kvq.alloc_residual(d, DEV)
+    rk.view(torch.uint8).fill_(0xAB)
+    rv.view(torch.uint8).fill_(0xAB)
+    xkd, xvd = xk.to(DEV), xv.to(DEV)
+    n = 0
+    for c in chunks:
+        n = kvq.append_kv(d, n, xkd[:, n:n + c].contiguous(), xvd[:, n:n + c].contiguous(), rk, rv, caches[0],
+                          caches[1], sgk, sgv)
+    torch.cuda.synchronize()
+    assert n == n_tot
+    for got, want in ((caches[0], ref_k), (caches[1], ref_v)):
+        for g, w in zip(got, want):
+            if w is None:
+                assert g is None
+            else:
+                assert torch.equal(g.view(torch.uint8), w.view(torch.uint8))
+    assert torch.equal(rk.view(torch.uint8), ref_rk.view(torch.uint8))
+    assert torch.equal(rv.view(torch.uint8), ref_rv.view(torch.uint8))
