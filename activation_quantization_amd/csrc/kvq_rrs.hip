@@ -33,6 +33,7 @@ constexpr int KG = 128;        // channels per smoothing group = the K block
 constexpr int GB = KG / 2;     // packed bytes of one row in one group
 constexpr int NST = 4;         // LDS stages: the group computed and three in flight
 constexpr int LPG = 4;         // global_load_lds instructions per wave and group
+constexpr int GM = 8;          // tile rows per group of the tile order
 
 // 16 packed codes (8 bytes) -> the 16 int8 bytes of one MFMA operand lane, each 16 times its code
 __device__ __forceinline__ i32x4 unpack16x16(u32x2 p) {
@@ -46,8 +47,15 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = w >> 1, wc = w & 1;
+  // each XCD takes a contiguous range of tiles, walked in groups of GM tile rows with the row
+  // fastest: the tiles in flight on one XCD share GM row tiles of A and a few column tiles of B,
+  // a working set its L2 holds (row-major order would sweep all of B once per tile row)
   const int64_t tile = xcd_tile(blockIdx.x, ntiles);
-  const int64_t tn = tile / tiles_m, tm = tile - tn * tiles_m;
+  const int64_t tiles_n = ntiles / tiles_m;
+  const int64_t grp = tile / (GM * tiles_m), in_grp = tile - grp * (GM * tiles_m);
+  const int64_t first_n = grp * GM;
+  const int64_t gsz = tiles_n - first_n < GM ? tiles_n - first_n : GM;
+  const int64_t tn = first_n + in_grp % gsz, tm = in_grp / gsz;
   const int64_t r0 = tn * TT, c0 = tm * TT;
   const int64_t kb = a.k / 2;                                   // packed bytes per row
   const int ng = (int)(a.k / KG);
