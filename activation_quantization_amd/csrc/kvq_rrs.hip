@@ -22,6 +22,8 @@
 // its fp32 conversion, and removed with the group scale (s_g / 256, a power-of-two factor).  The
 // int32 group products are scaled into fp32 accumulators; the epilogue applies a_t b_m.  Rows or columns past n or m read the last row
 // (addresses stay inside the operands) and are not stored.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -95,8 +97,10 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
     for (int jj = 0; jj < 4; ++jj) accf[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < NST - 1 && p < ng; ++p) issue(p, p);
-  for (int g = 0; g < ng; ++g) {
-    const int buf = g % NST;
+  // group g in LDS stage BUF = g mod NST; the loop is unrolled over the NST stages so that each
+  // stage's base is an immediate and the fragment addresses stay loop-invariant
+  auto group = [&](const int g, auto stage) {
+    constexpr int BUF = decltype(stage)::value;
     // the group's scale (the operands carry 16 x 16), read through the scalar unit: a vector load
     // here would be waited for with vmcnt(0), which also drains the operand loads in flight
     const float sg = ((const __attribute__((address_space(4))) float*)a.s)[g] * (1.f / 256.f);
@@ -115,9 +119,9 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
       const int o = 32 * ks + 8 * (lane >> 4);               // K position of this lane's 16 codes
       i32x4 af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = unpack16x16(frag(sa[buf], 64 * wr + 16 * i + (lane & 15), o));
+      for (int i = 0; i < 4; ++i) af[i] = unpack16x16(frag(sa[BUF], 64 * wr + 16 * i + (lane & 15), o));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bf[jj] = unpack16x16(frag(sb[buf], 64 * wc + 16 * jj + (lane & 15), o));
+      for (int jj = 0; jj < 4; ++jj) bf[jj] = unpack16x16(frag(sb[BUF], 64 * wc + 16 * jj + (lane & 15), o));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -130,7 +134,14 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) accf[i][jj][r] = __builtin_fmaf((float)acc[i][jj][r], sg, accf[i][jj][r]);
+  };
+  for (int g0 = 0; g0 < ng; g0 += NST) {
+    group(g0, std::integral_constant<int, 0>{});
+    if (g0 + 1 < ng) group(g0 + 1, std::integral_constant<int, 1>{});
+    if (g0 + 2 < ng) group(g0 + 2, std::integral_constant<int, 2>{});
+    if (g0 + 3 < ng) group(g0 + 3, std::integral_constant<int, 3>{});
   }
+  static_assert(NST == 4, "the group loop is unrolled over four stages");
 
   // epilogue: lane (q, j) holds rows 4 q + r, column j of every 16 x 16 block.  Every scale load is
   // issued first, at clamped indices (a row or column past the end is loaded, not stored), so none
