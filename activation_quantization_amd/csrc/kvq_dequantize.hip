@@ -6,8 +6,13 @@
 // "term-by-term" (R^-1 = R^T); NSNQuant summary "implementation details" (a dedicated
 // dequantization kernel that keeps DRAM traffic minimal).
 //
-// Same layout as quantize: a thread owns one row of R channels in VGPRs; codes come in and
-// values go out through XOR-swizzled LDS tiles so both HBM streams are coalesced.
+// Main kernel (dequant_mfma, every per-channel mode and per-token token counts that are a multiple
+// of 64): the inverse rotation is one matrix-core contraction per 16 tokens, codes (exact small
+// integers in fp16) times H diag(scale) built from per-tile fragments; each lane ends with 8
+// consecutive output channels of 4 tokens and the 16 lanes of a row store whole output rows.
+// Fallback (per-token modes with other token counts): one thread owns one row of R channels in
+// VGPRs, with a register butterfly, and codes come in and values go out through XOR-swizzled LDS
+// tiles so both HBM streams are coalesced.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_launch.h"

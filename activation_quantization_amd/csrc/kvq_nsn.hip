@@ -358,11 +358,11 @@ __global__ void __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2)))
           oinv);
     }
 
-    // 6. codes c = rne(fp32(u3 / scale)): g = fp32(u3 (Q / max) + 136.5) from one fp64 fma; g lies on
+    // 6. codes c = rne(u3 / scale): g = fp32(u3 (Q / max) + 136.5) from one fp64 fma; g lies on
     //    the 2^-16 grid of [128, 256), so byte 2 of its bits is floor(u3 / scale + 8.5) unless the
     //    rounding landed g on an integer, which happens exactly for the values within 2^-17 of a
     //    tie (and every value whose fp32 rounding could decide the tie); a lane holding such a value
-    //    (rare) rounds its values again as rint(fp32(u3 / scale))
+    //    (rare) rounds its values again as rint(u3 / scale) in fp64
     constexpr int NG = CQ / 8;                         // packed words per token
     uint32_t pk[4][NG];
     uint32_t fl = 0xffffffffu;
@@ -392,7 +392,7 @@ __global__ void __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2)))
           uint32_t word = 0u;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int c = (int)__builtin_rintf((float)(v[q * CQ + 8 * g + e] * oinv[cpad<D>(cb) + 8 * g + e]));
+            const int c = (int)__builtin_rint(v[q * CQ + 8 * g + e] * oinv[cpad<D>(cb) + 8 * g + e]);
             word |= ((uint32_t)c & 0xFu) << (4 * e);
           }
           pk[q][g] = word;

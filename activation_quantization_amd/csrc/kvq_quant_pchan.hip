@@ -6,13 +6,14 @@
 // (R = (1/sqrt K)[+-1]; runtime scale s_j = max over the tokens of column j); NSNQuant summary
 // "Hadamard transform" (random signs, then the Hadamard matrix).
 //
-// Work split: a tile is (sequence, block of B tokens, head).  Persistent workgroups of four
-// waves walk the tiles of their XCD's range; the rows of the next tile stream into a second
-// LDS buffer (global_load_lds, 1 KiB per wave instruction) while the current tile is
-// computed.  Wave w owns the output channels [w R/4, (w + 1) R/4) of every token of the tile,
-// so the per-channel max over the block, the scales and the exact re-decision of near-ties
-// are all wave-local.  Two workgroup barriers per tile: one publishes the token norms, one
-// hands the assembled code rows over, which the next iteration stores whole.
+// Work split: a tile is (sequence, block of B tokens, head), one tile per workgroup of four
+// waves (tile ids remapped so each XCD walks a contiguous range).  The tile's rows stream into
+// one LDS buffer (global_load_lds, 1 KiB per wave instruction).  Wave w owns the output
+// channels [w R/4, (w + 1) R/4) of every token of the tile, so the per-channel max over the
+// block, the scales and the exact re-decision of near-ties are all wave-local.  Workgroup
+// barriers: the rows have landed; every wave's token norms are published; every wave is done
+// with the staged rows (the buffer then takes the packed code rows); the code rows are
+// complete, and the tile's code block is stored whole.
 //
 // Rotation: Y^T = blockdiag(H_n) diag(sigma) X^T in 16-token sub-tiles with
 // v_mfma_f32_16x16x32 (fp16 or bf16 operands, fp32 accumulation; the +-1 products are exact).
@@ -30,7 +31,8 @@
 // one fma per value, b = bits(u * (Q / m) + 136.5): byte 2 of b is code + 8 (round half up on a
 // 2^-16 grid) and b & 0xffff == 0 marks a near-tie, |v - (k + 1/2)| <= 2^-17.  Near-ties are
 // re-decided exactly: the channel's max is recomputed in fp64 from the tokens whose fp32
-// value is within 2^-12 of it, the flagged values in fp64 too, and the code is rne(fp32(v)).
+// value is within 2^-12 of it, the flagged values in fp64 too, and the code is rne(v) of that
+// fp64 quotient.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -53,8 +55,9 @@ template <int DT> __device__ __forceinline__ double widen64(uint32_t h) {
   return (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
 }
 
+// the rounding decision on the fp64 quotient itself: round half to even
 __device__ __forceinline__ uint32_t exact_nibble(double v) {
-  return (uint32_t)(int)__builtin_rintf((float)v) & 0xfu;
+  return (uint32_t)(int)__builtin_rint(v) & 0xfu;
 }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
@@ -159,11 +162,11 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   //    MFMA-layout reads below are free of bank conflicts); wave 0 also fetches the signs
   {
     const unsigned char* xw = (const unsigned char*)a.x + ((row0 + (B / 4) * w) * a.heads + h) * ROWB;
-    const uint32_t tok_bytes = (uint32_t)(a.heads * ROWB);
+    const int64_t tok_bytes = a.heads * ROWB;               // x bytes from one token to the next (64-bit)
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int p = 64 * k + lane, row = p / CPR, cc = p % CPR;
-      const uint32_t off = (uint32_t)row * tok_bytes + 16u * (uint32_t)(cc ^ ((row + (B / 4) * w) % CPR));
+      const int64_t off = (int64_t)row * tok_bytes + 16 * (cc ^ ((row + (B / 4) * w) % CPR));
       __builtin_amdgcn_global_load_lds((const void*)(xw + off),
                                        (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, 0);
     }
@@ -351,8 +354,9 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
                     ((uint32_t)__builtin_amdgcn_readlane((int)cm, 32) << (2 * LCH)) |
                     ((uint32_t)__builtin_amdgcn_readlane((int)cm, 48) << (3 * LCH));
     const double qd = (double)a.q;
-    // exact u of tile row r for channel c: lane l takes inputs l, l + 64, ...
-    auto exact_u = [&](int r, int c) {
+    // exact unnormalized y (a sum of fp16/bf16 values, exact in fp64) and norm of tile row r for
+    // channel c: lane l takes inputs l, l + 64, ...
+    auto exact_y = [&](int r, int c, double& nu) {
       double y = 0.0, ss = 0.0;
 #pragma unroll
       for (int e = 0; e < R / 64; ++e) {
@@ -363,17 +367,18 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
         const int hv = LG == 0 ? (p == c ? 1 : 0) : hval<LG>(c, p);
         if (hv != 0) y += ((hv < 0) != (LG != 0 && sg[p] < 0)) ? -x : x;
       }
-      y = wave_sum64(y);
-      ss = wave_sum64(ss);
-      const double nu = sqrt(ss);
-      return a.nsep ? (nu > 0.0 ? y / nu : 0.0) : y;
+      nu = sqrt(wave_sum64(ss));
+      return wave_sum64(y);
     };
     // one flagged channel; its lane slot Q is a compile-time constant, so u and iv are plain
-    // registers (pass 0: exact max over the tokens near the fp32 max; pass 1: exact codes of
-    // the flagged values)
+    // registers.  Pass 0 finds the token holding the channel's exact max among those near the
+    // fp32 max and keeps its |y| and norm; pass 1 re-decides the flagged values from
+    // v = Q (y / |y_max|) (nu_max / nu) (the second factor only with NSEP): Q y / |y_max| is one
+    // correctly rounded division of exact values, so an exact tie between tokens of equal norm
+    // stays an exact tie and rounds half to even.
     auto fix_channel = [&](auto qc, int gc, int c) {
       constexpr int Q = decltype(qc)::value;
-      double mm = 0.0;
+      double um = 0.0, ym = 0.0, num = 0.0;
 #pragma unroll 1
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -386,12 +391,15 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
           while (tok) {
             const int jt = __builtin_ctzll(tok);
             tok &= tok - 1ull;
-            const double uex = exact_u(16 * s + jt, c);
+            double nu;
+            const double yex = exact_y(16 * s + jt, c, nu);
             if (pass == 0) {
-              mm = fmax(mm, fabs(uex));
+              const double ua = a.nsep ? (nu > 0.0 ? fabs(yex) / nu : 0.0) : fabs(yex);
+              if (ua > um) { um = ua; ym = fabs(yex); num = nu; }
             } else if (lane == 16 * gc + jt) {
-              const uint32_t nib = mm > 0.0 ? exact_nibble(qd * uex / mm) : 0u;
-              pk[s] = (pk[s] & ~(0xFu << (4 * Q))) | (nib << (4 * Q));
+              double v = 0.0;
+              if (ym > 0.0 && yex != 0.0) v = a.nsep ? (qd * yex / ym) * (num / nu) : qd * yex / ym;
+              pk[s] = (pk[s] & ~(0xFu << (4 * Q))) | (exact_nibble(v) << (4 * Q));
             }
           }
         }

@@ -23,7 +23,7 @@
 //     (|v - (k + 1/2)| <= 2^-17).  The clamp to [-Q, Q] is implied: |u| <= m.
 //   * near-ties (a few per 10^5 codes) are re-decided exactly: the affected channel (per-
 //     channel scales) or vector (per-token scales) is recomputed in fp64 from the input and
-//     the code is rne(fp32(v)), the rounding decision taken on the fp32 value of the quotient.
+//     the code is rne(v) of the fp64 quotient.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_launch.h"
@@ -174,9 +174,9 @@ __device__ __forceinline__ bool quantize_row(const float (&u)[R], InvF inv, uint
 }
 
 // ---------------------------------------------------------------------------------- exact
-// the exact rounding decision: rne of the fp32 value of the fp64 quotient
+// the exact rounding decision: rne of the fp64 quotient
 __device__ __forceinline__ uint32_t exact_code(double v) {
-  return (uint32_t)(int)__builtin_rintf((float)v) & 0xfu;
+  return (uint32_t)(int)__builtin_rint(v) & 0xfu;
 }
 
 // replace the nibble of channel c in row `row` of a staged code tile

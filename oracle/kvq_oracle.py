@@ -35,8 +35,8 @@ Readings where the pages are silent or garbled (each also listed in the design doc):
   R2 "per-channel" = max over the tokens of one B-token block of one sequence; the
      snippet's amax over the last dim is the per-token NSEP mode.
   R3 codes use the unrounded scale and norm; stored values are fp16(nu), fp16(scale).
-  R4 rounding is half-to-even; the rounding decision is taken on the fp32 value of the
-     quotient (the precision the kernels decide in): c = rne(fp32(u / scale)).
+  R4 rounding is half-to-even on the exact (fp64) quotient, as the snippet's .round() does:
+     c = clamp(rne(u / scale), -Q, Q).
   R5 nu = 0 or scale = 0 give codes 0 and stored 0.
   R6 the decode score is the plain dot product q . k^ (no 1/sqrt d, no softmax), with
      k^ the fp64 dequantized key before any output rounding.
@@ -44,6 +44,7 @@ Readings where the pages are silent or garbled (each also listed in the design doc):
 from __future__ import annotations
 
 import dataclasses
+from fractions import Fraction
 
 import numpy as np
 
@@ -109,6 +110,52 @@ def inverse_rotate(y: np.ndarray, signs: np.ndarray, n: int) -> np.ndarray:
     return x * signs.astype(np.float64)[None, :, :]
 
 
+# ----------------------------------------------------------------------------- rounding
+# The code is rne of the exact quotient (the snippet's .round() on the exact value).  fp64 decides
+# it everywhere except within TIE_CHECK of a half-integer, where the few roundings of the fp64
+# steps could put the value on either side of the tie: there the decision is taken exactly, in
+# rational arithmetic, from the squared quotient (norms enter squared, so no square root is needed).
+TIE_CHECK = 2.0 ** -36
+
+
+def _rne_from_square(sign: int, q2: Fraction) -> int:
+    """rne(v) for v = sign * sqrt(q2), exactly: k = floor(|v|), then |v| against k + 1/2."""
+    k = 0
+    while (k + 1) * (k + 1) <= q2:
+        k += 1
+    half2 = Fraction(2 * k + 1, 2) ** 2
+    if q2 > half2 or (q2 == half2 and k % 2 == 1):
+        k += 1
+    return sign * k
+
+
+def _near_tie(v: np.ndarray) -> np.ndarray:
+    a = np.abs(v)
+    return np.abs(a - np.floor(a) - 0.5) < TIE_CHECK
+
+
+def _exact_rotation(x_row: np.ndarray, signs_row, n: int) -> list:
+    """Y = H_n diag(sigma) x of one vector as exact Fractions, without the 1/sqrt(n) factor (it
+    cancels in every quotient); the identity when n == 0."""
+    xs = [Fraction(float(e)) * (int(signs_row[j]) if signs_row is not None else 1) for j, e in enumerate(x_row)]
+    if not n:
+        return xs
+    out = []
+    for c in range(len(xs)):
+        b = (c // n) * n
+        out.append(sum(xs[b + j] if bin((c % n) & j).count("1") % 2 == 0 else -xs[b + j] for j in range(n)))
+    return out
+
+
+def _round_codes(v: np.ndarray, Q: int, exact_square) -> np.ndarray:
+    """c = clamp(rne(v), -Q, Q); near a tie the exact quotient decides: exact_square(index) returns
+    (sign, v^2) as an int and a Fraction."""
+    c = np.rint(v)
+    for idx in zip(*np.nonzero(_near_tie(v) & (v != 0.0))):
+        c[idx] = _rne_from_square(*exact_square(idx))
+    return np.clip(c, -Q, Q).astype(np.int8)
+
+
 # ----------------------------------------------------------------------------- quantize
 @dataclasses.dataclass
 class Quantized:
@@ -151,10 +198,41 @@ def quantize(x: np.ndarray, spec: Spec, signs: np.ndarray | None = None) -> Quan
         scale = np.abs(u).max(axis=-1) / Q
         scale_full = np.broadcast_to(scale[..., None], u.shape)
 
-    # C4: quotient, rounding decision in fp32, half-to-even, clamp
+    # C4: quotient, round half to even, clamp
     safe = np.where(scale_full > 0.0, scale_full, 1.0)
     v = np.where(scale_full > 0.0, u / safe, 0.0)
-    c = np.clip(np.rint(v.astype(np.float32)), -Q, Q).astype(np.int8)
+
+    # the exact quotient near a tie: u / scale = Q u_c / max|u| over the scale's group, where the
+    # rotation's 1/sqrt(n) cancels and, per token, so does the norm; per channel with NSEP,
+    # (u_tc)^2 = Y_tc^2 / ||Y_t||^2
+    rot, nrm2, colmax = {}, {}, {}
+
+    def Y(r, h):
+        if (r, h) not in rot:
+            rot[r, h] = _exact_rotation(x[r, h], None if signs is None else signs[h], spec.hadamard)
+        return rot[r, h]
+
+    def u2(r, h, d):                       # the squared direction entry (up to the common 1/n)
+        if not spec.nsep:
+            return Y(r, h)[d] ** 2
+        if (r, h) not in nrm2:
+            nrm2[r, h] = sum(e * e for e in Y(r, h))
+        return Y(r, h)[d] ** 2 / nrm2[r, h] if nrm2[r, h] else Fraction(0)
+
+    def exact_square(idx):
+        r, h, d = (int(i) for i in idx)
+        if spec.per_channel:
+            first = (r // spec.block_tokens) * spec.block_tokens
+            if (first, h, d) not in colmax:
+                colmax[first, h, d] = max(u2(t, h, d) for t in range(first, first + spec.block_tokens))
+            num, m2 = u2(r, h, d), colmax[first, h, d]
+        else:
+            if (r, h) not in colmax:
+                colmax[r, h] = max(e * e for e in Y(r, h))
+            num, m2 = Y(r, h)[d] ** 2, colmax[r, h]
+        return (1 if Y(r, h)[d] > 0 else -1), Fraction(Q * Q) * num / m2
+
+    c = _round_codes(v, Q, exact_square)
 
     return Quantized(codes=c, packed=pack_nibbles(c), v=v, nu=nu, scale=scale,
                      norms16=None if nu is None else nu.astype(np.float16),
@@ -266,7 +344,7 @@ def nsn_quantize(x: np.ndarray, spec: Spec, signs: np.ndarray | None = None) -> 
     Per (token, head): y = R x (C1), s1 = ||y|| / sqrt(D), u1 = y / s1.  Per (sequence, B-token
     block, head): o = the mean of u1 over the block's tokens.  Per token: u2 = u1 - o,
     s2 = ||u2|| / sqrt(D), u3 = u2 / s2.  Then per-channel absmax / Q of u3 over the block and
-    c = rne(fp32(u3 / scale)) as in quantize().  The rotation is orthonormal and linear, so it
+    c = rne(u3 / scale) as in quantize().  The rotation is orthonormal and linear, so it
     commutes with both normalizations and with the mean; the stored offset is the mean in the
     original domain, R^T o.  s1 = 0 or s2 = 0 give zero directions (and codes 0); s2 counts as 0
     when ||u2|| < 2^-16 sqrt(D) (reading: a token equal to its block's mean up to round-off).
@@ -296,7 +374,10 @@ def nsn_quantize(x: np.ndarray, spec: Spec, signs: np.ndarray | None = None) -> 
     scale_full = np.repeat(scale.reshape(spec.seqs, nb, 1, Hh, D), B, axis=2).reshape(N, Hh, D)
     safe = np.where(scale_full > 0.0, scale_full, 1.0)
     v = np.where(scale_full > 0.0, u3 / safe, 0.0)
-    c = np.clip(np.rint(v.astype(np.float32)), -Q, Q).astype(np.int8)
+    # rne of the fp64 quotient: the shift subtracts a mean of directions scaled by irrational norms,
+    # so there is no rational form of the exact quotient to decide near-ties with; the fp64 value
+    # is within a few ulp of it
+    c = np.clip(np.rint(v), -Q, Q).astype(np.int8)
     o = o.reshape(spec.seqs * nb, Hh, D)
     offset = inverse_rotate(o, signs, spec.hadamard) if spec.hadamard else o
     return NsnQuantized(codes=c, packed=pack_nibbles(c), v=v, s1=s1, s2=s2, offset=offset, scale=scale,
@@ -397,8 +478,8 @@ def rrs_quantize_act(x: np.ndarray, signs: np.ndarray | None, hadamard: int, s: 
                      group: int = RRS_GROUP) -> RrsActivations:
     """X'_quant = Quantize(X R diag(s)^-1) ("master equation"): every column of the rotated
     activations divided by its group's smoothing scale, then symmetric per-token INT-b with
-    round-to-nearest (the per-token absmax reading of the activation quantizer), the rounding
-    decision on the fp32 quotient as for the cache modes."""
+    round-to-nearest (the per-token absmax reading of the activation quantizer), rounding the
+    quotient half to even as for the cache modes."""
     x = np.asarray(x, dtype=np.float64)
     N, K = x.shape
     Q = qmax(bits)
@@ -408,7 +489,22 @@ def rrs_quantize_act(x: np.ndarray, signs: np.ndarray | None, hadamard: int, s: 
     a = np.abs(u).max(axis=1) / Q if K else np.zeros(N)
     safe = np.where(a > 0.0, a, 1.0)
     v = np.where(a[:, None] > 0.0, u / safe[:, None], 0.0)
-    c = np.clip(np.rint(v.astype(np.float32)), -Q, Q).astype(np.int8)
+    # near a tie, the exact quotient: Q (Y_c / s_g(c)) / max_c' |Y_c' / s_g(c')| (1/sqrt(n) cancels)
+    sfr = [Fraction(float(e)) for e in np.asarray(s, dtype=np.float64)]
+    rows = {}
+
+    def smoothed(t):
+        if t not in rows:
+            yv = _exact_rotation(x[t], signs, hadamard)
+            rows[t] = [yv[j] / sfr[j // group] if sfr[j // group] else Fraction(0) for j in range(K)]
+        return rows[t]
+
+    def exact_square(idx):
+        t, j = (int(i) for i in idx)
+        z = smoothed(t)
+        return (1 if z[j] > 0 else -1), Fraction(Q * Q) * z[j] ** 2 / max(e * e for e in z)
+
+    c = _round_codes(v, Q, exact_square)
     return RrsActivations(codes=c, packed=pack_nibbles(c), v=v, scale=a, scales16=a.astype(np.float16))
 
 

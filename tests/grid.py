@@ -82,3 +82,59 @@ def all_ties(had, seed=0, T=128, H=2, D=64, extra_max=0):
         x = (y.reshape(T, H, D // had, had) @ Hm.T / np.sqrt(had)).reshape(T, H, D) * signs[None]
     assert np.all(x.astype(np.float16).astype(np.float64) == x)
     return x, signs, want
+
+
+# Near-tie inputs: with a 16-point rotation, a block x = (a, b, c, 0, ...) of one token rotates to
+# y_i = (a + H[i,1] b + H[i,2] c) / 4, and a tiny c (the smallest fp16 subnormal, 2^-24) moves every
+# quotient off its tie by far less than an fp32 ulp of it.  Per bit width, (a, b) makes channel 1's
+# quotient Q (a - b + c) / (a + b + c) a hair above a tie that half-to-even rounds down
+# (2.5 at INT4 and INT3, 0.5 at 2 bits) and channel 3's, Q (a - b - c) / (a + b + c), a hair below
+# it.  Decided on the fp64 quotient the two round apart; decided on its fp32 value both would
+# become the tie itself.
+NEAR_TIE_AB = {4: (9.5, 4.5), 3: (5.5, 0.5), 2: (24.0, 8.0)}
+NEAR_TIE_C = 2.0 ** -24
+
+
+def _hadamard_entry(i, j):
+    return -1 if bin(i & j).count("1") % 2 else 1
+
+
+def _rne(fr):
+    """Round a Fraction half to even (exact)."""
+    import fractions
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > fractions.Fraction(1, 2) or (rem == fractions.Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def near_ties(bits, per_channel, D=64, B=64):
+    """x float64 [B, 1, D] (one head, one sequence of B tokens), signs int8 [1, D] (all +1) and the
+    expected codes int8 [B, 1, D], derived in exact rational arithmetic (no oracle, no floating
+    point).  Per-token modes: token 2k + s is (+-a, +-b, c) (s picks the sign of b, k the overall
+    sign) in the first 16-channel block and zero elsewhere.  Per-channel modes: the same four
+    tokens 0..3 and zero tokens after them, so channel i's block max is the larger of its two
+    magnitudes (a + b +- c)."""
+    import fractions
+    F = fractions.Fraction
+    Q = (1 << (bits - 1)) - 1
+    a, b = NEAR_TIE_AB[bits]
+    c = NEAR_TIE_C
+    T = B
+    x = np.zeros((T, 1, D))
+    rows = 4 if per_channel else T
+    for t in range(rows):
+        sb = 1.0 if (t % 2 == 0) else -1.0
+        sg = 1.0 if ((t // 2) % 2 == 0) else -1.0
+        x[t, 0, :3] = sg * np.array([a, sb * b, c])
+    assert np.all(x.astype(np.float16).astype(np.float64) == x)
+    # exact rotation of every token (the 1/4 cancels in every quotient; kept for clarity)
+    y = [[sum(_hadamard_entry(i % 16, j % 16) * F(x[t, 0, j]) for j in range(16 * (i // 16), 16 * (i // 16) + 16)) / 4
+          for i in range(D)] for t in range(T)]
+    want = np.zeros((T, 1, D), dtype=np.int8)
+    for t in range(T):
+        for i in range(D):
+            m = max(abs(y[s][i]) for s in range(T)) if per_channel else max(abs(v) for v in y[t])
+            want[t, 0, i] = 0 if m == 0 else max(-Q, min(Q, _rne(Q * y[t][i] / m)))
+    return x, np.ones((1, D), dtype=np.int8), want

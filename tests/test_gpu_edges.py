@@ -144,7 +144,7 @@ def test_exact_ties_are_rounded_half_even(mode, had):
     torch.cuda.synchronize()
     got = oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy())
     np.testing.assert_array_equal(got, want)
-    # and the oracle agrees (its own decision in fp32 of the fp64 quotient)
+    # and the oracle agrees (rne of the exact quotient)
     sp = oracle.Spec(1, 128, 2, 64, 4, mode, d.block_tokens if "pchan" in mode else 0, had)
     np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
 
@@ -164,3 +164,19 @@ def test_exact_ties_wide_per_token(mode, dim, had, extra_max):
     np.testing.assert_array_equal(got, want)
     sp = oracle.Spec(1, 96, 2, dim, 4, mode, 0, had)
     np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_near_ties_follow_the_exact_quotient(mode, bits, dtype):
+    # quotients a hair (~2^-26) above and below a tie that half-to-even rounds down: the codes are
+    # the rounding of the exact quotient (rational arithmetic, tests/grid.py), with no tie band;
+    # a decision on the fp32 quotient would give the tie's even neighbour for both
+    per_channel = "pchan" in mode
+    x64, signs, want = grid.near_ties(bits, per_channel)
+    d = kvq.Desc(1, 64, 1, 64, bits, mode, 64 if per_channel else 0, 16, dtype)
+    codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).to(dtype).to(DEV), torch.from_numpy(signs).to(DEV))
+    torch.cuda.synchronize()
+    got = oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy())
+    np.testing.assert_array_equal(got, want)

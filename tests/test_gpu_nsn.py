@@ -105,3 +105,24 @@ def test_plain_entry_points_refuse_nsn():
     x = torch.zeros((128, 1, 128), dtype=torch.float16, device=DEV)
     with pytest.raises(kvq.KvqError):
         kvq.quantize(d, x, None, out=kvq.alloc_outputs(kvq.Desc(1, 128, 1, 128, 4, "pchan", 128, 0), DEV))
+
+
+@pytest.mark.parametrize("factor", [15, 17])
+def test_second_norm_threshold(factor):
+    # tokens 1 .. 63 of a 64-token block differ from the block mean of the directions by
+    # ||u2|| = eps / 64 (to O(eps^2)); eps = 15 or 17 2^-11 puts that just below or just above the
+    # zero threshold 2^-16 sqrt(64): s2 = 0 and codes 0 below it, s2 = ||u2|| / 8 above it
+    from tests.test_oracle_nsn import near_constant_block
+    x64 = near_constant_block(factor * 2.0 ** -11, b=64, d=64)
+    d = kvq.Desc(1, 64, 1, 64, 4, "nsn_pchan", 64, 0, torch.float16)
+    x = torch.from_numpy(x64).half()
+    assert torch.equal(x.double(), torch.from_numpy(x64))
+    _run(d, x, None)
+    codes, s1, s2, offsets, scales = kvq.quantize_nsn(d, x.to(DEV), None)
+    g2 = s2.cpu().numpy().reshape(64).astype(np.float64)
+    c = oracle.unpack_nibbles(codes.cpu().numpy()).reshape(64, 64)
+    if factor == 15:
+        assert np.all(g2[1:] == 0.0) and not np.any(c[1:])
+    else:
+        np.testing.assert_allclose(g2[1:], factor * 2.0 ** -11 / 64 / 8, rtol=1e-3)
+        assert np.all(np.abs(c[1:]).max(axis=-1) == 7)

@@ -121,14 +121,18 @@ def test_activation_4096_full():
     print(stats)
 
 
-def _sampled_tiles(d: kvq.Desc, x_cpu, signs_cpu, codes, norms, scales, n_tiles, seed):
-    """Oracle on randomly chosen (seq, block, head) tiles of a full-size GPU run."""
+def _sampled_tiles(d: kvq.Desc, x_cpu, signs_cpu, codes, norms, scales, n_tiles, seed, y=None):
+    """Oracle on chosen (seq, block, head) tiles of a full-size GPU run: the first and the last
+    tile (the highest element offsets) and n_tiles random ones.  y: the GPU's dequantized output
+    of the whole tensor (x's layout and dtype), compared on the same tiles with the oracle's
+    dequantization of the GPU's own codes, norms and scales."""
     rng = np.random.default_rng(seed)
     B, nb = d.block_tokens, d.tokens_per_seq // d.block_tokens
     gc, gn, gs = (t.cpu() for t in kvq.token_major(d, codes, norms, scales))
     flips, checked = 0, 0
-    for _ in range(n_tiles):
-        s, b, h = int(rng.integers(d.seqs)), int(rng.integers(nb)), int(rng.integers(d.heads))
+    tiles = [(0, 0, 0), (d.seqs - 1, nb - 1, d.heads - 1)]
+    tiles += [(int(rng.integers(d.seqs)), int(rng.integers(nb)), int(rng.integers(d.heads))) for _ in range(n_tiles)]
+    for s, b, h in tiles:
         r0 = s * d.tokens_per_seq + b * B
         xt = x_cpu[r0:r0 + B, h:h + 1].double().numpy()
         sp = oracle.Spec(1, B, 1, d.head_dim, d.bits, d.mode, B, d.hadamard)
@@ -140,8 +144,13 @@ def _sampled_tiles(d: kvq.Desc, x_cpu, signs_cpu, codes, norms, scales, n_tiles,
         checked += st["codes"]
         parity.check_rel_f16(gn[r0:r0 + B, h:h + 1].numpy(), ref.nu, "norms")
         parity.check_rel_f16(gs[s * nb + b, h:h + 1].numpy()[None], ref.scale, "scales")
-        dq = oracle.dequantize(c, gn[r0:r0 + B, h:h + 1].numpy(), gs[s * nb + b, h:h + 1].numpy()[None], sp, sg)
-        assert np.all(np.isfinite(dq))
+        if y is not None:
+            dq = oracle.dequantize(c, gn[r0:r0 + B, h:h + 1].numpy(), gs[s * nb + b, h:h + 1].numpy()[None], sp, sg)
+            yt = y[r0:r0 + B, h:h + 1].cpu()
+            if yt.dtype == torch.float32:
+                parity.check_dequant(yt.numpy(), dq)
+            else:
+                parity.check_dequant_lowp(yt, dq, "f16" if yt.dtype == torch.float16 else "bf16")
     assert flips <= parity.tie_budget(checked, d.rows * d.heads * d.head_dim)
     return checked, flips
 
@@ -150,9 +159,13 @@ def test_batched_hadamard_full_sampled():
     w = synth.WORKLOADS["batched_hadamard"]
     d = desc_for(w)
     x_cpu, signs = synth.make_x(w), synth.make_signs(w)
-    codes, norms, scales = kvq.quantize(d, x_cpu.to(DEV), signs.to(DEV))
+    sg = signs.to(DEV)
+    codes, norms, scales = kvq.quantize(d, x_cpu.to(DEV), sg)
+    y16 = kvq.dequantize(d, codes, norms, scales, sg, torch.float16)
+    y32 = kvq.dequantize(d, codes, norms, scales, sg, torch.float32)
     torch.cuda.synchronize()
-    print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 48, seed=3))
+    print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 48, seed=3, y=y16))
+    print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 16, seed=4, y=y32))
 
 
 # ----------------------------------------------------------------------------- decode score
@@ -201,7 +214,11 @@ def test_long_context_decode_full_sampled():
     sc = kvq.score_decode(d, q_cpu.to(DEV), codes, norms, scales, sg)
     torch.cuda.synchronize()
     del x
-    print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 64, seed=5))
+    # the dequantized cache in fp16, as the step writes it (2^31 elements: 64-bit offsets)
+    y = kvq.dequantize(d, codes, norms, scales, sg, torch.float16)
+    torch.cuda.synchronize()
+    print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 64, seed=5, y=y))
+    del y
     rng = np.random.default_rng(9)
     pairs = [(int(rng.integers(w.seqs)), int(rng.integers(w.heads))) for _ in range(3)] + [(w.seqs - 1, w.heads - 1)]
     print("worst score error / tolerance", _score_check(d, q_cpu, codes, norms, scales, signs, sc, pairs))

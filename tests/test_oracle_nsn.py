@@ -121,3 +121,29 @@ def test_score_folds_the_byproducts():
                 folded[s, hq, t] = (s1[s, t, h] * s2[s, t, h] * np.dot(rqv, c[s, t, h] * sc[s, b, h])
                                     + s1[s, t, h] * np.dot(qq[s, hq], off[s, b, h]))
     np.testing.assert_allclose(folded, direct, rtol=1e-10, atol=1e-10 * np.abs(direct).max())
+
+
+def near_constant_block(eps, b=B, d=D):
+    """b tokens (8, 0, ...) except token 0, (8, eps, 0, ...): every token but the first differs
+    from the block mean of the directions by about eps / b (norm), token 0 by (b - 1) eps / b."""
+    x = np.zeros((b, 1, d))
+    x[:, 0, 0] = 8.0
+    x[0, 0, 1] = eps
+    return x
+
+
+def test_second_norm_threshold_position():
+    # the second normalization counts as zero below ||u2|| = 2^-16 sqrt(D) = 2^-13 (D = 64); tokens
+    # 1 .. B-1 have ||u2|| = eps / 16 up to O(eps^2), so eps = 15 2^-13 puts them just below it and
+    # eps = 17 2^-13 just above
+    sp = oracle.Spec(1, B, 1, D, 4, "nsn_pchan", B, 0)
+    below = oracle.nsn_quantize(near_constant_block(15 * 2.0 ** -13), sp)
+    assert np.all(below.s2[1:] == 0.0) and np.all(below.codes[1:] == 0)
+    assert below.s2[0, 0] > 0.0
+    above = oracle.nsn_quantize(near_constant_block(17 * 2.0 ** -13), sp)
+    # s2 = ||u2|| / sqrt(D) = (eps / 16) / 8 to within O(eps^2)
+    np.testing.assert_allclose(above.s2[1:, 0], 17 * 2.0 ** -13 / 16 / 8, rtol=1e-5)
+    assert np.all(np.abs(above.codes[1:]).max(axis=-1) == 7)
+    # below the threshold x^ = s1 * offset: the block mean of the directions, scaled back
+    xh = oracle.nsn_dequantize(below.packed, below.s1_16, below.s2_16, below.offset16, below.scales16, sp)
+    np.testing.assert_allclose(xh[1:, 0, 0], 8.0, rtol=1e-3)

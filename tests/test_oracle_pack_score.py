@@ -107,3 +107,27 @@ def test_ordering_qwen_like_non_outlier_channels(bits):
     print({m: {k: round(v, 4) for k, v in e.items()} for m, e in r.items()})
     best = r["nsep_pchan"]["non_outlier"]
     assert all(best < r[m]["non_outlier"] for m in ("naive", "nsep", "pchan"))
+
+
+def test_reconstruction_errors_hand_computed():
+    # x [2 tokens, 2 heads, 4 channels] with one nonzero entry per (token, head), and an error in
+    # two places; every expected value worked out by hand
+    x = np.zeros((2, 2, 4))
+    x[0, 0, 0], x[0, 1, 1], x[1, 0, 2], x[1, 1, 3] = 1.0, 2.0, 3.0, 4.0
+    e = np.zeros_like(x)
+    e[0, 0, 0], e[1, 1, 3] = 1.0, 2.0
+    mask = np.zeros((2, 4), bool)
+    mask[0, 0] = True                                   # head 0, channel 0 is the "outlier"
+    r = oracle.reconstruction_errors(x, x + e, mask)
+    # ||e|| / ||x|| = sqrt(1 + 4) / sqrt(1 + 4 + 9 + 16)
+    assert r["frobenius"] == pytest.approx(np.sqrt(5.0 / 30.0), rel=1e-15)
+    # per (token, head) vector: 1/1, 0/2, 0/3, 2/4 -> mean 0.375
+    assert r["per_token"] == pytest.approx(0.375, rel=1e-15)
+    # per (head, channel) over the tokens: (0,0) 1/1 and (1,3) 2/4; the other six are 0 -> 1.5 / 8
+    assert r["per_channel"] == pytest.approx(0.1875, rel=1e-15)
+    # outside (head 0, channel 0): error 2 at (1,1,3); x entries 2, 3, 4 -> 2 / sqrt(29)
+    assert r["non_outlier"] == pytest.approx(2.0 / np.sqrt(29.0), rel=1e-15)
+    # the mask is per (head, channel): masking head 1 channel 3 instead leaves only the first error
+    mask2 = np.zeros((2, 4), bool)
+    mask2[1, 3] = True
+    assert oracle.reconstruction_errors(x, x + e, mask2)["non_outlier"] == pytest.approx(1.0 / np.sqrt(14.0), rel=1e-15)

@@ -143,3 +143,25 @@ def test_all_ties_round_half_even(mode, had):
     x, signs, want = grid.all_ties(had)
     sp = Spec(1, 128, 2, 64, 4, mode, 64 if "pchan" in mode else 0, had)
     np.testing.assert_array_equal(oracle.quantize(x, sp, signs).codes, want)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_near_ties_round_the_exact_quotient(bits, mode):
+    # quotients within ~2^-26 of a tie (2.5 or 0.5), above and below it: the code is the half-even
+    # rounding of the exact quotient (rational arithmetic in tests/grid.py), so the tie's two
+    # neighbours are told apart; a decision on the fp32 quotient would round both to the tie
+    per_channel = "pchan" in mode
+    x, signs, want = grid.near_ties(bits, per_channel)
+    sp = Spec(1, 64, 1, 64, bits, mode, 64 if per_channel else 0, 16)
+    q = oracle.quantize(x, sp, signs)
+    np.testing.assert_array_equal(q.codes, want)
+    tie = 0.5 if bits == 2 else 2.5
+    up = 1 if bits == 2 else 3
+    # channel 1 of token 0 lies just above the tie, channel 3 just below; token 2 is the negation
+    # of token 0
+    assert want[0, 0, 1] == up and want[0, 0, 3] == up - 1
+    assert 0 < q.v[0, 0, 1] - tie < 2.0 ** -24 and 0 < tie - q.v[0, 0, 3] < 2.0 ** -24
+    assert want[2, 0, 1] == -up and q.codes[2, 0, 1] == -up
+    # an fp32 decision would have returned the tie's even neighbour for both channels
+    assert np.rint(np.float32(q.v[0, 0, 1])) == up - 1
