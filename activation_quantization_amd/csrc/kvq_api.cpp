@@ -9,6 +9,8 @@
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 
+static_assert(KVQ_ATTENTION_SCRATCH_BYTES == kvq::ATTENTION_SCRATCH_BYTES, "scratch size in the header");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -473,10 +475,12 @@ kvq_status attention_impl(const kvq_desc* d, int64_t tokens_cached, const uint16
                           const uint8_t* k_codes, const uint16_t* k_norms, const uint16_t* k_scales,
                           const int8_t* k_signs, const void* k_res, const uint8_t* v_codes, const uint16_t* v_norms,
                           const uint16_t* v_scales, const int8_t* v_signs, const void* v_res, float* out,
-                          void* workspace, int64_t workspace_bytes, void* stream, const char* what) {
+                          void* workspace, int64_t workspace_bytes, void* stream, const char* what,
+                          bool static_scratch = false) {
   kvq_status s;
-  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out || !workspace)
-    return fail(KVQ_ERR_NULL, "q, codes, scales, out and workspace are required");
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out)
+    return fail(KVQ_ERR_NULL, "q, codes, scales and out are required");
+  if (!static_scratch && !workspace) return fail(KVQ_ERR_NULL, "workspace is required");
   const int64_t nres = tokens_cached % d->block_tokens;
   if (nres > 0 && (!k_res || !v_res)) return fail(KVQ_ERR_NULL, "a partly filled block needs both residual buffers");
   if ((k_res && !aligned(k_res, 2)) || (v_res && !aligned(v_res, 2)))
@@ -490,12 +494,24 @@ kvq_status attention_impl(const kvq_desc* d, int64_t tokens_cached, const uint16
       (k_signs && !aligned(k_signs, 16)) || (v_signs && !aligned(v_signs, 16)))
     return fail(KVQ_ERR_ALIGN, "codes, scales and signs must be 16-byte aligned");
   if (!aligned(q, 2) || (k_norms && !aligned(k_norms, 2)) || (v_norms && !aligned(v_norms, 2)) || !aligned(out, 4) ||
-      !aligned(workspace, 4))
+      (!static_scratch && !aligned(workspace, 4)))
     return fail(KVQ_ERR_ALIGN, "q and norms must be 2-byte, out and workspace 4-byte aligned");
   const int64_t need = kvq_attention_workspace_bytes(d, q_heads);
-  if (workspace_bytes < need)
+  if (static_scratch) {
+    if (need > kvq::ATTENTION_SCRATCH_BYTES)
+      return fail(KVQ_ERR_UNSUPPORTED,
+                  "%s: the partials need %lld bytes, more than the %lld-byte static scratch; use "
+                  "kvq_attention_decode with a workspace", what, (long long)need, (long long)kvq::ATTENTION_SCRATCH_BYTES);
+  } else if (workspace_bytes < need) {
     return fail(KVQ_ERR_SHAPE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+  }
   if ((s = device_ready()) != KVQ_OK) return s;
+  if (static_scratch) {
+    float* p = nullptr;
+    const hipError_t e = kvq::attention_scratch(&p);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: static scratch lookup failed: %s", what, hipGetErrorString(e));
+    workspace = p;
+  }
 
   kvq::AttnArgs a = attn_args(d, q_heads);
   a.tokens = tokens_cached - nres;
@@ -518,6 +534,17 @@ kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_
   if (d->seqs == 0) return ok();
   return attention_impl(d, d->tokens_per_seq, q, q_heads, k_codes, k_norms, k_scales, k_signs, nullptr, v_codes,
                         v_norms, v_scales, v_signs, nullptr, out, workspace, workspace_bytes, stream, "attention_decode");
+}
+
+kvq_status kvq_attention_decode_noalloc(const kvq_desc* d, const uint16_t* q, int64_t q_heads, const uint8_t* k_codes,
+                                        const uint16_t* k_norms, const uint16_t* k_scales, const int8_t* k_signs,
+                                        const uint8_t* v_codes, const uint16_t* v_norms, const uint16_t* v_scales,
+                                        const int8_t* v_signs, float* out, void* stream) {
+  kvq_status s = check_attention(d, q_heads);
+  if (s != KVQ_OK) return s;
+  if (d->seqs == 0) return ok();
+  return attention_impl(d, d->tokens_per_seq, q, q_heads, k_codes, k_norms, k_scales, k_signs, nullptr, v_codes,
+                        v_norms, v_scales, v_signs, nullptr, out, nullptr, 0, stream, "attention_decode_noalloc", true);
 }
 
 kvq_status kvq_attention_decode_stream(const kvq_desc* d, int64_t tokens_cached, const uint16_t* q, int64_t q_heads,

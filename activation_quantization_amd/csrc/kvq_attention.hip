@@ -22,6 +22,7 @@
 // exact integer dot products (v_dot2_u32_u16).  The four waves' (m, l, partial sum) are merged in LDS and the
 // workgroup writes one partial per query head to the caller's workspace.  Pass 2 merges the
 // partials of a head (log-sum-exp weights), rotates the result back and writes it.
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -466,6 +467,32 @@ __global__ void __launch_bounds__(128) attn_combine(AttnArgs a, int64_t NP) {
 }
 
 }  // namespace
+
+// Decode attention's per-workgroup partials for callers that cannot allocate (the no-alloc entry
+// point): a file-scope device array, one per GPU, held until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) float scratch[ATTENTION_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t attention_scratch(float** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static float* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int64_t attention_partials(const AttnArgs& a) {
   const int64_t nunits = a.tokens / a.block;

@@ -136,5 +136,9 @@ hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_copy_tokens(const void* const* src, void* const* dst, int npairs, int64_t seqs, int64_t k, int64_t rowb,
                               int64_t src_seq, int64_t dst_seq, hipStream_t stream);
 int64_t attention_partials(const AttnArgs& a);   // partials per (sequence, query head)
+// The static partials buffer of the no-alloc attention entry point (its device address on the
+// current device, looked up once per device); ATTENTION_SCRATCH_BYTES is its size.
+constexpr int64_t ATTENTION_SCRATCH_BYTES = int64_t(32) << 20;
+hipError_t attention_scratch(float** ptr);
 
 }  // namespace kvq

@@ -42,6 +42,8 @@ _SIGNATURES = {
     "kvq_attention_workspace_bytes": (ctypes.c_int64, [ctypes.POINTER(KvqDesc), ctypes.c_int64]),
     "kvq_attention_decode": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, ctypes.c_int64, _P]),
+    "kvq_attention_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(KvqDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P,
+                                                    _P, _P, _P, _P, _P]),
     "kvq_append": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
     "kvq_append_kv": (ctypes.c_int, [ctypes.POINTER(KvqDesc), ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _P, _P, _P, _P, _P]),
@@ -241,6 +243,26 @@ def attention_decode(d: Desc, q: torch.Tensor, k_cache, v_cache, k_signs=None, v
                                     _ptr(vc), _ptr(vn), _ptr(vs), _ptr(v_signs), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "kvq_attention_decode")
+    return out
+
+
+def attention_decode_noalloc(d: Desc, q: torch.Tensor, k_cache, v_cache, k_signs=None, v_signs=None,
+                             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_attention_decode_noalloc: kvq_attention_decode with the partials in the library's static
+    per-GPU scratch instead of a caller workspace (the C call allocates nothing; `out` is allocated
+    here with torch when not supplied)."""
+    if q.dtype != torch.float16:
+        raise ValueError("q must be fp16")
+    q_heads = q.shape[1]
+    kc, kn, ks = k_cache
+    vc, vn, vs = v_cache
+    if out is None:
+        out = torch.empty((d.seqs, q_heads, d.head_dim), dtype=torch.float32, device=q.device)
+    _need_cuda(q, kc, kn, ks, vc, vn, vs, k_signs, v_signs, out)
+    st = lib().kvq_attention_decode_noalloc(ctypes.byref(d.c()), _ptr(q), q_heads, _ptr(kc), _ptr(kn), _ptr(ks),
+                                            _ptr(k_signs), _ptr(vc), _ptr(vn), _ptr(vs), _ptr(v_signs), _ptr(out),
+                                            _stream(stream))
+    _check(st, "kvq_attention_decode_noalloc")
     return out
 
 

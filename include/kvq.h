@@ -160,6 +160,22 @@ kvq_status kvq_attention_decode(const kvq_desc* d, const uint16_t* q, int64_t q_
                                 int64_t workspace_bytes, void* stream);
 
 /*
+ * kvq_attention_decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, requirements and
+ * result as kvq_attention_decode, without the workspace: the partials live in a static device
+ * array of KVQ_ATTENTION_SCRATCH_BYTES bytes per GPU, which the library holds until the process
+ * ends.  A shape whose kvq_attention_workspace_bytes exceeds that returns KVQ_ERR_UNSUPPORTED (the
+ * 64 x 32768-token, 8-head, 32-query-head decode step needs 17,039,360 bytes).  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and give wrong results.
+ */
+#define KVQ_ATTENTION_SCRATCH_BYTES 33554432
+kvq_status kvq_attention_decode_noalloc(const kvq_desc* d, const uint16_t* q, int64_t q_heads,
+                                        const uint8_t* k_codes, const uint16_t* k_norms, const uint16_t* k_scales,
+                                        const int8_t* k_signs, const uint8_t* v_codes, const uint16_t* v_norms,
+                                        const uint16_t* v_scales, const int8_t* v_signs, float* out, void* stream);
+
+/*
  * Streaming append with a full-precision residual (NSNQuant summary, "implementation details": the
  * KV cache is a quantized part plus a full-precision residual; when the residual is full it is
  * quantized and moved into the quantized part).  Per-channel modes only: a per-channel scale needs
