@@ -162,12 +162,17 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   //    MFMA-layout reads below are free of bank conflicts); wave 0 also fetches the signs
   {
     const unsigned char* xw = (const unsigned char*)a.x + ((row0 + (B / 4) * w) * a.heads + h) * ROWB;
-    const int64_t tok_bytes = a.heads * ROWB;               // x bytes from one token to the next (64-bit)
+    const int64_t tok_bytes = a.heads * ROWB;               // x bytes from one token to the next
+    // instruction k reads rows RPI k + lane / CPR: a wave-uniform 64-bit base plus a 32-bit lane
+    // offset (below 8 rows of at most 2^20 heads x 256 bytes: the descriptor check caps heads at 2^20)
+    constexpr int RPI = 64 / CPR;                             // rows per load instruction
+    const uint32_t lrow = (uint32_t)(lane / CPR);
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
-      const int p = 64 * k + lane, row = p / CPR, cc = p % CPR;
-      const int64_t off = (int64_t)row * tok_bytes + 16 * (cc ^ ((row + (B / 4) * w) % CPR));
-      __builtin_amdgcn_global_load_lds((const void*)(xw + off),
+      const int row = RPI * k + (int)lrow, cc = lane % CPR;
+      const unsigned char* base = xw + (int64_t)(RPI * k) * tok_bytes;
+      const uint32_t off = lrow * (uint32_t)tok_bytes + 16u * (uint32_t)(cc ^ ((row + (B / 4) * w) % CPR));
+      __builtin_amdgcn_global_load_lds((const void*)(base + off),
                                        (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, 0);
     }
     if constexpr (LG != 0) {

@@ -24,6 +24,35 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, ~8 TB/s
 WORKLOAD = "long_context_decode"
 
 
+def percentile(sorted_vals, p):
+    """Linear-interpolated percentile of an ascending list."""
+    if not sorted_vals:
+        return float("nan")
+    k = (len(sorted_vals) - 1) * p / 100.0
+    i = int(k)
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (k - i)
+
+
+def time_calls(torch, fn, stream, steps, warmup, before=None):
+    """Median, p10 and p90 (us) of `steps` calls of fn, each bracketed by HIP events on `stream`
+    after `warmup` untimed calls; before() (a cache flush) runs ahead of each timed call, outside
+    the events."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        if before is not None:
+            before()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    return {"us": round(percentile(t, 50), 2), "us_p10": round(percentile(t, 10), 2), "us_p90": round(percentile(t, 90), 2)}
+
+
 def algorithmic_bytes(w, q_heads):
     """Every input read once and every output written once (bytes per kernel launch)."""
     n = w.seqs * w.tokens * w.heads * w.head_dim            # K elements
@@ -67,35 +96,92 @@ def measured_traffic(kernel: str):
     return None
 
 
-def cpu_baseline(w, n_seqs: int):
-    """The fp64 oracle (as it stands) on the first n_seqs sequences, one at a time."""
-    import threadpoolctl
-    import oracle
+def _oracle_inputs(w, s):
     from activation_quantization_amd import synth
-    sub = synth.scaled(w, seqs=1)
+    return (synth.make_x(w, seq_range=(s, s + 1)).double().numpy(),
+            synth.make_q(w, seq_range=(s, s + 1)).double().numpy())
+
+
+def _oracle_run(w, signs, x, q):
+    """One sequence of the long-context workload through the fp64 oracle: quantize, dequantize,
+    decode scores (one thread)."""
+    import oracle
     sp = oracle.Spec(1, w.tokens, w.heads, w.head_dim, 4, "nsep_pchan", w.block_tokens, w.hadamard)
+    r = oracle.quantize(x, sp, signs)
+    kh = oracle.dequantize(r.packed, r.norms16, r.scales16, sp, signs)
+    oracle.score_decode(q, kh, sp)
+
+
+def _oracle_worker(name, seq_ids, barrier, results):
+    """A process of the all-core leg: generate its sequences, wait for every worker, then run the
+    oracle on them and report the seconds that took."""
+    import threadpoolctl
+    from activation_quantization_amd import synth
+    w = synth.WORKLOADS[name]
     signs = synth.make_signs(w).numpy()
-    q_all = synth.make_q(w)
-    t_total = cpu_total = 0.0
-    for s in range(n_seqs):
-        x = synth.make_x(w, seq_range=(s, s + 1)).double().numpy()
-        q = q_all[s:s + 1].double().numpy()
-        t0, c0 = time.perf_counter(), time.process_time()
-        r = oracle.quantize(x, sp, signs)
-        kh = oracle.dequantize(r.packed, r.norms16, r.scales16, sp, signs)
-        oracle.score_decode(q, kh, sp)
-        t_total += time.perf_counter() - t0
-        cpu_total += time.process_time() - c0
-    b = algorithmic_bytes(sub, w.q_heads)
-    step_bytes = (b["quantize"] + b["dequantize"] + b["score_decode"]) * n_seqs
-    # threads actually busy on average (process CPU time over wall time); BLAS may use up to
-    # the pool size reported by threadpoolctl
-    pool = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    used = max(1.0, round(cpu_total / t_total, 1))
-    return {"value": round(step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": used, "thread_pool": pool,
-            "kind": "oracle",
-            "sample": f"{n_seqs} of {w.seqs} sequences ({n_seqs * w.tokens * w.heads * w.head_dim} K elements), "
-                      f"quantize+dequantize+score, fp64 numpy, {t_total:.1f} s"}
+    inputs = [_oracle_inputs(w, s) for s in seq_ids]
+    with threadpoolctl.threadpool_limits(1):
+        barrier.wait()
+        t0 = time.perf_counter()
+        for x, q in inputs:
+            _oracle_run(w, signs, x, q)
+        results.put(time.perf_counter() - t0)
+
+
+def _host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def cpu_baseline(w, seqs_one: int, seqs_all: int, workers: int):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload's sequences: seqs_one
+    sequences on one thread, then seqs_all sequences split over `workers` single-threaded processes
+    (the host's cores; sequences are independent).  Only the oracle's work is timed (inputs are
+    generated first).  GB/s counts the step's algorithmic bytes."""
+    import multiprocessing as mp
+    import threadpoolctl
+    from activation_quantization_amd import synth
+    b = algorithmic_bytes(synth.scaled(w, seqs=1), w.q_heads)
+    seq_bytes = b["quantize"] + b["dequantize"] + b["score_decode"]
+    signs = synth.make_signs(w).numpy()
+    t_one = 0.0
+    with threadpoolctl.threadpool_limits(1):
+        for s in range(seqs_one):
+            x, q = _oracle_inputs(w, s)
+            t0 = time.perf_counter()
+            _oracle_run(w, signs, x, q)
+            t_one += time.perf_counter() - t0
+    out = {"value": round(seqs_one * seq_bytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           **_host_info(),
+           "one_thread": {"GB/s": round(seqs_one * seq_bytes / t_one / 1e9, 4), "seqs": seqs_one, "s": round(t_one, 1)}}
+    if workers > 1 and seqs_all >= workers:
+        ctx = mp.get_context("spawn")          # fresh interpreters: nothing of this process's GPU state
+        barrier, results = ctx.Barrier(workers + 1), ctx.Queue()
+        procs = [ctx.Process(target=_oracle_worker, args=(WORKLOAD, list(range(i, seqs_all, workers)), barrier, results))
+                 for i in range(workers)]
+        for p in procs:
+            p.start()
+        barrier.wait()
+        t0 = time.perf_counter()
+        busy = sum(results.get() for _ in procs)
+        wall = time.perf_counter() - t0
+        for p in procs:
+            p.join()
+        out["all_cores"] = {"GB/s": round(seqs_all * seq_bytes / wall / 1e9, 4), "seqs": seqs_all,
+                            "workers": workers, "s": round(wall, 1), "busy_cores": round(busy / wall, 1)}
+        out["value"] = out["all_cores"]["GB/s"]
+        out["cores"] = workers
+    out["sample"] = (f"{seqs_one} sequence(s) on one thread, then {seqs_all} split over {workers} single-threaded "
+                     f"processes, of {w.seqs} sequences ({w.tokens * w.heads * w.head_dim} K elements each), "
+                     "quantize+dequantize+score, fp64 numpy, oracle time only; value = the all-core figure")
+    return out
 
 
 def config_bytes(w, bits_mode):
@@ -150,21 +236,13 @@ def stream_decode(torch, kvq, d, w, q, k_cache, v_cache, signs, att_out, ws, str
                                    "cycle_bytes": cycle_bytes,
                                    "GB/s": round(cycle_bytes / (cycle_us * 1e-6) / 1e9, 1)}}
     n = T - 1
-    for _ in range(warmup):
-        kvq.attention_decode_stream(d, n, q, k_cache, rk, v_cache, rv, signs, signs, out=att_out, workspace=ws,
-                                    stream=stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        kvq.attention_decode_stream(d, n, q, k_cache, rk, v_cache, rv, signs, signs, out=att_out, workspace=ws,
-                                    stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    t = time_calls(torch, lambda: kvq.attention_decode_stream(d, n, q, k_cache, rk, v_cache, rv, signs, signs,
+                                                              out=att_out, workspace=ws, stream=stream),
+                   stream, steps, warmup)
     nb = algorithmic_bytes(w, w.q_heads)["attention_decode"]
-    rows["attention_decode_stream"] = {"us": round(us, 2), "tokens_cached": n, "residual_tokens": B - 1,
-                                       "GB/s": round(nb / (us * 1e-6) / 1e9, 1),
-                                       "frac_hbm": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    gbs = nb / (t["us"] * 1e-6) / 1e9
+    rows["attention_decode_stream"] = {**t, "tokens_cached": n, "residual_tokens": B - 1, "GB/s": round(gbs, 1),
+                                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     return rows
 
 
@@ -187,19 +265,10 @@ def nsn_kernels(torch, kvq, w, x, q, signs, y, stream, dev, steps, warmup, only=
         calls["quantize_nsn"]()
         calls = {only: calls[only]}
     for name, fn in calls.items():
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
-        gbs = nbytes[name] / (us * 1e-6) / 1e9
-        rows[name] = {"us": round(us, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
-                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "in_step": False}
+        t = time_calls(torch, fn, stream, steps, warmup)
+        gbs = nbytes[name] / (t["us"] * 1e-6) / 1e9
+        rows[name] = {**t, "bytes": nbytes[name], "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "in_step": False}
     del out, scores
     return rows
 
@@ -236,18 +305,10 @@ def rrs_kernels(torch, kvq, synth, dev, steps, warmup, only=None):
         calls = {only: calls[only]}
     rows = {}
     for name, fn in calls.items():
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        t = time_calls(torch, fn, stream, steps, warmup)
+        us = t["us"]
         gbs = nbytes[name] / (us * 1e-6) / 1e9
-        row = {"us": round(us, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        row = {**t, "bytes": nbytes[name], "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                "shape": [n, m, k], "in_step": False}
         if name == "rrs_gemm":
             tops = 2.0 * n * m * k / (us * 1e-6) / 1e12
@@ -258,40 +319,35 @@ def rrs_kernels(torch, kvq, synth, dev, steps, warmup, only=None):
 
 
 def other_configs(torch, kvq, synth, dev, steps, warmup):
-    """Quantize and dequantize of the other workloads, each iteration after a 512 MiB read that
-    evicts L2 and the MALL (the events bracket the kernel only).  A read, not a write: a written
-    flush buffer leaves dirty lines whose write-back would land inside the timed kernel."""
+    """Quantize and dequantize of the other workloads at every bit width they name (K and V for the
+    Qwen-like layer), each call after a 512 MiB read that evicts L2 and the MALL (the events bracket
+    the kernel only).  A read, not a write: a written flush buffer leaves dirty lines whose
+    write-back would land inside the timed kernel."""
     flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     rows = []
     for name in ("qwen_kv_layer", "batched_hadamard", "activation_4096"):
         w = synth.WORKLOADS[name]
         dt = synth.torch_dtype(w)
-        d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, 4, w.mode, w.block_tokens, w.hadamard, dt)
-        x = synth.make_x(w).to(dev)
         sg = synth.make_signs(w).to(dev) if w.hadamard else None
-        out = kvq.alloc_outputs(d, dev)
-        y = torch.empty_like(x)
-        qb, db = config_bytes(w, w.mode)
-        for kname, fn, nbytes in (("quantize", lambda: kvq.quantize(d, x, sg, out=out, stream=stream), qb),
-                                  ("dequantize", lambda: kvq.dequantize(d, *out, sg, out_dtype=dt, out=y, stream=stream), db)):
-            for _ in range(warmup):
-                fn()
-            tot = 0.0
-            for _ in range(steps):
-                flush.sum()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                tot += e0.elapsed_time(e1)
-            us = tot * 1e3 / steps
-            gbs = nbytes / (us * 1e-6) / 1e9
-            rows.append({"workload": name, "kernel": kname, "shape": [w.seqs, w.tokens, w.heads, w.head_dim],
-                         "mode": w.mode, "bits": 4, "hadamard": w.hadamard, "dtype": w.dtype, "us": round(us, 2),
-                         "bytes": nbytes, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
-        del x, y, out
+        for tensor_id in range(w.tensors):
+            x = synth.make_x(w, tensor_id=tensor_id).to(dev)
+            y = torch.empty_like(x)
+            for bits in w.bits:
+                d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, bits, w.mode, w.block_tokens, w.hadamard, dt)
+                out = kvq.alloc_outputs(d, dev)
+                qb, db = config_bytes(w, w.mode)
+                for kname, fn, nbytes in (("quantize", lambda: kvq.quantize(d, x, sg, out=out, stream=stream), qb),
+                                          ("dequantize", lambda: kvq.dequantize(d, *out, sg, out_dtype=dt, out=y,
+                                                                                 stream=stream), db)):
+                    t = time_calls(torch, fn, stream, steps, warmup, before=flush.sum)
+                    gbs = nbytes / (t["us"] * 1e-6) / 1e9
+                    rows.append({"workload": name, "tensor": "KV"[tensor_id] if w.tensors == 2 else "x", "kernel": kname,
+                                 "shape": [w.seqs, w.tokens, w.heads, w.head_dim], "mode": w.mode, "bits": bits,
+                                 "hadamard": w.hadamard, "dtype": w.dtype, **t, "bytes": nbytes, "GB/s": round(gbs, 1),
+                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+                del out
+            del x, y
     return rows
 
 
@@ -300,7 +356,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seqs", type=int, default=10, help="sequences in the oracle baseline sample (0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=2,
+                    help="sequences the oracle baseline times on one thread (0 = skip the baseline)")
+    ap.add_argument("--cpu-seqs-all", type=int, default=16,
+                    help="sequences the oracle baseline times over all host cores")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes for the all-core leg (0 = the host's cores, at most 16)")
     ap.add_argument("--only", choices=("quantize", "dequantize", "score_decode", "attention_decode") + NSN_KERNELS
                     + RRS_KERNELS,
                     default=None,
@@ -391,8 +452,10 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per_kernel_ms = {n: sum(e[k].elapsed_time(e[k + 1]) for e in events) / args.steps for k, n in enumerate(names)}
-    gpu_step_ms = sum(events[i][0].elapsed_time(events[i][3]) for i in range(args.steps)) / args.steps
+    # per kernel: median, p10 and p90 over the timed steps (HIP events on the stream the kernels run on)
+    samples = {n: sorted(e[k].elapsed_time(e[k + 1]) for e in events) for k, n in enumerate(names)}
+    per_kernel_ms = {n: percentile(v, 50) for n, v in samples.items()}
+    gpu_step_ms = percentile(sorted(events[i][0].elapsed_time(events[i][3]) for i in range(args.steps)), 50)
     ms_per_step = wall * 1e3 / args.steps
 
     b = algorithmic_bytes(w, w.q_heads)
@@ -411,27 +474,22 @@ def main():
         att_out = torch.empty((w.seqs, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
         ws = torch.empty(kvq.attention_workspace_bytes(d, w.q_heads) // 4, dtype=torch.float32, device=dev)
         kc = (codes, norms, scales)
-        for _ in range(args.warmup):
-            kvq.attention_decode(d, q, kc, vcache, signs, signs, out=att_out, workspace=ws, stream=stream)
-        torch.cuda.synchronize()
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        for _ in range(args.steps):
-            kvq.attention_decode(d, q, kc, vcache, signs, signs, out=att_out, workspace=ws, stream=stream)
-        a1.record(stream)
-        torch.cuda.synchronize()
-        attn_us = a0.elapsed_time(a1) * 1e3 / args.steps
+        attn_t = time_calls(torch, lambda: kvq.attention_decode(d, q, kc, vcache, signs, signs, out=att_out,
+                                                                 workspace=ws, stream=stream),
+                            stream, args.steps, args.warmup)
+        attn_us = attn_t["us"]
     kernels = {}
     for n in names:
         if not run[n]:
             continue
         gbs = b[n] / (per_kernel_ms[n] * 1e-3) / 1e9
-        kernels[n] = {"us": round(per_kernel_ms[n] * 1e3, 2), "bytes": b[n], "GB/s": round(gbs, 1),
+        kernels[n] = {"us": round(per_kernel_ms[n] * 1e3, 2), "us_p10": round(percentile(samples[n], 10) * 1e3, 2),
+                      "us_p90": round(percentile(samples[n], 90) * 1e3, 2), "bytes": b[n], "GB/s": round(gbs, 1),
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     traffic = measured_traffic("quantize")
     if attn_us is not None:
         gbs = b["attention_decode"] / (attn_us * 1e-6) / 1e9
-        kernels["attention_decode"] = {"us": round(attn_us, 2), "bytes": b["attention_decode"], "GB/s": round(gbs, 1),
+        kernels["attention_decode"] = {**attn_t, "bytes": b["attention_decode"], "GB/s": round(gbs, 1),
                                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "in_step": False}
     if attn_us is not None and not args.only:
         kernels.update(stream_decode(torch, kvq, d, w, q, kc, vcache, signs, att_out, ws, stream, dev,
@@ -469,7 +527,8 @@ def main():
     if args.cpu_seqs > 0:
         del x, y
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, args.cpu_seqs_all, workers)
     print(json.dumps(out), flush=True)
 
 
