@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_quant_pchan.hip", "kvq_quantize.hip", "kvq_dequantize.hip", "kvq_score.hip", "kvq_attention.hip", "kvq_stream.hip", "kvq_nsn.hip", "kvq_rrs.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quant_pchan.hip", "kvq_quantize.hip", "kvq_quant_ptok.hip", "kvq_dequantize.hip", "kvq_score.hip", "kvq_attention.hip", "kvq_stream.hip", "kvq_nsn.hip", "kvq_rrs.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.

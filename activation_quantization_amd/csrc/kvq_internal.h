@@ -121,6 +121,9 @@ struct AttnArgs {
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);
+// the matrix-core per-token kernel (head_dim a power of two in [128, 8192]); launch_quantize_ptok
+// dispatches to it
+hipError_t launch_quantize_ptok_mfma(const QuantArgs& a, hipStream_t stream);
 // RRS: s[k] = max over the rows of |(x R)| over 128-channel segment k (fp32, orthonormal units), for
 // a per-token QuantArgs with heads = 1 and dim a power of two >= 128
 hipError_t launch_rrs_colmax(const QuantArgs& a, float* s, hipStream_t stream);

@@ -1,0 +1,105 @@
+// Matrix-core rotation helpers shared by the quantize kernels for gfx950: the blockdiag(H_n)
+// fragments of the 16x16x32 MFMA layout, cross-lane reductions, and the exact (fp64) rounding
+// decision of the near-tie paths.
+//
+// Layout (16-row sub-tiles): lane l = 16 g + j holds row j of the sub-tile; the B operand of K step
+// K is input channels 32 K + 8 g + e, and MFMA row i of a wave's I-block I is output channel
+// c = (R/4) w + 8 (i >> 2) + 4 I + (i & 3) (R = 128; R = 64 uses one I-block), so lane l ends with
+// output channels (R/4) w + 8 g + [0, 8) of row j.  Every 16 x 32 block of blockdiag(H_n), n = 2^LG,
+// factors bit by bit into beta(w, K), from the bits of c and c' that the wave index and the K step
+// set alone (a sign, or zero outside the diagonal blocks), times a fragment F_I over the remaining
+// bits, so two fragment registers per wave hold the transform.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace rot {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int DT> __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+template <int DT> __device__ __forceinline__ double widen64(uint32_t h) {
+  return (double)(DT == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h));
+}
+
+// the rounding decision on the fp64 quotient itself: round half to even
+__device__ __forceinline__ uint32_t exact_nibble(double v) {
+  return (uint32_t)(int)__builtin_rint(v) & 0xfu;
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max over the 16 lanes of each row (lanes 16 g .. 16 g + 15) with DPP row rotations
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));   // row_ror:2
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));   // row_ror:1
+  return v;
+}
+
+__device__ __forceinline__ uint32_t row_or16(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// entry (c, c') of blockdiag(H_n), n = 2^LG: zero unless c and c' share their n-block
+template <int LG> __device__ __forceinline__ constexpr int hval(int c, int cp) {
+  if ((c >> LG) != (cp >> LG)) return 0;
+  return (__builtin_popcount(c & cp & ((1 << LG) - 1)) & 1) ? -1 : 1;
+}
+
+template <int R> __device__ __forceinline__ constexpr int out_channel(int w, int I, int i) {
+  return R == 128 ? 32 * w + 8 * (i >> 2) + 4 * I + (i & 3) : 16 * w + 4 * (i >> 2) + (i & 3);
+}
+// bits of the channel numbers that are set by the wave index (c) and by the K step (c')
+template <int R> constexpr int UMASK = R == 128 ? 0x60 : 0x20;
+
+// F_{w,I}: this lane's 8 A-operand entries (row i = lane & 15, inputs 8 (lane >> 4) + e of K
+// step 0) over the bits of c and c' that are not both uniform
+template <int DT, int R, int LG> __device__ __forceinline__ u32x4 hadamard_fragment(int w, int I, int lane) {
+  const int c = out_channel<R>(w, I, lane & 15) & ~UMASK<R>;
+  const uint32_t one = DT == DT_F16 ? 0x3C00u : 0x3F80u;
+  uint32_t q4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t pair = 0u;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int cp = (8 * (lane >> 4) + 2 * q + hh) & ~UMASK<R>;
+      const int v = hval<LG>(c, cp);
+      pair |= (v == 0 ? 0u : (one | (v < 0 ? 0x8000u : 0u))) << (16 * hh);
+    }
+    q4[q] = pair;
+  }
+  return u32x4{q4[0], q4[1], q4[2], q4[3]};
+}
+// beta(w, K) at run time for R = 128 (w wave-uniform): the same factor as frag_beta
+template <int LG> __device__ __forceinline__ int blk_beta(int w, int K) {
+  return hval<LG>((32 * w) & 0x60, (32 * K) & 0x60);
+}
+// beta(w, K): the factor from the uniform bits
+template <int R, int LG> __device__ __forceinline__ constexpr int frag_beta(int w, int K) {
+  return hval<LG>(out_channel<R>(w, 0, 0) & UMASK<R>, (32 * K) & UMASK<R>);
+}
+
+
+}  // namespace rot
+}  // namespace kvq
