@@ -4,12 +4,19 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 
 static_assert(KVQ_ATTENTION_SCRATCH_BYTES == kvq::ATTENTION_SCRATCH_BYTES, "scratch size in the header");
+
+bool kvq::rotation_butterfly() {
+  const char* e = std::getenv("KVQ_ROTATION");
+  return e != nullptr && std::strcmp(e, "butterfly") == 0;
+}
 
 namespace {
 

@@ -408,7 +408,7 @@ static void dq_ptok_k(const DequantArgs& a, hipStream_t st) {
   constexpr int OB = ODT == DT_F32 ? 4 : 2;
   int lgL = 0;
   while ((R << lgL) < a.dim) ++lgL;
-  if (a.tokens % 64 == 0) {                             // whole 64-token chunks: matrix cores
+  if (a.tokens % 64 == 0 && !rotation_butterfly()) {   // whole 64-token chunks: matrix cores
     dq_mfma_k<ODT, R, LG, true>(a, st, lgL);
     return;
   }

@@ -118,6 +118,11 @@ struct AttnArgs {
   int32_t res_dtype;        // DT_F16 / DT_BF16
 };
 
+// The 128-point rotation of the per-token kernels runs on the matrix cores unless the environment
+// variable KVQ_ROTATION is "butterfly" (read at every call), which selects the register-butterfly
+// kernels (the comparison the rotation choice rests on).
+bool rotation_butterfly();
+
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);

@@ -561,7 +561,7 @@ static void ptok_dt(const QuantArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t st) {
-  if (a.dim >= 128) return launch_quantize_ptok_mfma(a, st);
+  if (a.dim >= 128 && !rotation_butterfly()) return launch_quantize_ptok_mfma(a, st);
   if (a.dtype == DT_F16) ptok_dt<DT_F16>(a, st); else ptok_dt<DT_BF16>(a, st);
   return hipGetLastError();
 }

@@ -318,7 +318,7 @@ def rrs_kernels(torch, kvq, synth, dev, steps, warmup, only=None):
     return rows
 
 
-def other_configs(torch, kvq, synth, dev, steps, warmup):
+def other_configs(torch, kvq, synth, dev, steps, warmup, only=None):
     """Quantize and dequantize of the other workloads at every bit width they name (K and V for the
     Qwen-like layer), each call after a 512 MiB read that evicts L2 and the MALL (the events bracket
     the kernel only).  A read, not a write: a written flush buffer leaves dirty lines whose
@@ -326,7 +326,10 @@ def other_configs(torch, kvq, synth, dev, steps, warmup):
     flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     rows = []
-    for name in ("qwen_kv_layer", "batched_hadamard", "activation_4096"):
+    names = ("qwen_kv_layer", "batched_hadamard", "activation_4096")
+    if only is not None:                                   # "<workload>/<kernel>"
+        names = (only.split("/")[0],)
+    for name in names:
         w = synth.WORKLOADS[name]
         dt = synth.torch_dtype(w)
         sg = synth.make_signs(w).to(dev) if w.hadamard else None
@@ -340,6 +343,10 @@ def other_configs(torch, kvq, synth, dev, steps, warmup):
                 for kname, fn, nbytes in (("quantize", lambda: kvq.quantize(d, x, sg, out=out, stream=stream), qb),
                                           ("dequantize", lambda: kvq.dequantize(d, *out, sg, out_dtype=dt, out=y,
                                                                                  stream=stream), db)):
+                    if only is not None and only.split("/")[1] != kname:
+                        if kname == "quantize":
+                            fn()                           # the codes the dequantize reads
+                        continue
                     t = time_calls(torch, fn, stream, steps, warmup, before=flush.sum)
                     gbs = nbytes / (t["us"] * 1e-6) / 1e9
                     rows.append({"workload": name, "tensor": "KV"[tensor_id] if w.tensors == 2 else "x", "kernel": kname,
@@ -366,6 +373,9 @@ def main():
                     + RRS_KERNELS,
                     default=None,
                     help="run just this kernel in each step (for profiler runs; no cpu baseline)")
+    ap.add_argument("--config-only", default=None,
+                    help="time just <workload>/<kernel> of the other workloads (e.g. activation_4096/quantize; "
+                         "for profiler runs) and exit")
     ap.add_argument("--other-configs", type=int, default=1,
                     help="also time quantize / dequantize of the other workloads (1 = yes), after an L2/MALL flush")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -384,6 +394,11 @@ def main():
     w = synth.WORKLOADS[WORKLOAD]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config_only:
+        rows = other_configs(torch, kvq, synth, dev, args.steps, args.warmup, only=args.config_only)
+        print(json.dumps({"profile_only": args.config_only, "rotation": os.environ.get("KVQ_ROTATION", "mfma"),
+                          "rows": rows}), flush=True)
+        return
     d = kvq.Desc(w.seqs, w.tokens, w.heads, w.head_dim, 4, "nsep_pchan", w.block_tokens, w.hadamard, torch.float16)
     print(f"[bench] generating {WORKLOAD} x {w.seqs}x{w.tokens}x{w.heads}x{w.head_dim} fp16", file=sys.stderr, flush=True)
     t0 = time.time()

@@ -105,12 +105,17 @@ int64_t kvq_scales_count(const kvq_desc* d);
 
 /*
  * Quantize x [rows, heads, head_dim] (dtype d->dtype) into packed codes, fp16 norms (NSEP
- * modes) and fp16 scales.  Steps per (token, head) vector: optional signs then orthonormal
- * block Hadamard (1/sqrt n, natural Sylvester order); nu = ||y||_2 and u = y/nu (NSEP modes;
- * nu = 0 gives u = 0); scale = absmax / Q per token or per channel over the token block;
- * code = clamp(round_half_even(u / scale), -Q, Q) computed from the unrounded fp32 scale and
- * norm (scale = 0 gives code 0).  Stored norms and scales are the fp16 (round-to-nearest-even)
- * values of nu and scale.
+ * modes) and fp16 scales.  Sources: norm-separation post, "the fix" (an fp16 L2 norm per KV vector
+ * and a unit direction; absmax / Q; round and clamp to +-Q) and per-channel scaling; Rotated Runtime
+ * Smooth analysis, "problem definition" (alpha = max|X| / (2^(N-1) - 1)) and "term-by-term"
+ * (R = (1/sqrt K)[+-1]); NSNQuant summary, "Hadamard transform" (random signs before the Hadamard
+ * matrix).  Steps per (token, head) vector: optional signs then orthonormal block Hadamard
+ * (1/sqrt n, natural Sylvester order); nu = ||y||_2 and u = y/nu (NSEP modes; nu = 0 gives u = 0);
+ * scale = absmax / Q per token or per channel over the token block; code =
+ * clamp(round_half_even(u / scale), -Q, Q) of the exact quotient (from the unrounded scale and norm;
+ * scale = 0 gives code 0).  Stored norms and scales are the fp16 (round-to-nearest-even) values of
+ * nu and scale.  Outputs are head-major: codes [seqs, heads, tokens, head_dim/2], norms and per-token
+ * scales [seqs, heads, tokens], per-channel scales [seqs, heads, tokens/B, head_dim].
  *   norms must be NULL for NAIVE / PCHAN and non-NULL for NSEP modes.
  */
 kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs,
@@ -119,7 +124,10 @@ kvq_status kvq_quantize(const kvq_desc* d, const void* x, const int8_t* signs,
 /*
  * Dequantize: y^ = code * scale * (norm for NSEP modes), then the inverse rotation
  * sigma * (1/sqrt n) H y^, written to y [rows, heads, head_dim] in y_dtype (F16, BF16 or
- * F32, round-to-nearest-even).  Inputs are exactly the buffers kvq_quantize writes.
+ * F32, round-to-nearest-even).  Inputs are exactly the buffers kvq_quantize writes.  Sources:
+ * norm-separation post, "the fix" (the quantized direction is code times scale, and the norm
+ * multiplies back); Rotated Runtime Smooth analysis, "term-by-term" (R^-1 = R^T); NSNQuant summary,
+ * "implementation details" (a dedicated dequantization kernel).
  */
 kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_t* norms,
                           const uint16_t* scales, const int8_t* signs, void* y, int32_t y_dtype,
@@ -130,7 +138,10 @@ kvq_status kvq_dequantize(const kvq_desc* d, const uint8_t* codes, const uint16_
  * 128):  scores[s, hq, t] = sum_d q[s, hq, d] * k^[s*T + t, hq / G, d], G = q_heads/heads
  * (query heads grouped contiguously), k^ the dequantized key.  No 1/sqrt(d), no softmax.
  * The kernel works in the rotated domain: it rotates each query once and folds the stored
- * scales and norms into the contraction.
+ * scales and norms into the contraction.  Sources: NSNQuant summary, "implementation details"
+ * (scores computed from the quantized keys with the stored byproducts folded into the kernel) and
+ * "latency"; Rotated Runtime Smooth analysis, Figure 2 (XR (R^-1 W^T) = X W^T: the product may run
+ * in the rotated domain).
  *   q: fp16 bits [seqs, q_heads, head_dim]; scores: fp32 [seqs, q_heads, tokens_per_seq].
  */
 kvq_status kvq_score_decode(const kvq_desc* d, const uint16_t* q, int64_t q_heads,
