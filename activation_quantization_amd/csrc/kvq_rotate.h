@@ -54,10 +54,35 @@ __device__ __forceinline__ uint32_t row_or16(uint32_t v) {
   return v;
 }
 
+// fp64 sum over the wave, the same value in every lane (each step adds a pair symmetrically):
+// within a 16-lane row by DPP moves (quad_perm xor 1, xor 2, row_half_mirror, row_mirror), across
+// rows by v_permlane16_swap / v_permlane32_swap; no LDS round trips
+template <int CTL> __device__ __forceinline__ double dpp64(double v) {
+  const u32x2 p = __builtin_bit_cast(u32x2, v);
+  return __builtin_bit_cast(double, u32x2{(uint32_t)__builtin_amdgcn_mov_dpp((int)p.x, CTL, 0xF, 0xF, false),
+                                          (uint32_t)__builtin_amdgcn_mov_dpp((int)p.y, CTL, 0xF, 0xF, false)});
+}
+// v_permlane16_swap (32_swap) of a value with itself: one output holds the even (lower) row's
+// value in both rows of a pair, the other the odd (upper) row's, so their sum is the pair's sum
+__device__ __forceinline__ double pair_sum16(double v) {
+  const u32x2 p = __builtin_bit_cast(u32x2, v);
+  const auto lo = __builtin_amdgcn_permlane16_swap(p.x, p.x, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(p.y, p.y, false, false);
+  return __builtin_bit_cast(double, u32x2{lo[0], hi[0]}) + __builtin_bit_cast(double, u32x2{lo[1], hi[1]});
+}
+__device__ __forceinline__ double pair_sum32(double v) {
+  const u32x2 p = __builtin_bit_cast(u32x2, v);
+  const auto lo = __builtin_amdgcn_permlane32_swap(p.x, p.x, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(p.y, p.y, false, false);
+  return __builtin_bit_cast(double, u32x2{lo[0], hi[0]}) + __builtin_bit_cast(double, u32x2{lo[1], hi[1]});
+}
 __device__ __forceinline__ double wave_sum64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp64<0xB1>(v);      // quad_perm [1, 0, 3, 2]
+  v += dpp64<0x4E>(v);      // quad_perm [2, 3, 0, 1]
+  v += dpp64<0x141>(v);     // row_half_mirror
+  v += dpp64<0x140>(v);     // row_mirror
+  v = pair_sum16(v);
+  return pair_sum32(v);
 }
 
 // entry (c, c') of blockdiag(H_n), n = 2^LG: zero unless c and c' share their n-block
