@@ -15,14 +15,16 @@
 // where q . offset (original domain) is one dot product per unit and query head.
 //
 // Work: a workgroup takes a chunk of one head-major (sequence, KV head) stream; each wave
-// walks units of U tokens (U = the scale block for per-channel modes, 128 otherwise).  Per unit
-// the wave issues all of its loads at once (16 bytes of codes per lane and 16-token group, the
-// unit's scale row, the norms), then builds the MFMA A operand: g = (R q) * scale in fp32, split
-// into an fp16 hi/lo pair, rows 2 h + {0, 1} = (hi, lo) of query head h (8 heads per pass).
-// The B operand is 16 tokens x 32 channels of codes as fp16 subnormals (c + 8) 2^-24 (two bit
-// operations per pair); the K order inside a lane is [n0 n4 n1 n5 n2 n6 n3 n7] and the A
-// operand uses the same order.  Lane (g, j) of the
-// result holds rows 4 g + r: heads 2 g and 2 g + 1 (hi and lo rows summed) of token j.
+// walks units of U tokens (U = the scale block for per-channel modes, 128 otherwise).  The MFMA
+// tile is 16 rows x 16 tokens: row i serves query head 4 hc + i / 4 of pass hc, and i % 4 picks
+// the part of g = (R q) * scale it carries: bit 0 the fp16 high part hi (the fp32 value truncated
+// to 11 significant bits) or the low part 2^10 (g - hi), bit 1 the even or the odd channels (the
+// other parity's K slots are zero).  The B operand is 16 tokens x 32 channels of codes as fp16
+// subnormals (c + 8) m 2^-24, the nibbles masked in place (m = 1 for even, 16 for odd channels);
+// the K order inside a lane is [n0 n4 n1 n5 n2 n6 n3 n7].  Lane (g, j) of the result holds the
+// four parts of head 4 hc + g for token j, and sums them with the factors 1, 2^-10, 2^-4, 2^-14.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -30,24 +32,29 @@ namespace kvq {
 
 __device__ __forceinline__ int nib_of(int e) { return (e >> 1) + ((e & 1) << 2); }
 
-// B operand of the 8 codes of one packed word, in [n0 n4 n1 n5 n2 n6 n3 n7] order, as the fp16
-// subnormals (c + 8) 2^-24: (word ^ 0x88888888) >> 4 q & 0x000F000F is the pair (c_q + 8,
-// c_{q+4} + 8) in the mantissa bits, exact.  The bias 8 leaves through the accumulator's start
-// value (-8 2^-24 times the row sums of A) and 2^24 through the epilogue factor.
+// B operand of the 8 codes of one packed word, slots [n0 n4 | n1 n5 | n2 n6 | n3 n7] (one 32-bit
+// word per pair, low half first): the xor turns each two's-complement nibble into c + 8, and the
+// nibbles are masked where they sit (bits 0-3 or 4-7 of a 16-bit half, after one 8-bit shift), so
+// even channels read (c + 8) 2^-24 and odd channels (c + 8) 16 2^-24, all exact fp16 subnormals
 __device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
-  const uint32_t xb = word ^ 0x88888888u;
-  return u32x4{xb & 0x000F000Fu, (xb >> 4) & 0x000F000Fu, (xb >> 8) & 0x000F000Fu, (xb >> 12) & 0x000F000Fu};
+  // a rotate rather than a shift keeps the bias constant (0x88888888 rotated is itself), so each
+  // output is one xor-and of three operands
+  const uint32_t ws = __builtin_amdgcn_alignbit(word, word, 8);
+  constexpr uint32_t B8 = 0x88888888u;
+  return u32x4{(word ^ B8) & 0x000F000Fu, (word ^ B8) & 0x00F000F0u, (ws ^ B8) & 0x000F000Fu, (ws ^ B8) & 0x00F000F0u};
 }
 
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
-
+constexpr uint32_t HI_MASK = 0xFFFFE000u;      // fp32 bits that survive truncation to fp16 precision
 
 template <int R, bool NS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
                                                     int vec_scales) {
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
   constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
-  __shared__ __attribute__((aligned(16))) float qr[16 * R];   // rotated queries of this KV head's group
+  // rotated queries of this KV head's group: [head][part: x1, x2^10][parity][R / 2] (zero past G)
+  __shared__ __attribute__((aligned(16))) float qa[16 * 2 * R];
+  __shared__ __attribute__((aligned(16))) float qr[16 * R];   // the rotation's work area
   __shared__ float qob[NS ? SCORE_UNITS_PER_BLOCK : 1][16];  // NSN: q . offset per (unit, query head)
   __shared__ __attribute__((aligned(16))) uint16_t qh[NS ? 16 * R : 8];   // NSN: fp16 queries (zero rows past G)
   __shared__ float tokf[4][2][256];   // per wave, the unit's tokens: norm 2^24 token-scale s2, and norm
@@ -60,6 +67,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
   const int64_t ci = tile % nchunks;
   const int64_t sh = tile / nchunks;                        // head-major stream: s * heads + kvh
   const int64_t kvh = sh % a.heads, s = sh / a.heads;
+  const int NHC = (G + 3) / 4;                              // passes of 4 query heads
 
   // 1. rotated queries R q = (1/sqrt n) H (sigma * q), once per workgroup (butterflies in LDS)
   for (int e = tid; e < G * R; e += 256) {
@@ -80,19 +88,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     }
     __syncthreads();
   }
-  if (a.lg_had) {
-    for (int e = tid; e < G * R; e += 256) qr[e] *= a.inv_sqrt_n;
-    __syncthreads();
+  // the A-operand table: both parts' scalings (exact powers of two) and the channels split by parity
+  for (int e = tid; e < 4 * NHC * R; e += 256) {
+    const int hh = e / R, d = e % R;
+    const float v = hh < G ? (a.lg_had ? qr[e] * a.inv_sqrt_n : qr[e]) : 0.f;
+    float* row = qa + hh * 2 * R + (d & 1) * (R / 2) + (d >> 1);
+    row[0] = v;
+    row[R] = v * 0x1p10f;
   }
 
   // NSN: the original-domain fp16 queries, the A operand of q . offset on the matrix cores (row i =
   // query head i of the group, zero rows past G)
-  if constexpr (NS) {
+  if constexpr (NS)
     for (int e = tid; e < 16 * R; e += 256) qh[e] = e / R < G ? a.q[(s * a.q_heads + kvh * G) * R + e] : (uint16_t)0;
-    __syncthreads();
-  }
+  __syncthreads();
 
-  const int NHC = (G + 7) / 8;                              // passes of 8 query heads
   const int64_t nunits = (T + U - 1) / U;
   const int64_t u_begin = ci * SCORE_UNITS_PER_BLOCK;
   const int64_t u_end = u_begin + SCORE_UNITS_PER_BLOCK < nunits ? u_begin + SCORE_UNITS_PER_BLOCK : nunits;
@@ -131,8 +141,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
       f32x4 qo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int K = 0; K < KS; ++K) {
-        const f16x8 qa = __builtin_bit_cast(f16x8, *(const u32x4*)(qh + j * R + 32 * K + 8 * g));
-        qo = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, __builtin_bit_cast(f16x8, ov[i][K]), qo, 0, 0, 0);
+        const f16x8 qv = __builtin_bit_cast(f16x8, *(const u32x4*)(qh + j * R + 32 * K + 8 * g));
+        qo = __builtin_amdgcn_mfma_f32_16x16x32_f16(qv, __builtin_bit_cast(f16x8, ov[i][K]), qo, 0, 0, 0);
       }
       if (j == 0)
 #pragma unroll
@@ -141,6 +151,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
   }
+
+  // this lane's A row: part (j & 1: hi or 2^10 lo), channel parity p = (j >> 1) & 1
+  const int par = (j >> 1) & 1;
+  const uint32_t lo_mask = (j & 1) ? HI_MASK : 0u;          // g - (g & mask): g itself, or its low part
+  const uint32_t keep = par ? 0u : 0xFFFFFFFFu;             // even rows fill words 0, 2; odd rows 1, 3
 
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
@@ -155,8 +170,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
       sv[k] = tsc_p[a.per_channel ? 0 : tc];
       if constexpr (NS) s2v[k] = a.s2[tstream + tc];
     }
-    // scales of this lane's channels (LB g .. as fp16), loaded with the unit
-    float sc[KS * 8];
+    // scales of this lane's channels of its parity: (R / 4) g + 8 K + 2 i + par, i = 0..3
+    float sc[KS][4];
     if (a.per_channel) {
       const uint16_t* srow = a.scales + (sh * nb + un) * R + (R / 4) * g;
       if (vec_scales) {
@@ -165,17 +180,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
           const u32x4 v = *(const u32x4*)(srow + 8 * K);
           const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int n = nib_of(e);
-            sc[8 * K + e] = f16_to_f32((n & 1) ? wv[n >> 1] >> 16 : wv[n >> 1] & 0xffffu);
-          }
+          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((wv[i] >> (16 * par)) & 0xffffu);
         }
       } else {
 #pragma unroll
         for (int K = 0; K < KS; ++K)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sc[8 * K + e] = f16_to_f32(srow[8 * K + nib_of(e)]);
+          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32(srow[8 * K + 2 * i + par]);
       }
+    } else {
+#pragma unroll
+      for (int K = 0; K < KS; ++K)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[K][i] = 1.f;
     }
     // f = norm 2^24 token-scale (s2), f1 = norm (a mode without the value reads the constant 1.0)
 #pragma unroll
@@ -190,93 +207,86 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
+    // tokens of this unit past the stream's end read the last token (their scores are not stored)
+    const int lim = T - t0 < U ? (int)(T - 1 - t0) : U - 1;
+    const unsigned char* cu = cstream + t0 * (R / 2) + LB * g;
     for (int hc = 0; hc < NHC; ++hc) {
-      // A operand: row i = lane & 15 -> head hc 8 + i / 2, hi (i even) or lo (i odd) part
-      const int hl = hc * 8 + (j >> 1);
-      const bool live = hl < G;
+      // A operand of row j: g (x 2^10 for the low part) of the lane's parity, its high part
+      // truncated by the fp16 conversion or its low part left after the mask
+      const float* qp = qa + ((4 * hc + (j >> 2)) * 2 + (j & 1)) * R + par * (R / 2) + (R / 8) * g;
       f16x8 av[KS];
 #pragma unroll
       for (int K = 0; K < KS; ++K) {
-        const float* qp = qr + hl * R + (R / 4) * g + 8 * K;   // inside qr even when not live
-        const f32x4 q0 = *(const f32x4*)qp, q1 = *(const f32x4*)(qp + 4);
-        // rows of even j take hi = fp16(g), odd j take lo = fp16(g - hi); hi + lo = g to ~2^-21
-        // relative with any rounding, so the packed round-toward-zero conversion serves
+        const f32x4 q4 = *(const f32x4*)(qp + 4 * K);
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int n0 = nib_of(e), n1 = nib_of(e + 1);
-          float g0 = n0 < 4 ? q0[n0] : q1[n0 - 4], g1 = n1 < 4 ? q0[n1] : q1[n1 - 4];
-          if (a.per_channel) {
-            g0 *= sc[8 * K + e];
-            g1 *= sc[8 * K + e + 1];
-          }
-          const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(g0, g1));
-          const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(g0 - (float)hi[0], g1 - (float)hi[1]));
-          const f16x2 pv = live ? ((j & 1) ? lo : hi) : f16x2{(_Float16)0.f, (_Float16)0.f};
-          av[K][e] = pv[0];
-          av[K][e + 1] = pv[1];
+        for (int i = 0; i < 4; ++i) {
+          const float gv = q4[i] * sc[K][i];
+          v[i] = gv - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gv) & lo_mask);
         }
+        const uint32_t w02 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[0], v[2]));
+        const uint32_t w13 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[1], v[3]));
+        av[K] = __builtin_bit_cast(f16x8, u32x4{w02 & keep, w02 & ~keep, w13 & keep, w13 & ~keep});
       }
-      // NSN: q . offset of this lane's two heads for the unit
-      float qo0 = 0.f, qo1 = 0.f;
-      if constexpr (NS) {
-        const int h0 = hc * 8 + 2 * g;
-        qo0 = qob[un - u_begin][h0 < 16 ? h0 : 15];
-        qo1 = qob[un - u_begin][h0 + 1 < 16 ? h0 + 1 : 15];
-      }
-      // accumulator start: -8 2^-24 sum_k A[i][k], from one more product with B = ones (lane (g, j)
-      // receives rows 4 g + r)
+      // NSN: q . offset of this lane's head for the unit
+      float qo = 0.f;
+      if constexpr (NS) qo = qob[un - u_begin][4 * hc + g < 16 ? 4 * hc + g : 15];
+      // accumulator start: -8 2^-24 sum_k A[i][k] m_k, from one more product with B = m (1 for the
+      // even-channel slots, 16 for the odd ones; lane (g, j) receives rows 4 g + r)
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int K = 0; K < KS; ++K)
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}), acc0, 0, 0, 0);
+            av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u}), acc0, 0, 0, 0);
       acc0 *= -8.f * 0x1p-24f;
-      // 16-token groups, four at a time: every load of the four first, then the products
-      for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
-        uint32_t wd[4][KS];
-        float f[4], f1[4];
-        // the four groups' code loads are all issued before any is used (a token past the end
-        // reads the last token; its scores are not stored)
+      const int hq = 4 * hc + g;                            // this lane's query head in the group
+      float* sp = a.scores + (s * a.q_heads + kvh * G + (hq < G ? hq : 0)) * T + t0 + j;
+      const bool store = hq < G;
+      // 16-token groups, four at a time: every load of the four first, then the products.  A whole
+      // unit loads at fixed offsets from the lane's token; the stream's last, partial unit clamps
+      // each token to the last one and stores only tokens inside the stream.
+      auto groups = [&](auto full_unit) {
+        constexpr bool FULL = decltype(full_unit)::value;
+        const unsigned char* cj = cu + j * (R / 2);
+        for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
+          uint32_t wd[4][KS];
+          float f[4], f1[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int64_t t = t0 + 16 * (gr0 + b) + j;
-          const int64_t tc = t < T ? t : T - 1;
-          const unsigned char* cp = cstream + tc * (R / 2) + LB * g;
-          if constexpr (KS == 4) {
-            const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
-            wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
-          } else {
-            const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
-            wd[b][0] = v.x; wd[b][1] = v.y;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          f[b] = tokf[w][0][16 * (gr0 + b) + j];
-          f1[b] = tokf[w][1][16 * (gr0 + b) + j];
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int64_t t = t0 + 16 * (gr0 + b) + j;
-          f32x4 acc = acc0;
-#pragma unroll
-          for (int K = 0; K < KS; ++K)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, codes_to_sub16(wd[b][K])), acc, 0, 0, 0);
-          // rows 4 g + r: (head 2 g, hi), (2 g, lo), (2 g + 1, hi), (2 g + 1, lo) of this pass
-          if (t < T) {
-            const int h0 = hc * 8 + 2 * g;
-            float* sp = a.scores + (s * a.q_heads + kvh * G + h0) * T + t;
-            if constexpr (NS) {
-              if (h0 < G) sp[0] = __builtin_fmaf(acc.x + acc.y, f[b], f1[b] * qo0);
-              if (h0 + 1 < G) sp[T] = __builtin_fmaf(acc.z + acc.w, f[b], f1[b] * qo1);
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t lt = 16u * (gr0 + b) + j;
+            const unsigned char* cp = FULL ? cj + 16 * (R / 2) * (gr0 + b) : cu + (lt < (uint32_t)lim ? lt : (uint32_t)lim) * (R / 2);
+            if constexpr (KS == 4) {
+              const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
+              wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
             } else {
-              if (h0 < G) sp[0] = (acc.x + acc.y) * f[b];
-              if (h0 + 1 < G) sp[T] = (acc.z + acc.w) * f[b];
+              const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
+              wd[b][0] = v.x; wd[b][1] = v.y;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            f[b] = tokf[w][0][16 * (gr0 + b) + j];
+            if constexpr (NS) f1[b] = tokf[w][1][16 * (gr0 + b) + j];
+          }
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            f32x4 acc = acc0;
+#pragma unroll
+            for (int K = 0; K < KS; ++K)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, codes_to_sub16(wd[b][K])), acc, 0, 0, 0);
+            // rows 4 g + r: even hi, even 2^10 lo, odd 16 hi, odd 16 2^10 lo of head hq
+            const float sum = __builtin_fmaf(__builtin_fmaf(acc.w, 0x1p-10f, acc.z), 0x1p-4f,
+                                             __builtin_fmaf(acc.y, 0x1p-10f, acc.x));
+            if (store && (FULL || 16 * (gr0 + b) + j <= lim)) {
+              if constexpr (NS) sp[16 * (gr0 + b)] = __builtin_fmaf(sum, f[b], f1[b] * qo);
+              else sp[16 * (gr0 + b)] = sum * f[b];
             }
           }
         }
-      }
+      };
+      if (lim == U - 1) groups(std::true_type{});
+      else groups(std::false_type{});
     }
   }
 }
