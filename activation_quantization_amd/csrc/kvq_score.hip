@@ -52,9 +52,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
                                                     int vec_scales) {
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
   constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
-  // rotated queries of this KV head's group: [head][part: x1, x2^10][parity][R / 2] (zero past G)
-  __shared__ __attribute__((aligned(16))) float qa[16 * 2 * R];
-  __shared__ __attribute__((aligned(16))) float qr[16 * R];   // the rotation's work area
+  constexpr int UMAX = R == 64 ? 256 : 128;                 // largest unit (scale block)
+  constexpr int SROW = UMAX + 16;                           // staged score row (padded: no bank conflicts)
+  // rotated queries of this KV head's group: [head][parity][R / 2] (zero past G)
+  __shared__ __attribute__((aligned(16))) float qa[16 * R];
+  // the rotation's work area, then per wave the scores of one unit and pass: [4 heads][SROW]
+  __shared__ __attribute__((aligned(16))) float qs[4 * 4 * SROW > 16 * R ? 4 * 4 * SROW : 16 * R];
+  float* const qr = qs;
   __shared__ float qob[NS ? SCORE_UNITS_PER_BLOCK : 1][16];  // NSN: q . offset per (unit, query head)
   __shared__ __attribute__((aligned(16))) uint16_t qh[NS ? 16 * R : 8];   // NSN: fp16 queries (zero rows past G)
   __shared__ float tokf[4][2][256];   // per wave, the unit's tokens: norm 2^24 token-scale s2, and norm
@@ -88,13 +92,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     }
     __syncthreads();
   }
-  // the A-operand table: both parts' scalings (exact powers of two) and the channels split by parity
+  // the A-operand table, the channels split by parity
   for (int e = tid; e < 4 * NHC * R; e += 256) {
     const int hh = e / R, d = e % R;
-    const float v = hh < G ? (a.lg_had ? qr[e] * a.inv_sqrt_n : qr[e]) : 0.f;
-    float* row = qa + hh * 2 * R + (d & 1) * (R / 2) + (d >> 1);
-    row[0] = v;
-    row[R] = v * 0x1p10f;
+    qa[hh * R + (d & 1) * (R / 2) + (d >> 1)] = hh < G ? (a.lg_had ? qr[e] * a.inv_sqrt_n : qr[e]) : 0.f;
   }
 
   // NSN: the original-domain fp16 queries, the A operand of q . offset on the matrix cores (row i =
@@ -155,6 +156,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
   // this lane's A row: part (j & 1: hi or 2^10 lo), channel parity p = (j >> 1) & 1
   const int par = (j >> 1) & 1;
   const uint32_t lo_mask = (j & 1) ? HI_MASK : 0u;          // g - (g & mask): g itself, or its low part
+  const float part = (j & 1) ? 0x1p10f : 1.f;               // the low part's exact scaling
+  float* const stg = qs + w * 4 * SROW;                     // this wave's score staging rows
+  const bool vec_out = (T & 3) == 0 && ((uintptr_t)a.scores & 15u) == 0;
   const uint32_t keep = par ? 0u : 0xFFFFFFFFu;             // even rows fill words 0, 2; odd rows 1, 3
 
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
@@ -180,19 +184,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
           const u32x4 v = *(const u32x4*)(srow + 8 * K);
           const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((wv[i] >> (16 * par)) & 0xffffu);
+          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((wv[i] >> (16 * par)) & 0xffffu) * part;
         }
       } else {
 #pragma unroll
         for (int K = 0; K < KS; ++K)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32(srow[8 * K + 2 * i + par]);
+          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32(srow[8 * K + 2 * i + par]) * part;
       }
     } else {
 #pragma unroll
       for (int K = 0; K < KS; ++K)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[K][i] = 1.f;
+        for (int i = 0; i < 4; ++i) sc[K][i] = part;
     }
     // f = norm 2^24 token-scale (s2), f1 = norm (a mode without the value reads the constant 1.0)
 #pragma unroll
@@ -213,7 +217,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     for (int hc = 0; hc < NHC; ++hc) {
       // A operand of row j: g (x 2^10 for the low part) of the lane's parity, its high part
       // truncated by the fp16 conversion or its low part left after the mask
-      const float* qp = qa + ((4 * hc + (j >> 2)) * 2 + (j & 1)) * R + par * (R / 2) + (R / 8) * g;
+      const float* qp = qa + (4 * hc + (j >> 2)) * R + par * (R / 2) + (R / 8) * g;
       f16x8 av[KS];
 #pragma unroll
       for (int K = 0; K < KS; ++K) {
@@ -239,9 +243,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u}), acc0, 0, 0, 0);
       acc0 *= -8.f * 0x1p-24f;
-      const int hq = 4 * hc + g;                            // this lane's query head in the group
-      float* sp = a.scores + (s * a.q_heads + kvh * G + (hq < G ? hq : 0)) * T + t0 + j;
-      const bool store = hq < G;
+      float* const srow_l = stg + g * SROW + j;             // this lane's head of the pass, token j
       // 16-token groups, four at a time: every load of the four first, then the products.  A whole
       // unit loads at fixed offsets from the lane's token; the stream's last, partial unit clamps
       // each token to the last one and stores only tokens inside the stream.
@@ -278,15 +280,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
             // rows 4 g + r: even hi, even 2^10 lo, odd 16 hi, odd 16 2^10 lo of head hq
             const float sum = __builtin_fmaf(__builtin_fmaf(acc.w, 0x1p-10f, acc.z), 0x1p-4f,
                                              __builtin_fmaf(acc.y, 0x1p-10f, acc.x));
-            if (store && (FULL || 16 * (gr0 + b) + j <= lim)) {
-              if constexpr (NS) sp[16 * (gr0 + b)] = __builtin_fmaf(sum, f[b], f1[b] * qo);
-              else sp[16 * (gr0 + b)] = sum * f[b];
-            }
+            if constexpr (NS) srow_l[16 * (gr0 + b)] = __builtin_fmaf(sum, f[b], f1[b] * qo);
+            else srow_l[16 * (gr0 + b)] = sum * f[b];
           }
         }
       };
       if (lim == U - 1) groups(std::true_type{});
       else groups(std::false_type{});
+      // the pass's 4 x U scores out as whole rows: lane l of step c takes 4 tokens of one head
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+      float* const orow0 = a.scores + (s * a.q_heads + kvh * G + 4 * hc) * T + t0;
+      for (int c = 0; c < U / 64; ++c) {
+        const int e = 256 * c + 4 * lane, hh = e / U, tk = e % U;
+        const f32x4 v = *(const f32x4*)(stg + hh * SROW + tk);
+        if (4 * hc + hh < G) {
+          float* op = orow0 + hh * T + tk;
+          if (vec_out && tk + 3 <= lim) {
+            __builtin_nontemporal_store(v, (f32x4*)op);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (tk + r <= lim) op[r] = v[r];
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
     }
   }
 }
