@@ -47,13 +47,14 @@ __device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
 constexpr uint32_t HI_MASK = 0xFFFFE000u;      // fp32 bits that survive truncation to fp16 precision
 
-template <int R, bool NS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks, int U,
+// U: tokens per unit (the scale block, or 128 per token).  WHOLE: every unit lies inside the stream
+// and the fp32 score rows take 16-byte stores (the launcher checks T % U, T % 4 and alignment).
+template <int R, bool NS, int U, bool WHOLE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) score_kernel(ScoreArgs a, int64_t ntiles, int64_t nchunks,
                                                     int vec_scales) {
   constexpr int KS = R / 32;               // MFMA K steps of 32 channels
   constexpr int LB = R / 8;                // code bytes per lane and token (lanes 16 g + j: bytes LB g ..)
-  constexpr int UMAX = R == 64 ? 256 : 128;                 // largest unit (scale block)
-  constexpr int SROW = UMAX + 16;                           // staged score row (padded: no bank conflicts)
+  constexpr int SROW = U + 16;                              // staged score row (padded: no bank conflicts)
   // rotated queries of this KV head's group: [head][parity][R / 2] (zero past G)
   __shared__ __attribute__((aligned(16))) float qa[16 * R];
   // the rotation's work area, then per wave the scores of one unit and pass: [4 heads][SROW]
@@ -110,7 +111,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
   const unsigned char* cstream = a.codes + sh * T * (R / 2);
   const int64_t tstream = sh * T;                           // index of the stream's first token
   const int64_t nb = a.per_channel ? T / a.block : 0;
-  const int ngr = U / 16;                                   // 16-token groups per unit
   const uint16_t* nrm_p = a.nsep ? a.norms + tstream : kF16One;              // per-token norms
   const uint16_t* tsc_p = a.per_channel ? kF16One : a.scales + tstream;      // per-token scales
 
@@ -158,156 +158,172 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
   const uint32_t lo_mask = (j & 1) ? HI_MASK : 0u;          // g - (g & mask): g itself, or its low part
   const float part = (j & 1) ? 0x1p10f : 1.f;               // the low part's exact scaling
   float* const stg = qs + w * 4 * SROW;                     // this wave's score staging rows
-  const bool vec_out = (T & 3) == 0 && ((uintptr_t)a.scores & 15u) == 0;
   const uint32_t keep = par ? 0u : 0xFFFFFFFFu;             // even rows fill words 0, 2; odd rows 1, 3
 
-  for (int64_t un = u_begin + w; un < u_end; un += 4) {
-    const int64_t t0 = un * U;
-    // the unit's per-token factors: coalesced 2-byte loads by all lanes (token t0 + lane + 64 k,
-    // clamped to the last token), issued before the scale loads, into this wave's LDS table
-    uint16_t nv[4], sv[4], s2v[4];
+  // A pass's scores stay in the staging rows until the next pass has issued its first code loads:
+  // loads and stores retire in order through one counter, so a store issued before a load would be
+  // waited for with it.  With WHOLE units the stores are unconditional and fixed in number (lanes
+  // past the pass's last head rewrite that head's row with the same values), so the compiler's
+  // counter waits for the next loads do not include them.
+  float* pend = nullptr;                                    // head row 0 of the pending pass
+  int pend_lim = U - 1, pend_heads = 4;
+  auto flush = [&]() {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t tt = t0 + lane + 64 * k;
-      const int64_t tc = tt < T ? tt : T - 1;
-      nv[k] = nrm_p[a.nsep ? tc : 0];
-      sv[k] = tsc_p[a.per_channel ? 0 : tc];
-      if constexpr (NS) s2v[k] = a.s2[tstream + tc];
+    for (int c = 0; c < U / 64; ++c) {
+      const int e = 256 * c + 4 * lane, tk = e % U;
+      const int hh = WHOLE ? (e / U < pend_heads ? e / U : pend_heads - 1) : e / U;
+      const f32x4 v = *(const f32x4*)(stg + hh * SROW + tk);
+      float* op = pend + hh * T + tk;
+      if constexpr (WHOLE) {
+        __builtin_nontemporal_store(v, (f32x4*)op);
+      } else if (hh < pend_heads) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tk + r <= pend_lim) op[r] = v[r];
+      }
     }
-    // scales of this lane's channels of its parity: (R / 4) g + 8 K + 2 i + par, i = 0..3
-    float sc[KS][4];
-    if (a.per_channel) {
-      const uint16_t* srow = a.scales + (sh * nb + un) * R + (R / 4) * g;
-      if (vec_scales) {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int64_t first = u_begin + w;
+  const int nsteps = first < u_end ? (int)((u_end - first + 3) / 4) * NHC : 0;   // (unit, pass) steps
+  float sc[KS][4];
+  // one (unit, pass) step; the first step of the wave has no pending scores to write
+  auto step = [&](int it, auto flush_tag) {
+    constexpr bool FLUSH = decltype(flush_tag)::value;
+    const int hc = it % NHC;
+    const int64_t un = first + 4 * (it / NHC);
+    const int64_t t0 = un * U;
+    if (hc == 0) {
+      // the unit's per-token factors: coalesced 2-byte loads by all lanes (token t0 + lane + 64 k,
+      // clamped to the last token), issued before the scale loads, into this wave's LDS table
+      uint16_t nv[4], sv[4], s2v[4];
 #pragma unroll
-        for (int K = 0; K < KS; ++K) {
-          const u32x4 v = *(const u32x4*)(srow + 8 * K);
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      for (int k = 0; k < 4; ++k) {
+        const int64_t tt = t0 + lane + 64 * k;
+        const int64_t tc = tt < T ? tt : T - 1;
+        nv[k] = nrm_p[a.nsep ? tc : 0];
+        sv[k] = tsc_p[a.per_channel ? 0 : tc];
+        if constexpr (NS) s2v[k] = a.s2[tstream + tc];
+      }
+      // scales of this lane's channels of its parity: (R / 4) g + 8 K + 2 i + par, i = 0..3
+      if (a.per_channel) {
+        const uint16_t* srow = a.scales + (sh * nb + un) * R + (R / 4) * g;
+        if (vec_scales) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((wv[i] >> (16 * par)) & 0xffffu) * part;
+          for (int K = 0; K < KS; ++K) {
+            const u32x4 v = *(const u32x4*)(srow + 8 * K);
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((wv[i] >> (16 * par)) & 0xffffu) * part;
+          }
+        } else {
+#pragma unroll
+          for (int K = 0; K < KS; ++K)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32(srow[8 * K + 2 * i + par]) * part;
         }
       } else {
 #pragma unroll
         for (int K = 0; K < KS; ++K)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32(srow[8 * K + 2 * i + par]) * part;
+          for (int i = 0; i < 4; ++i) sc[K][i] = part;
       }
-    } else {
+      // f = norm 2^24 token-scale (s2), f1 = norm (a mode without the value reads the constant 1.0)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (64 * k < U) {
+          const float n1 = f16_to_f32(nv[k]);
+          float fk = n1 * 0x1p24f * f16_to_f32(sv[k]);
+          if constexpr (NS) fk *= f16_to_f32(s2v[k]);
+          tokf[w][0][lane + 64 * k] = fk;
+          tokf[w][1][lane + 64 * k] = n1;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    }
+    // tokens of this unit past the stream's end read the last token (their scores are not stored)
+    const int lim = WHOLE ? U - 1 : (T - t0 < U ? (int)(T - 1 - t0) : U - 1);
+    const unsigned char* cu = cstream + t0 * (R / 2) + LB * g;
+    // A operand of row j: g (x 2^10 for the low part) of the lane's parity, its high part
+    // truncated by the fp16 conversion or its low part left after the mask
+    const float* qp = qa + (4 * hc + (j >> 2)) * R + par * (R / 2) + (R / 8) * g;
+    f16x8 av[KS];
+#pragma unroll
+    for (int K = 0; K < KS; ++K) {
+      const f32x4 q4 = *(const f32x4*)(qp + 4 * K);
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gv = q4[i] * sc[K][i];
+        v[i] = gv - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gv) & lo_mask);
+      }
+      const uint32_t w02 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[0], v[2]));
+      const uint32_t w13 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[1], v[3]));
+      av[K] = __builtin_bit_cast(f16x8, u32x4{w02 & keep, w02 & ~keep, w13 & keep, w13 & ~keep});
+    }
+    // NSN: q . offset of this lane's head for the unit
+    float qo = 0.f;
+    if constexpr (NS) qo = qob[un - u_begin][4 * hc + g < 16 ? 4 * hc + g : 15];
+    // accumulator start: -8 2^-24 sum_k A[i][k] m_k, from one more product with B = m (1 for the
+    // even-channel slots, 16 for the odd ones; lane (g, j) receives rows 4 g + r)
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = 0; K < KS; ++K)
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u}), acc0, 0, 0, 0);
+    acc0 *= -8.f * 0x1p-24f;
+    float* const srow_l = stg + g * SROW + j;               // this lane's head of the pass, token j
+    // the unit's 16-token groups: every code load first (ascending, so each group waits only for
+    // its own), then the pending pass's stores, then the products group by group.  A whole unit
+    // loads at fixed offsets from the lane's token; a partial last unit clamps each token to the
+    // stream's last one.
+    constexpr int NG = U / 16;
+    const unsigned char* cj = cu + j * (R / 2);
+    uint32_t wd[NG][KS];
+#pragma unroll
+    for (int b = 0; b < NG; ++b) {
+      const uint32_t lt = 16u * b + j;
+      const unsigned char* cp = (WHOLE || lim == U - 1) ? cj + 16 * (R / 2) * b
+                                                        : cu + (lt < (uint32_t)lim ? lt : (uint32_t)lim) * (R / 2);
+      if constexpr (KS == 4) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
+        wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
+      } else {
+        const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
+        wd[b][0] = v.x; wd[b][1] = v.y;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FLUSH) flush();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NG; ++b) {
+      const float f = tokf[w][0][16 * b + j];
+      f32x4 acc = acc0;
 #pragma unroll
       for (int K = 0; K < KS; ++K)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[K][i] = part;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, codes_to_sub16(wd[b][K])), acc, 0, 0, 0);
+      // rows 4 g + r: even hi, even 2^10 lo, odd 16 hi, odd 16 2^10 lo of head 4 hc + g
+      const float sum = __builtin_fmaf(__builtin_fmaf(acc.w, 0x1p-10f, acc.z), 0x1p-4f,
+                                       __builtin_fmaf(acc.y, 0x1p-10f, acc.x));
+      if constexpr (NS) srow_l[16 * b] = __builtin_fmaf(sum, f, tokf[w][1][16 * b + j] * qo);
+      else srow_l[16 * b] = sum * f;
     }
-    // f = norm 2^24 token-scale (s2), f1 = norm (a mode without the value reads the constant 1.0)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (64 * k < U) {
-        const float n1 = f16_to_f32(nv[k]);
-        float fk = n1 * 0x1p24f * f16_to_f32(sv[k]);
-        if constexpr (NS) fk *= f16_to_f32(s2v[k]);
-        tokf[w][0][lane + 64 * k] = fk;
-        tokf[w][1][lane + 64 * k] = n1;
-      }
-    }
+    // this pass's 4 x U scores are written as whole rows (lane l of step c: 4 tokens of one head)
+    // once the next pass has its first loads in flight
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    // tokens of this unit past the stream's end read the last token (their scores are not stored)
-    const int lim = T - t0 < U ? (int)(T - 1 - t0) : U - 1;
-    const unsigned char* cu = cstream + t0 * (R / 2) + LB * g;
-    for (int hc = 0; hc < NHC; ++hc) {
-      // A operand of row j: g (x 2^10 for the low part) of the lane's parity, its high part
-      // truncated by the fp16 conversion or its low part left after the mask
-      const float* qp = qa + (4 * hc + (j >> 2)) * R + par * (R / 2) + (R / 8) * g;
-      f16x8 av[KS];
-#pragma unroll
-      for (int K = 0; K < KS; ++K) {
-        const f32x4 q4 = *(const f32x4*)(qp + 4 * K);
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = q4[i] * sc[K][i];
-          v[i] = gv - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gv) & lo_mask);
-        }
-        const uint32_t w02 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[0], v[2]));
-        const uint32_t w13 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[1], v[3]));
-        av[K] = __builtin_bit_cast(f16x8, u32x4{w02 & keep, w02 & ~keep, w13 & keep, w13 & ~keep});
-      }
-      // NSN: q . offset of this lane's head for the unit
-      float qo = 0.f;
-      if constexpr (NS) qo = qob[un - u_begin][4 * hc + g < 16 ? 4 * hc + g : 15];
-      // accumulator start: -8 2^-24 sum_k A[i][k] m_k, from one more product with B = m (1 for the
-      // even-channel slots, 16 for the odd ones; lane (g, j) receives rows 4 g + r)
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int K = 0; K < KS; ++K)
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u}), acc0, 0, 0, 0);
-      acc0 *= -8.f * 0x1p-24f;
-      float* const srow_l = stg + g * SROW + j;             // this lane's head of the pass, token j
-      // 16-token groups, four at a time: every load of the four first, then the products.  A whole
-      // unit loads at fixed offsets from the lane's token; the stream's last, partial unit clamps
-      // each token to the last one and stores only tokens inside the stream.
-      auto groups = [&](auto full_unit) {
-        constexpr bool FULL = decltype(full_unit)::value;
-        const unsigned char* cj = cu + j * (R / 2);
-        for (int gr0 = 0; gr0 < ngr; gr0 += 4) {
-          uint32_t wd[4][KS];
-          float f[4], f1[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t lt = 16u * (gr0 + b) + j;
-            const unsigned char* cp = FULL ? cj + 16 * (R / 2) * (gr0 + b) : cu + (lt < (uint32_t)lim ? lt : (uint32_t)lim) * (R / 2);
-            if constexpr (KS == 4) {
-              const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
-              wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
-            } else {
-              const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
-              wd[b][0] = v.x; wd[b][1] = v.y;
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            f[b] = tokf[w][0][16 * (gr0 + b) + j];
-            if constexpr (NS) f1[b] = tokf[w][1][16 * (gr0 + b) + j];
-          }
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            f32x4 acc = acc0;
-#pragma unroll
-            for (int K = 0; K < KS; ++K)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, codes_to_sub16(wd[b][K])), acc, 0, 0, 0);
-            // rows 4 g + r: even hi, even 2^10 lo, odd 16 hi, odd 16 2^10 lo of head hq
-            const float sum = __builtin_fmaf(__builtin_fmaf(acc.w, 0x1p-10f, acc.z), 0x1p-4f,
-                                             __builtin_fmaf(acc.y, 0x1p-10f, acc.x));
-            if constexpr (NS) srow_l[16 * (gr0 + b)] = __builtin_fmaf(sum, f[b], f1[b] * qo);
-            else srow_l[16 * (gr0 + b)] = sum * f[b];
-          }
-        }
-      };
-      if (lim == U - 1) groups(std::true_type{});
-      else groups(std::false_type{});
-      // the pass's 4 x U scores out as whole rows: lane l of step c takes 4 tokens of one head
-      __builtin_amdgcn_wave_barrier();
-      asm volatile("" ::: "memory");
-      float* const orow0 = a.scores + (s * a.q_heads + kvh * G + 4 * hc) * T + t0;
-      for (int c = 0; c < U / 64; ++c) {
-        const int e = 256 * c + 4 * lane, hh = e / U, tk = e % U;
-        const f32x4 v = *(const f32x4*)(stg + hh * SROW + tk);
-        if (4 * hc + hh < G) {
-          float* op = orow0 + hh * T + tk;
-          if (vec_out && tk + 3 <= lim) {
-            __builtin_nontemporal_store(v, (f32x4*)op);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (tk + r <= lim) op[r] = v[r];
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      asm volatile("" ::: "memory");
-    }
+    pend = a.scores + (s * a.q_heads + kvh * G + 4 * hc) * T + t0;
+    pend_lim = lim;
+    pend_heads = G - 4 * hc < 4 ? G - 4 * hc : 4;
+  };
+  if (nsteps > 0) {
+    step(0, std::false_type{});
+    for (int it = 1; it < nsteps; ++it) step(it, std::true_type{});
+    flush();
   }
 }
 
@@ -317,13 +333,28 @@ hipError_t launch_score_decode(const ScoreArgs& a, hipStream_t st) {
   const int64_t nchunks = (nunits + SCORE_UNITS_PER_BLOCK - 1) / SCORE_UNITS_PER_BLOCK;
   const int64_t ntiles = a.seqs * a.heads * nchunks;
   const int vec_scales = ((uintptr_t)a.scales & 15u) == 0 && (!a.nsn || ((uintptr_t)a.offsets & 15u) == 0);
+  const bool whole = a.tokens % U == 0 && a.tokens % 4 == 0 && ((uintptr_t)a.scores & 15u) == 0;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, U, vec_scales);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nchunks, vec_scales);
+  };
+  // per R and NSN flag: the unit size, then whole or partial units
+  auto by_u = [&](auto r_tag, auto ns_tag) {
+    constexpr int R = decltype(r_tag)::value;
+    constexpr bool NS = decltype(ns_tag)::value;
+    if (U == 64) {
+      if (whole) go(score_kernel<R, NS, 64, true>); else go(score_kernel<R, NS, 64, false>);
+    } else if (U == 128) {
+      if (whole) go(score_kernel<R, NS, 128, true>); else go(score_kernel<R, NS, 128, false>);
+    } else if constexpr (R == 64) {
+      if (whole) go(score_kernel<R, NS, 256, true>); else go(score_kernel<R, NS, 256, false>);
+    }
   };
   if (a.nsn) {
-    if (a.dim == 128) go(score_kernel<128, true>); else go(score_kernel<64, true>);
+    if (a.dim == 128) by_u(std::integral_constant<int, 128>{}, std::true_type{});
+    else by_u(std::integral_constant<int, 64>{}, std::true_type{});
   } else {
-    if (a.dim == 128) go(score_kernel<128, false>); else go(score_kernel<64, false>);
+    if (a.dim == 128) by_u(std::integral_constant<int, 128>{}, std::false_type{});
+    else by_u(std::integral_constant<int, 64>{}, std::false_type{});
   }
   return hipGetLastError();
 }

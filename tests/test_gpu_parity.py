@@ -225,7 +225,10 @@ def test_long_context_decode_full_sampled():
 
 
 @pytest.mark.parametrize("mode", oracle.MODES)
-@pytest.mark.parametrize("dim,G,T,had", [(128, 4, 512, 128), (64, 1, 256, 0), (128, 16, 384, 32), (64, 8, 200, 64)])
+# G = 3 on whole units: the lanes past the pass's last head rewrite that head's row; T = 201: the
+# score rows take 4-byte stores and the last unit is partial
+@pytest.mark.parametrize("dim,G,T,had", [(128, 4, 512, 128), (64, 1, 256, 0), (128, 16, 384, 32), (64, 8, 200, 64),
+                                         (128, 3, 256, 128), (64, 2, 201, 0)])
 def test_score_shapes_and_modes(mode, dim, G, T, had):
     if "pchan" in mode and T % 64:
         pytest.skip("per-channel blocks must divide the sequence")
