@@ -35,7 +35,7 @@ __device__ __forceinline__ void unsign(float (&y)[R], const int8_t* __restrict__
 
 // signed 4-bit code e of a packed word, as float
 __device__ __forceinline__ float nib_f(uint32_t word, int e) {
-  return (float)((int)((word >> (4 * e)) & 0xfu ^ 8u) - 8);
+  return (float)((int)(((word >> (4 * e)) & 0xfu) ^ 8u) - 8);
 }
 
 // Write row `row` (R values) into the LDS output tile in the output dtype.

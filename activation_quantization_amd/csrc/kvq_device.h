@@ -103,6 +103,16 @@ __device__ __forceinline__ float shfl_f(float v, int src) {
 // fp16 1.0: the per-token norm or scale of a mode that has none, read like a real one (no branch
 // between the load and its use)
 static __device__ const uint16_t kF16One[1] = {0x3C00u};
+// four fp16 ones, 8-byte aligned: the per-token factors of a mode that stores none
+static __device__ __attribute__((aligned(8))) const uint16_t kF16Ones4[4] = {0x3C00u, 0x3C00u, 0x3C00u, 0x3C00u};
+
+// A load through a global-address-space pointer.  A pointer that may be a kernel argument or a
+// device constant is generic to the compiler, and a load through it is a flat load, which the
+// compiler can only wait for together with every other load and store in flight.
+template <typename V>
+__device__ __forceinline__ V ld_global(const V* p) {
+  return *(const __attribute__((address_space(1))) V*)p;
+}
 
 // ------------------------------------------------------------------ code packing
 // Codes by one fma into [128, 256), where the fp32 ulp is 2^-16: b = bits(v + 136.5) has code + 8

@@ -45,6 +45,7 @@ __device__ __forceinline__ u32x4 codes_to_sub16(uint32_t word) {
 }
 
 constexpr int SCORE_UNITS_PER_BLOCK = 16;
+
 constexpr uint32_t HI_MASK = 0xFFFFE000u;      // fp32 bits that survive truncation to fp16 precision
 
 // U: tokens per unit (the scale block, or 128 per token).  WHOLE: every unit lies inside the stream
@@ -195,35 +196,69 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     const int hc = it % NHC;
     const int64_t un = first + 4 * (it / NHC);
     const int64_t t0 = un * U;
+    // A unit's first pass loads its per-token factors (coalesced 2-byte loads by all lanes, token
+    // t0 + lane + 64 k clamped to the last token) and the scales of this lane's channels of its
+    // parity ((R / 4) g + 8 K + 2 i + par), then every code load of the unit, then the pending
+    // stores; only then does it wait, for the factors and scales alone.
+    uint16_t nv[4], sv[4], s2v[4];
+    uint32_t sraw[KS][4];                                   // scale bits (shifted by sshift)
+    const int sshift = vec_scales ? 16 * par : 0;
     if (hc == 0) {
-      // the unit's per-token factors: coalesced 2-byte loads by all lanes (token t0 + lane + 64 k,
-      // clamped to the last token), issued before the scale loads, into this wave's LDS table
-      uint16_t nv[4], sv[4], s2v[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t tt = t0 + lane + 64 * k;
         const int64_t tc = tt < T ? tt : T - 1;
-        nv[k] = nrm_p[a.nsep ? tc : 0];
-        sv[k] = tsc_p[a.per_channel ? 0 : tc];
-        if constexpr (NS) s2v[k] = a.s2[tstream + tc];
+        nv[k] = ld_global(nrm_p + (a.nsep ? tc : 0));
+        sv[k] = ld_global(tsc_p + (a.per_channel ? 0 : tc));
+        if constexpr (NS) s2v[k] = ld_global(a.s2 + tstream + tc);
       }
-      // scales of this lane's channels of its parity: (R / 4) g + 8 K + 2 i + par, i = 0..3
       if (a.per_channel) {
         const uint16_t* srow = a.scales + (sh * nb + un) * R + (R / 4) * g;
         if (vec_scales) {
 #pragma unroll
           for (int K = 0; K < KS; ++K) {
-            const u32x4 v = *(const u32x4*)(srow + 8 * K);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((wv[i] >> (16 * par)) & 0xffffu) * part;
+            const u32x4 v = ld_global((const u32x4*)(srow + 8 * K));
+            sraw[K][0] = v.x; sraw[K][1] = v.y; sraw[K][2] = v.z; sraw[K][3] = v.w;
           }
         } else {
 #pragma unroll
           for (int K = 0; K < KS; ++K)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32(srow[8 * K + 2 * i + par]) * part;
+            for (int i = 0; i < 4; ++i) sraw[K][i] = ld_global(srow + 8 * K + 2 * i + par);
         }
+      }
+    }
+    // tokens of this unit past the stream's end read the last token (their scores are not stored)
+    const int lim = WHOLE ? U - 1 : (T - t0 < U ? (int)(T - 1 - t0) : U - 1);
+    const unsigned char* cu = cstream + t0 * (R / 2) + LB * g;
+    // the unit's 16-token groups (ascending, so each group waits only for its own); a whole unit
+    // loads at fixed offsets from the lane's token, a partial last unit clamps each token to the
+    // stream's last one
+    constexpr int NG = U / 16;
+    const unsigned char* cj = cu + j * (R / 2);
+    uint32_t wd[NG][KS];
+#pragma unroll
+    for (int b = 0; b < NG; ++b) {
+      const uint32_t lt = 16u * b + j;
+      const unsigned char* cp = (WHOLE || lim == U - 1) ? cj + 16 * (R / 2) * b
+                                                        : cu + (lt < (uint32_t)lim ? lt : (uint32_t)lim) * (R / 2);
+      if constexpr (KS == 4) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
+        wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
+      } else {
+        const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
+        wd[b][0] = v.x; wd[b][1] = v.y;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FLUSH) flush();
+    __builtin_amdgcn_sched_barrier(0);
+    if (hc == 0) {
+      if (a.per_channel) {
+#pragma unroll
+        for (int K = 0; K < KS; ++K)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[K][i] = f16_to_f32((sraw[K][i] >> sshift) & 0xffffu) * part;
       } else {
 #pragma unroll
         for (int K = 0; K < KS; ++K)
@@ -244,9 +279,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
       __builtin_amdgcn_wave_barrier();
       asm volatile("" ::: "memory");
     }
-    // tokens of this unit past the stream's end read the last token (their scores are not stored)
-    const int lim = WHOLE ? U - 1 : (T - t0 < U ? (int)(T - 1 - t0) : U - 1);
-    const unsigned char* cu = cstream + t0 * (R / 2) + LB * g;
     // A operand of row j: g (x 2^10 for the low part) of the lane's parity, its high part
     // truncated by the fp16 conversion or its low part left after the mask
     const float* qp = qa + (4 * hc + (j >> 2)) * R + par * (R / 2) + (R / 8) * g;
@@ -276,29 +308,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
           av[K], __builtin_bit_cast(f16x8, u32x4{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u}), acc0, 0, 0, 0);
     acc0 *= -8.f * 0x1p-24f;
     float* const srow_l = stg + g * SROW + j;               // this lane's head of the pass, token j
-    // the unit's 16-token groups: every code load first (ascending, so each group waits only for
-    // its own), then the pending pass's stores, then the products group by group.  A whole unit
-    // loads at fixed offsets from the lane's token; a partial last unit clamps each token to the
-    // stream's last one.
-    constexpr int NG = U / 16;
-    const unsigned char* cj = cu + j * (R / 2);
-    uint32_t wd[NG][KS];
-#pragma unroll
-    for (int b = 0; b < NG; ++b) {
-      const uint32_t lt = 16u * b + j;
-      const unsigned char* cp = (WHOLE || lim == U - 1) ? cj + 16 * (R / 2) * b
-                                                        : cu + (lt < (uint32_t)lim ? lt : (uint32_t)lim) * (R / 2);
-      if constexpr (KS == 4) {
-        const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
-        wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
-      } else {
-        const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
-        wd[b][0] = v.x; wd[b][1] = v.y;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (FLUSH) flush();
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < NG; ++b) {
       const float f = tokf[w][0][16 * b + j];
