@@ -38,7 +38,7 @@ namespace {
 
 using namespace rot;
 
-constexpr int PT_ROWS = 128;   // rows per tile
+constexpr int PT_ROWS = 64;    // rows per tile (16 per wave; a vector of at most 64 rows fits)
 constexpr float PT_MAGIC = 136.5f;
 
 template <int CTL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -74,10 +74,10 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[PT_ROWS * ROWB];   // the tile's rows (signed)
   __shared__ __attribute__((aligned(16))) unsigned char cstage[PT_ROWS * RB];    // the tile's code rows
   __shared__ __attribute__((aligned(16))) uint32_t pmax[PT_ROWS][4];            // per (vector, wave) max bits
-  __shared__ __attribute__((aligned(8))) float psum[PT_ROWS][2];               // per vector sums of squares
+  __shared__ __attribute__((aligned(16))) float psum[PT_ROWS][4];              // per vector partial sums of squares
   __shared__ uint32_t vflag[PT_ROWS / 32];                                      // vectors holding a near-tie
   __shared__ uint64_t xmax[PT_ROWS];                                            // their exact max (fp64 bits)
-  __shared__ float dinv_s[PT_ROWS / 2];                                         // RRS: 1 / smoothing scale per segment
+  __shared__ float dinv_s[64];                                                  // RRS: 1 / smoothing scale per segment
 
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -88,7 +88,10 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
   const int lgJ = lgL < 4 ? lgL : 4;            // log2 rows of one vector inside a sub-tile
   const int lgS = lgL > 4 ? lgL - 4 : 0;        // log2 sub-tiles one vector spans
   if (tid < PT_ROWS / 32) vflag[tid] = 0u;
-  if (tid < PT_ROWS) xmax[tid] = 0ull;
+  if (tid < PT_ROWS) {
+    xmax[tid] = 0ull;
+    *(f32x4*)psum[tid] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // 1. this wave's 32 rows into LDS: instruction k moves rows 32 w + 4 k + g, lane slot j holding
   //    global chunk j ^ (row % 16); the sign bytes of those chunks come along into registers
@@ -151,13 +154,16 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
     return *(const u32x4*)(stage + 16 * s * ROWB + (j * ROWB + 16 * ((4 * K + g) ^ (j % CPR))));
   };
 
-  // 3. NSEP: sums of squares of this wave's own rows (sub-tiles 2 w, 2 w + 1) from the diagonal of
-  //    the Gram matrix, summed over each vector's rows; wave w's rows hold whole vectors when L <= 32
+  // 3. NSEP: sums of squares of this wave's own rows (its SW sub-tiles) from the diagonal of the Gram
+  //    matrix, summed over each vector's rows.  A vector of at most 16 rows lies in one sub-tile; a
+  //    longer one covers whole waves' rows (or a whole wave covers it), and each of its waves adds
+  //    one partial (slot w mod partials).
   if (a.nsep) {
+    constexpr int SW = ST / 4;                                // sub-tiles per wave
     float tot = 0.f;
 #pragma unroll
-    for (int o = 0; o < 2; ++o) {
-      const int s = 2 * w + o;
+    for (int o = 0; o < SW; ++o) {
+      const int s = SW * w + o;
       u32x4 x[NK];
 #pragma unroll
       for (int K = 0; K < NK; ++K) x[K] = read_x(s, K);
@@ -170,17 +176,15 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
                                                                          __builtin_bit_cast(int, dg)));
       ssq = group_sum(ssq, lgJ);
       if (lgS == 0) {
-        if (lane < 16 && (j & (L - 1)) == 0) {
-          const int v = (16 * s + j) >> lgL;
-          psum[v][0] = ssq;
-          psum[v][1] = 0.f;
-        }
+        if (lane < 16 && (j & (L - 1)) == 0) psum[(16 * s + j) >> lgL][0] = ssq;
       } else {
         tot += ssq;
       }
     }
-    if (lgS == 1 && lane == 0) { psum[w][0] = tot; psum[w][1] = 0.f; }
-    if (lgS == 2 && lane == 0) psum[w >> 1][w & 1] = tot;
+    if (lgS >= 1 && lane == 0) {
+      const int np = (L >> 4) / SW > 1 ? (L >> 4) / SW : 1;   // partials per vector
+      psum[(16 * SW * w) >> lgL][w & (np - 1)] = tot;
+    }
   }
 
   // 4. the rotation of this wave's channels, sub-tile by sub-tile.  The block sign beta(w, K) is a
@@ -273,7 +277,8 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
     const int64_t vh = head_major(a.heads, a.tokens, (row0 >> lgL) + tid);
     float scale = m * a.scale_mul;
     if (a.nsep) {
-      const float nu = sqrtf(psum[tid][0] + psum[tid][1]);
+      const f32x4 ps = *(const f32x4*)psum[tid];
+      const float nu = sqrtf((ps.x + ps.y) + (ps.z + ps.w));
       a.norms[vh] = (uint16_t)f32_to_f16(nu);
       scale = nu > 0.f ? scale / nu : 0.f;
     }
@@ -307,8 +312,14 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
   }
   lds_barrier();
 
-  const uint32_t vf0 = vflag[0], vf1 = vflag[1], vf2 = vflag[2], vf3 = vflag[3];
-  if ((vf0 | vf1 | vf2 | vf3) != 0u) {
+  constexpr int NVW = PT_ROWS / 32;                          // flag words (one bit per vector)
+  uint32_t vfw[NVW], vany = 0u;
+#pragma unroll
+  for (int k = 0; k < NVW; ++k) {
+    vfw[k] = vflag[k];
+    vany |= vfw[k];
+  }
+  if (vany != 0u) {
     // the rare path recomputes its row -> vector indices from an opaque copy of the shift, so the
     // main path does not keep them live for it
     int lgLr;
@@ -333,7 +344,9 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
       return y;
     };
     auto vflagged = [&](int v) {
-      const uint32_t wd = v < 32 ? vf0 : v < 64 ? vf1 : v < 96 ? vf2 : vf3;
+      uint32_t wd = vfw[0];
+#pragma unroll
+      for (int k = 1; k < NVW; ++k) wd = (v >> 5) == k ? vfw[k] : wd;
       return ((wd >> (v & 31)) & 1u) != 0u;
     };
     // Sub-tile by sub-tile, the rotated values are computed again (so the main path need not keep
@@ -406,7 +419,7 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
     // (b) the flagged values, decided from the exact quotient
     const double qd = (double)a.q;
 #pragma unroll 1
-    for (int sl = 0; sl < 64; ++sl) {
+    for (int sl = 0; sl < 8 * ST; ++sl) {
       for (uint64_t fb2 = __ballot((fmask >> sl) & 1ull); fb2; fb2 &= fb2 - 1ull) {
         const int l = __builtin_ctzll(fb2);
         const int r = 16 * (sl >> 3) + (l & 15);
@@ -428,14 +441,14 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
   if (a.heads == 1) {
     unsigned char* cb = a.codes + (row0 + (PT_ROWS / 4) * w) * RB;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int pc = 64 * k + lane;                          // piece of this wave's 32 rows
+    for (int k = 0; k < PT_ROWS / 64; ++k) {
+      const int pc = 64 * k + lane;                          // piece of this wave's rows
       if ((PT_ROWS / 4) * w + pc / 4 < nvalid)
         *(u32x4*)(cb + 16 * pc) = *(const u32x4*)(cstage + (PT_ROWS / 4) * w * RB + 16 * pc);
     }
   } else {
-    const int r = (PT_ROWS / 4) * w + (lane >> 1);
-    if (r < nvalid) {
+    const int r = (PT_ROWS / 4) * w + (lane >> 1);          // two lanes per row
+    if ((lane >> 1) < PT_ROWS / 4 && r < nvalid) {
       const int64_t rabs = row0 + r;
       const int64_t dst = (head_major(a.heads, a.tokens, rabs >> lgL) << lgL) + (rabs & (L - 1));
 #pragma unroll
@@ -470,6 +483,7 @@ void launch_lg(const QuantArgs& a, hipStream_t st, int64_t nrows, int lgL) {
 hipError_t launch_quantize_ptok_mfma(const QuantArgs& a, hipStream_t st) {
   int lgL = 0;
   while ((int64_t(128) << lgL) < a.dim) ++lgL;
+  if ((1 << lgL) > PT_ROWS) return hipErrorInvalidValue;   // a vector must fit in one tile
   const int64_t nrows = a.seqs * a.tokens * a.heads * (a.dim / 128);
   if (nrows > 0) {
     const bool rrs = a.seg_div != nullptr;
