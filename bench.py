@@ -80,18 +80,30 @@ def algorithmic_bytes(w, q_heads):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "long_context_hbm_traffic.md")
 
 
+def source_digest(sources: str):
+    """SHA-256 over the listed source files (comma-separated, repo-relative, in order), or None if
+    one is missing."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in sources.split(","):
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
-    or None when there is none or the kernel source has changed since it was taken."""
-    import hashlib
+    or None when there is none or a source of the kernel (its file and the headers it includes) has
+    changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     for line in open(TRAFFIC_FILE):
         f = line.split()
         if len(f) == 5 and f[0] == "traffic" and f[1] == kernel:
             kv = dict(x.split("=", 1) for x in f[2:])
-            src = os.path.join(ROOT, kv["source"])
-            if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == kv["sha256"]:
+            if source_digest(kv["source"]) == kv["sha256"]:
                 return int(kv["bytes_per_launch"])
     return None
 
