@@ -127,28 +127,41 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
   const uint16_t* vnp = a.nsep ? a.v_norms + tstream : kF16One;
   for (int64_t un = u_begin + w; un < u_end; un += 4) {
     const int64_t t0 = un * U;
-    // the block's V codes into LDS (U * 64 bytes, 1 KiB per instruction, linear)
-#pragma unroll
-    for (int k = 0; k < NGR; ++k)
-      __builtin_amdgcn_global_load_lds((const void*)(vstream + t0 * (R / 2) + k * 1024 + 16 * lane),
-                                       (__attribute__((address_space(3))) void*)(vw + k * 1024), 16, 0, 0);
-    // the block's K and V norms: coalesced 2-byte loads by all lanes (token t0 + lane + 64 k),
-    // issued with the scale loads, then kept in this wave's LDS table
+    // Every load of the block is issued before any is waited for, into registers and in the order
+    // they are needed: the K and V norms (coalesced 2-byte loads by all lanes, token t0 + lane +
+    // 64 k), the K and V scales, all of the block's K code groups (each group waited for on its
+    // own), and the V codes (U * 64 bytes, 16 per lane and KiB; written to LDS only when the value
+    // sum needs them).  All through
+    // global-address-space pointers, so the compiler counts the loads in flight exactly (copies
+    // into LDS, or flat loads, would make it wait for every load before the first LDS access).
     uint16_t kn[U / 64], vn[U / 64];
 #pragma unroll
     for (int k = 0; k < U / 64; ++k) {
       const int64_t tt = t0 + lane + 64 * k;
-      kn[k] = knp[a.nsep ? tt : 0];
-      vn[k] = vnp[a.nsep ? tt : 0];
+      kn[k] = ld_global(knp + (a.nsep ? tt : 0));
+      vn[k] = ld_global(vnp + (a.nsep ? tt : 0));
     }
     // K scales of this lane's channels (R/4) g + 8 K + nib(e); V scales of channels 8 vb ..
     // (scale rows are 16-byte aligned: the entry point requires it)
     const uint16_t* ksrow = a.k_scales + (sh * nb + un) * R + (R / 4) * g;
+    u32x4 ksw[KS];
+#pragma unroll
+    for (int K = 0; K < KS; ++K) ksw[K] = ld_global((const u32x4*)(ksrow + 8 * K));
+    const u32x4 vsw = ld_global((const u32x4*)(a.v_scales + (sh * nb + un) * R + 8 * vb));
+    uint32_t wd[NGR][KS];
+#pragma unroll
+    for (int b = 0; b < NGR; ++b) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(kstream + (t0 + 16 * b + j) * (R / 2) + LB * g));
+      wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
+    }
+    u32x4 vcw[NGR];                                         // V codes: lane's 16 bytes of each KiB
+#pragma unroll
+    for (int k = 0; k < NGR; ++k) vcw[k] = ld_global((const u32x4*)(vstream + t0 * (R / 2) + k * 1024 + 16 * lane));
+    __builtin_amdgcn_sched_barrier(0);
     float sc[KS * 8];
 #pragma unroll
     for (int K = 0; K < KS; ++K) {
-      const u32x4 v = *(const u32x4*)(ksrow + 8 * K);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t wv[4] = {ksw[K].x, ksw[K].y, ksw[K].z, ksw[K].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int n = att_nib(e);
@@ -157,8 +170,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     }
     float vs[8];
     {
-      const u32x4 v = *(const u32x4*)(a.v_scales + (sh * nb + un) * R + 8 * vb);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t wv[4] = {vsw.x, vsw.y, vsw.z, vsw.w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) vs[c] = f16_to_f32((c & 1) ? wv[c >> 1] >> 16 : wv[c >> 1] & 0xffffu);
     }
@@ -203,30 +215,15 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     // z[gr][0/1]: scaled scores of heads 2 g, 2 g + 1 for token 16 gr + j; nv: V norm of it
     float z[NGR][2], nvv[NGR];
 #pragma unroll
-    for (int gr0 = 0; gr0 < NGR; gr0 += 4) {
-      uint32_t wd[4][KS];
-      float fk[4];
+    for (int b = 0; b < NGR; ++b) {
+      const float fk = tokf[w][0][16 * b + j];
+      nvv[b] = tokf[w][1][16 * b + j];
+      f32x4 acc = acc0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t t = t0 + 16 * (gr0 + b) + j;
-        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(kstream + t * (R / 2) + LB * g));
-        wd[b][0] = v.x; wd[b][1] = v.y; wd[b][2] = v.z; wd[b][3] = v.w;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        fk[b] = tokf[w][0][16 * (gr0 + b) + j];
-        nvv[gr0 + b] = tokf[w][1][16 * (gr0 + b) + j];
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f32x4 acc = acc0;
-#pragma unroll
-        for (int K = 0; K < KS; ++K)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, att_codes_sub16(wd[b][K])), acc, 0, 0, 0);
-        z[gr0 + b][0] = (acc.x + acc.y) * fk[b];
-        z[gr0 + b][1] = (acc.z + acc.w) * fk[b];
-      }
+      for (int K = 0; K < KS; ++K)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[K], __builtin_bit_cast(f16x8, att_codes_sub16(wd[b][K])), acc, 0, 0, 0);
+      z[b][0] = (acc.x + acc.y) * fk;
+      z[b][1] = (acc.z + acc.w) * fk;
     }
 
     // 3. online softmax for the row's two heads.  The value weights p' = p * norm_v become
@@ -293,7 +290,8 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     //    D[4 h + b][j] of group m = sum_t W_b(t) (c_t + 8), column j = channel 8 j + m.  Lane
     //    (kg, j) reads word j (channels 8 j .. 8 j + 7) of its 16 tokens of the K step and takes
     //    nibble m of each as a byte; a ninth product with B = 8 gives the bias 8 sum_t W_b(t).
-    __builtin_amdgcn_s_waitcnt(0x0070);                   // the V codes (and everything else) landed
+#pragma unroll
+    for (int k = 0; k < NGR; ++k) *(u32x4*)&vbuf[w][k * 1024 + 16 * lane] = vcw[k];
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
     i32x4 acc[9];
