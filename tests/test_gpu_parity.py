@@ -128,7 +128,7 @@ def _sampled_tiles(d: kvq.Desc, x_cpu, signs_cpu, codes, norms, scales, n_tiles,
     dequantization of the GPU's own codes, norms and scales."""
     rng = np.random.default_rng(seed)
     B, nb = d.block_tokens, d.tokens_per_seq // d.block_tokens
-    gc, gn, gs = (t.cpu() for t in kvq.token_major(d, codes, norms, scales))
+    gc, gn, gs = (None if t is None else t.cpu() for t in kvq.token_major(d, codes, norms, scales))
     flips, checked = 0, 0
     tiles = [(0, 0, 0), (d.seqs - 1, nb - 1, d.heads - 1)]
     tiles += [(int(rng.integers(d.seqs)), int(rng.integers(nb)), int(rng.integers(d.heads))) for _ in range(n_tiles)]
@@ -142,10 +142,12 @@ def _sampled_tiles(d: kvq.Desc, x_cpu, signs_cpu, codes, norms, scales, n_tiles,
         st = parity.check_codes(c, ref, d.bits, sampled_from=d.rows * d.heads * d.head_dim)
         flips += st["tie_flips"]
         checked += st["codes"]
-        parity.check_rel_f16(gn[r0:r0 + B, h:h + 1].numpy(), ref.nu, "norms")
+        if gn is not None:
+            parity.check_rel_f16(gn[r0:r0 + B, h:h + 1].numpy(), ref.nu, "norms")
         parity.check_rel_f16(gs[s * nb + b, h:h + 1].numpy()[None], ref.scale, "scales")
         if y is not None:
-            dq = oracle.dequantize(c, gn[r0:r0 + B, h:h + 1].numpy(), gs[s * nb + b, h:h + 1].numpy()[None], sp, sg)
+            nt = None if gn is None else gn[r0:r0 + B, h:h + 1].numpy()
+            dq = oracle.dequantize(c, nt, gs[s * nb + b, h:h + 1].numpy()[None], sp, sg)
             yt = y[r0:r0 + B, h:h + 1].cpu()
             if yt.dtype == torch.float32:
                 parity.check_dequant(yt.numpy(), dq)
@@ -166,6 +168,26 @@ def test_batched_hadamard_full_sampled():
     torch.cuda.synchronize()
     print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 48, seed=3, y=y16))
     print(_sampled_tiles(d, x_cpu, signs, codes, norms, scales, 16, seed=4, y=y32))
+
+
+# Caches of a few thousand tiles with head counts that are not powers of two and every block size:
+# every scale row must be written (they start as NaN), and sampled tiles match the oracle.
+@pytest.mark.parametrize("S,T,H,D,B,mode,had,dt", [(5, 1024, 67, 128, 128, "nsep_pchan", 128, torch.float16),
+                                                   (5, 1024, 67, 128, 64, "pchan", 32, torch.bfloat16),
+                                                   (3, 2048, 100, 64, 256, "nsep_pchan", 64, torch.float16)])
+def test_quantize_every_tile_written(S, T, H, D, B, mode, had, dt):
+    rng = np.random.default_rng(S * T + H + D + B)
+    x = torch.from_numpy(rng.standard_normal((S * T, H, D)).astype(np.float32))
+    x[:, :, 3] *= 25
+    x = x.to(dt)
+    signs = torch.from_numpy(rng.choice(np.array([-1, 1], np.int8), size=(H, D)))
+    d = kvq.Desc(S, T, H, D, 4, mode, B, had, dt)
+    codes, norms, scales = kvq.alloc_outputs(d, DEV)
+    scales.fill_(float("nan"))
+    kvq.quantize(d, x.to(DEV), signs.to(DEV), out=(codes, norms, scales))
+    torch.cuda.synchronize()
+    assert not torch.isnan(scales.float()).any(), "a tile was not written"
+    print(_sampled_tiles(d, x, signs, codes, norms, scales, 24, seed=11))
 
 
 # ----------------------------------------------------------------------------- decode score
