@@ -13,7 +13,10 @@
 // block, the scales and the exact re-decision of near-ties are all wave-local.  Workgroup
 // barriers: the rows have landed; every wave's token norms are published; every wave is done
 // with the staged rows (the buffer then takes the packed code rows); the code rows are
-// complete, and the tile's code block is stored whole.
+// complete, and the tile's code block is stored whole.  With B = 128 a workgroup takes 34 KB
+// of LDS and its waves at most 128 registers, so four workgroups share a CU (four waves per
+// SIMD); the rotated tile is therefore not kept past the codes, and the near-tie path
+// recomputes the part it needs.
 //
 // Rotation: Y^T = blockdiag(H_n) diag(sigma) X^T in 16-token sub-tiles with
 // v_mfma_f32_16x16x32 (fp16 or bf16 operands, fp32 accumulation; the +-1 products are exact).
@@ -45,7 +48,7 @@ namespace {
 using namespace rot;
 
 template <int DT, int R, int LG, int B>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B > 128 ? 3 : 4)))
 quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   constexpr int NK = R / 32;            // K steps of the contraction
   constexpr int NIW = R / 64;           // output I-blocks per wave
@@ -244,7 +247,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
 
   // 6. codes and near-tie flags
   uint32_t pk[ST];
-  uint32_t fl = 0xffffffffu;
+  uint32_t fl = 0xffffffffu, fl1 = 0xffffffffu;            // flags of I-block 0 and of I-block 1
 #pragma unroll
   for (int s = 0; s < ST; ++s) {
     uint32_t b[8];
@@ -253,8 +256,8 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
     if constexpr (LCH == 8) {
       fl = min3_u16(fl, b[0], b[1]);
       fl = min3_u16(fl, b[2], b[3]);
-      fl = min3_u16(fl, b[4], b[5]);
-      fl = min3_u16(fl, b[6], b[7]);
+      fl1 = min3_u16(fl1, b[4], b[5]);
+      fl1 = min3_u16(fl1, b[6], b[7]);
     } else {
       fl = min3_u16(fl, b[0], b[1]);
       fl = min3_u16(fl, b[2], b[3]);
@@ -263,95 +266,166 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
     pk[s] = pack8(b);
   }
 
-  // 7. rare path, wave-local: exact re-decision of this wave's near-ties (u is still live)
-  if (__ballot((fl & 0xffffu) == 0u) != 0ull) {
-    uint32_t cm = 0u;                                       // bit q: channel (R/4) w + LCH g + q
-#pragma unroll
-    for (int q = 0; q < LCH; ++q) {
-      uint32_t mn = 0xffffffffu;
-#pragma unroll
-      for (int s = 0; s < ST; s += 2)
-        mn = min3_u16(mn, __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s][q >> 2][q & 3], iv[q], CODE_MAGIC)),
-                      __builtin_bit_cast(uint32_t, __builtin_fmaf(u[s + 1][q >> 2][q & 3], iv[q], CODE_MAGIC)));
-      cm |= ((mn & 0xffffu) == 0u ? 1u : 0u) << q;
-    }
-    // OR over the 16 lanes of each row, then the four rows side by side
-    cm = row_or16(cm);
-    uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)cm, 0) |
-                    ((uint32_t)__builtin_amdgcn_readlane((int)cm, 16) << LCH) |
-                    ((uint32_t)__builtin_amdgcn_readlane((int)cm, 32) << (2 * LCH)) |
-                    ((uint32_t)__builtin_amdgcn_readlane((int)cm, 48) << (3 * LCH));
+  // 7. rare path, wave-local: exact re-decision of this wave's near-ties.  The rotated values are
+  //    not kept past step 6 (that would hold 64 more registers through the common path): the path
+  //    recomputes one I-block at a time with the same matrix-core sequence (same operands, same
+  //    K order, same accumulator start), so every value, flag and code it sees is bit for bit the
+  //    one step 6 saw.  One code path serves every flagged channel: the channel's lane slot is a
+  //    wave-uniform runtime value and the tokens to evaluate exactly are bit masks walked by a
+  //    single loop, so the path stays small in the instruction cache.
+  const uint64_t flagged0 = __ballot((fl & 0xffffu) == 0u), flagged1 = NIW == 2 ? __ballot((fl1 & 0xffffu) == 0u) : 0ull;
+  if ((flagged0 | flagged1) != 0ull) {
     const double qd = (double)a.q;
-    // exact unnormalized y (a sum of fp16/bf16 values, exact in fp64) and norm of tile row r for
-    // channel c: lane l takes inputs l, l + 64, ...
-    auto exact_y = [&](int r, int c, double& nu) {
-      double y = 0.0, ss = 0.0;
+    // exact unnormalized y (a sum of fp16/bf16 values, exact in fp64) and norm of tile rows ra
+    // and rb for channel c, side by side so their wave reductions overlap: lane l takes inputs
+    // l, l + 64, ... (each row's sums are accumulated and reduced in the same order either way)
+    auto exact2 = [&](int ra, int rb, int c, double& ya, double& nua, double& yb, double& nub) {
+      double sa = 0.0, sb = 0.0;
+      ya = yb = 0.0;
 #pragma unroll
       for (int e = 0; e < R / 64; ++e) {
         const int p = lane + 64 * e;
-        const uint32_t hw = *(const uint16_t*)(stage + r * ROWB + 16 * ((p >> 3) ^ (r % CPR)) + 2 * (p & 7));
-        const double x = widen64<DT>(hw);
-        ss = __builtin_fma(x, x, ss);
+        const int off = 16 * (p >> 3), lo = 2 * (p & 7);
+        const double xa = widen64<DT>(*(const uint16_t*)(stage + ra * ROWB + (off ^ (16 * (ra % CPR))) + lo));
+        const double xb = widen64<DT>(*(const uint16_t*)(stage + rb * ROWB + (off ^ (16 * (rb % CPR))) + lo));
+        sa = __builtin_fma(xa, xa, sa);
+        sb = __builtin_fma(xb, xb, sb);
         const int hv = LG == 0 ? (p == c ? 1 : 0) : hval<LG>(c, p);
-        if (hv != 0) y += ((hv < 0) != (LG != 0 && sg[p] < 0)) ? -x : x;
-      }
-      nu = sqrt(wave_sum64(ss));
-      return wave_sum64(y);
-    };
-    // one flagged channel; its lane slot Q is a compile-time constant, so u and iv are plain
-    // registers.  Pass 0 finds the token holding the channel's exact max among those near the
-    // fp32 max and keeps its |y| and norm; pass 1 re-decides the flagged values from
-    // v = Q (y / |y_max|) (nu_max / nu) (the second factor only with NSEP): Q y / |y_max| is one
-    // correctly rounded division of exact values, so an exact tie between tokens of equal norm
-    // stays an exact tie and rounds half to even.
-    auto fix_channel = [&](auto qc, int gc, int c) {
-      constexpr int Q = decltype(qc)::value;
-      double um = 0.0, ym = 0.0, num = 0.0;
-#pragma unroll 1
-      for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int s = 0; s < ST; ++s) {
-          const float uq = u[s][Q >> 2][Q & 3];
-          const bool hit = pass == 0
-                               ? fabsf(uq) * iv[Q] >= a.q * (1.f - 0x1p-12f)
-                               : (__builtin_bit_cast(uint32_t, __builtin_fmaf(uq, iv[Q], CODE_MAGIC)) & 0xffffu) == 0u;
-          uint64_t tok = (__ballot(g == gc && hit) >> (16 * gc)) & 0xffffull;
-          while (tok) {
-            const int jt = __builtin_ctzll(tok);
-            tok &= tok - 1ull;
-            double nu;
-            const double yex = exact_y(16 * s + jt, c, nu);
-            if (pass == 0) {
-              const double ua = a.nsep ? (nu > 0.0 ? fabs(yex) / nu : 0.0) : fabs(yex);
-              if (ua > um) { um = ua; ym = fabs(yex); num = nu; }
-            } else if (lane == 16 * gc + jt) {
-              double v = 0.0;
-              if (ym > 0.0 && yex != 0.0) v = a.nsep ? (qd * yex / ym) * (num / nu) : qd * yex / ym;
-              pk[s] = (pk[s] & ~(0xFu << (4 * Q))) | (exact_nibble(v) << (4 * Q));
-            }
-          }
+        const bool neg = (hv < 0) != (LG != 0 && sg[p] < 0);
+        if (hv != 0) {
+          ya += neg ? -xa : xa;
+          yb += neg ? -xb : xb;
         }
       }
+      sa = wave_sum64(sa);
+      sb = wave_sum64(sb);
+      ya = wave_sum64(ya);
+      yb = wave_sum64(yb);
+      nua = sqrt(sa);
+      nub = sqrt(sb);
     };
-    while (bits) {
-      const int cl = __builtin_ctz(bits);                   // channel (R/4) w + cl
-      bits &= bits - 1u;
-      const int gc = cl / LCH, c = (R / 4) * w + cl;
-      switch (cl % LCH) {
-        case 0: fix_channel(std::integral_constant<int, 0>{}, gc, c); break;
-        case 1: fix_channel(std::integral_constant<int, 1>{}, gc, c); break;
-        case 2: fix_channel(std::integral_constant<int, 2>{}, gc, c); break;
-        case 3: fix_channel(std::integral_constant<int, 3>{}, gc, c); break;
-        default:
-          if constexpr (LCH == 8) {
-            switch (cl % LCH) {
-              case 4: fix_channel(std::integral_constant<int, 4 % LCH>{}, gc, c); break;
-              case 5: fix_channel(std::integral_constant<int, 5 % LCH>{}, gc, c); break;
-              case 6: fix_channel(std::integral_constant<int, 6 % LCH>{}, gc, c); break;
-              default: fix_channel(std::integral_constant<int, 7 % LCH>{}, gc, c); break;
-            }
+    // step 3's rotation of sub-tile s, I-block I, times step 4's 1 / norm (w and I at run time)
+    // (op is an opaque zero added to the operand addresses, so the reads stay inside the I loop
+    // instead of being hoisted out of it with every sub-tile's operands live)
+    auto rotated = [&](int s, int I, const u32x4& fbI, int op) {
+      auto rx = [&](int K) {
+        return *(const u32x4*)(stage + op + 16 * s * ROWB + (j * ROWB + 16 * ((4 * K + g) ^ (j % CPR))));
+      };
+      f32x4 us = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (LG == 0) {
+        const int c0 = (R / 4) * w + LCH * g;
+        const uint32_t e0 = (uint32_t)((c0 & 7) >> 1);
+        const u32x4 xr = R == 128 ? rx(w) : *(const u32x4*)(stage + op + 16 * s * ROWB + (j * ROWB + 16 * ((c0 >> 3) ^ (j % CPR))));
+        const uint32_t i0 = (e0 + 2 * I) & 3, i1 = (e0 + 2 * I + 1) & 3;
+        const uint32_t w0 = i0 == 0 ? xr.x : i0 == 1 ? xr.y : i0 == 2 ? xr.z : xr.w;
+        const uint32_t w1 = i1 == 0 ? xr.x : i1 == 1 ? xr.y : i1 == 2 ? xr.z : xr.w;
+        us = f32x4{lo_f32<DT>(w0), hi_f32<DT>(w0), lo_f32<DT>(w1), hi_f32<DT>(w1)};
+      } else {
+#pragma unroll
+        for (int K = 0; K < NK; ++K) {
+          const int bt = frag_beta<R, LG>(w, K);
+          if (bt == 0) continue;
+          const u32x2 s8 = *(const u32x2*)(sg + 32 * K + 8 * g);
+          uint32_t m[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            m[q] = (__builtin_amdgcn_perm(0u, q < 2 ? s8.x : s8.y, (q & 1) ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u) ^
+                   (bt < 0 ? 0x80008000u : 0u);
+          us = mfma16<DT>(fbI ^ u32x4{m[0], m[1], m[2], m[3]}, rx(K), us);
+        }
+      }
+      return us * ninv[j * ST + s];
+    };
+#pragma unroll 1
+    for (int I = 0; I < NIW; ++I) {
+      if ((I == 0 ? flagged0 : flagged1) == 0ull) continue;  // no near-tie in this I-block
+      // an opaque zero: the fragments and operand reads below are recomputed here rather than
+      // matched to the common path's and kept live through it
+      int op = 0;
+      asm volatile("" : "+v"(op));
+      const u32x4 fbI = LG != 0 ? hadamard_fragment<DT, R, LG>(w, I, lane + op) : u32x4{0u, 0u, 0u, 0u};
+      f32x4 us[ST];
+#pragma unroll
+      for (int s = 0; s < ST; ++s) us[s] = rotated(s, I, fbI, op);
+      float ivI[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ivI[r] = NIW == 1 || I == 0 ? iv[r] : iv[(4 + r) % LCH];
+      uint32_t cm = 0u;                                     // bit r: channel (R/4) w + LCH g + 4 I + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t mn = 0xffffffffu;
+#pragma unroll
+        for (int s = 0; s < ST; s += 2)
+          mn = min3_u16(mn, __builtin_bit_cast(uint32_t, __builtin_fmaf(us[s][r], ivI[r], CODE_MAGIC)),
+                        __builtin_bit_cast(uint32_t, __builtin_fmaf(us[s + 1][r], ivI[r], CODE_MAGIC)));
+        cm |= ((mn & 0xffffu) == 0u ? 1u : 0u) << r;
+      }
+      // OR over the 16 lanes of each row, then the four rows side by side
+      cm = row_or16(cm);
+      uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)cm, 0) | ((uint32_t)__builtin_amdgcn_readlane((int)cm, 16) << 4) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)cm, 32) << 8) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)cm, 48) << 12);
+      while (bits) {
+        const int cl = __builtin_ctz(bits);                 // wave-uniform
+        bits &= bits - 1u;
+        const int gc = cl >> 2, r = cl & 3, qc = 4 * I + r; // lane row, slot in the lane
+        const int c = (R / 4) * w + LCH * gc + qc;
+        float uq[ST];
+#pragma unroll
+        for (int s = 0; s < ST; ++s) uq[s] = r == 0 ? us[s][0] : r == 1 ? us[s][1] : r == 2 ? us[s][2] : us[s][3];
+        const float ivq = r == 0 ? ivI[0] : r == 1 ? ivI[1] : r == 2 ? ivI[2] : ivI[3];
+        // per lane of row gc, bit s: token 16 s + j is near the fp32 max (within 2^-12 of it) / is
+        // flagged
+        uint32_t hn = 0u, hf = 0u;
+#pragma unroll
+        for (int s = 0; s < ST; ++s) {
+          hn |= (fabsf(uq[s]) * ivq >= a.q * (1.f - 0x1p-12f) ? 1u : 0u) << s;
+          hf |= ((__builtin_bit_cast(uint32_t, __builtin_fmaf(uq[s], ivq, CODE_MAGIC)) & 0xffffu) == 0u ? 1u : 0u) << s;
+        }
+        if (g != gc) hn = hf = 0u;
+        // the next token of a kind, lane by lane (wave-uniform result; -1 once the kind is spent)
+        auto pop = [&](uint32_t& hm) {
+          const uint64_t lanes = __ballot(hm != 0u);
+          if (lanes == 0ull) return -1;
+          const int lj = (int)__builtin_ctzll(lanes);
+          const int sb = __builtin_ctz((uint32_t)__builtin_amdgcn_readlane((int)hm, lj));
+          if (lane == lj) hm &= hm - 1u;
+          return 16 * sb + (lj & 15);                       // tile row
+        };
+        // every near token before any flagged one: the one holding the channel's exact max keeps
+        // its |y| and norm; every flagged value is then re-decided from v = Q (y / |y_max|)
+        // (nu_max / nu) (the second factor only with NSEP): Q y / |y_max| is one correctly rounded
+        // division of exact values, so an exact tie between tokens of equal norm stays an exact
+        // tie and rounds half to even.  Two tokens per pass (a near one then a flagged one in the
+        // common case of one each); a flagged token is decided only after every near one is done.
+        double um = 0.0, ym = 0.0, num = 0.0;
+        auto take = [&](int t, bool flagged, double yex, double nu) {
+          if (!flagged) {
+            const double ua = a.nsep ? (nu > 0.0 ? fabs(yex) / nu : 0.0) : fabs(yex);
+            if (ua > um) { um = ua; ym = fabs(yex); num = nu; }
+          } else if (lane == 16 * gc + (t & 15)) {
+            double v = 0.0;
+            if (ym > 0.0 && yex != 0.0) v = a.nsep ? (qd * yex / ym) * (num / nu) : qd * yex / ym;
+            const uint32_t nib = exact_nibble(v) << (4 * qc), keep = ~(0xFu << (4 * qc));
+#pragma unroll
+            for (int s = 0; s < ST; ++s)
+              if (s == (t >> 4)) pk[s] = (pk[s] & keep) | nib;
           }
-          break;
+        };
+#pragma unroll 1
+        while (true) {
+          int ta = pop(hn);
+          bool fa = false;
+          if (ta < 0) { ta = pop(hf); fa = true; }
+          if (ta < 0) break;
+          int tb = fa ? -1 : pop(hn);
+          bool fb = false;
+          if (tb < 0) { tb = pop(hf); fb = true; }
+          double ya, nua, yb, nub;
+          exact2(ta, tb < 0 ? ta : tb, c, ya, nua, yb, nub);
+          take(ta, fa, ya, nua);
+          if (tb >= 0) take(tb, fb, yb, nub);
+        }
       }
     }
   }
