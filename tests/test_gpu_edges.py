@@ -166,16 +166,35 @@ def test_exact_ties_wide_per_token(mode, dim, had, extra_max):
     np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
 
 
+@pytest.mark.parametrize("had,extra_max", [(0, 0), (64, 0), (64, 3), (0, 5)])
+@pytest.mark.parametrize("mode", ["pchan", "nsep_pchan"])
+def test_exact_ties_per_channel_d128(mode, had, extra_max):
+    # head_dim 128 and 128-token blocks: every code is a tie, in both 64-channel halves of each
+    # wave's channels, every value of every wave is re-decided exactly, and with extra_max > 0 a
+    # channel's max sits in several tokens at once
+    x64, signs, want = grid.all_ties(had, seed=7 + extra_max, T=128, H=2, D=128, extra_max=extra_max)
+    d = kvq.Desc(1, 128, 2, 128, 4, mode, 128, had, torch.float16)
+    sg = None if signs is None else torch.from_numpy(signs).to(DEV)
+    codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).half().to(DEV), sg)
+    torch.cuda.synchronize()
+    got = oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy())
+    np.testing.assert_array_equal(got, want)
+    sp = oracle.Spec(1, 128, 2, 128, 4, mode, 128, had)
+    np.testing.assert_array_equal(oracle.quantize(x64, sp, signs).codes, want)
+
+
+@pytest.mark.parametrize("dim", [64, 128])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("mode", oracle.MODES)
-def test_near_ties_follow_the_exact_quotient(mode, bits, dtype):
+def test_near_ties_follow_the_exact_quotient(mode, bits, dtype, dim):
     # quotients a hair (~2^-26) above and below a tie that half-to-even rounds down: the codes are
     # the rounding of the exact quotient (rational arithmetic, tests/grid.py), with no tie band;
-    # a decision on the fp32 quotient would give the tie's even neighbour for both
+    # a decision on the fp32 quotient would give the tie's even neighbour for both.  With head_dim
+    # 128 the flagged channels 0..15 fall in both 4-channel halves of the first wave's slots.
     per_channel = "pchan" in mode
-    x64, signs, want = grid.near_ties(bits, per_channel)
-    d = kvq.Desc(1, 64, 1, 64, bits, mode, 64 if per_channel else 0, 16, dtype)
+    x64, signs, want = grid.near_ties(bits, per_channel, D=dim, B=dim)
+    d = kvq.Desc(1, dim, 1, dim, bits, mode, dim if per_channel else 0, 16, dtype)
     codes, norms, scales = kvq.quantize(d, torch.from_numpy(x64).to(dtype).to(DEV), torch.from_numpy(signs).to(DEV))
     torch.cuda.synchronize()
     got = oracle.unpack_nibbles(kvq.token_major(d, codes)[0].cpu().numpy())
