@@ -526,6 +526,14 @@ def main():
     if args.only:
         print(json.dumps({"profile_only": args.only, "kernels": kernels, "steps": args.steps}), flush=True)
         return
+    # the attainable ceiling: a device-to-device copy of the 4 GiB fp16 cache (as many bytes read as
+    # written), timed like the kernels; each long-context kernel's rate is also given against it
+    copy_t = time_calls(torch, lambda: y.copy_(x), stream, min(args.steps, 10), min(args.warmup, 2))
+    copy_bytes = 2 * x.numel() * x.element_size()
+    copy_gbs = copy_bytes / (copy_t["us"] * 1e-6) / 1e9
+    for n, k in kernels.items():
+        if "GB/s" in k and "us" in k and "shape" not in k:
+            k["frac_copy"] = round(k["GB/s"] / copy_gbs, 4)
     qa = kernels["quantize"]["GB/s"]
     out = {
         "metric": "quantize/dequant/decode-score GB/s and % of HBM peak, 1x MI355X",
@@ -543,6 +551,8 @@ def main():
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": qa, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(qa / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "copy_ceiling": {**copy_t, "bytes": copy_bytes, "GB/s": round(copy_gbs, 1),
+                         "frac_hbm": round(copy_gbs / HBM_PEAK_GBS, 4), "what": "torch device-to-device copy of the fp16 cache"},
         "cpu_baseline": None,
     }
     if args.other_configs:
