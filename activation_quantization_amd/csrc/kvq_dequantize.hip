@@ -310,8 +310,10 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
         unsigned char* op = yw + r * orow;
 #pragma unroll
         for (int q = 0; q < OW / 4; ++q)
-          *(u32x4*)(op + 16 * q) = u32x4{ow[r][4 * q], ow[r][4 * q + 1], ow[r][4 * q + 2], ow[r][4 * q + 3]};
-        if constexpr (OW % 4 == 2) *(u32x2*)(op + 16 * (OW / 4)) = u32x2{ow[r][OW - 2], ow[r][OW - 1]};
+          __builtin_nontemporal_store(u32x4{ow[r][4 * q], ow[r][4 * q + 1], ow[r][4 * q + 2], ow[r][4 * q + 3]},
+                                      (u32x4*)(op + 16 * q));
+        if constexpr (OW % 4 == 2)
+          __builtin_nontemporal_store(u32x2{ow[r][OW - 2], ow[r][OW - 1]}, (u32x2*)(op + 16 * (OW / 4)));
       }
     }
   }

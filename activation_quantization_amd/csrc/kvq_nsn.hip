@@ -402,9 +402,9 @@ __global__ void __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2)))
     for (int q = 0; q < 4; ++q) {
       unsigned char* cp = a.codes + (tok0 + 32 * w + tq(q)) * (D / 2) + cb / 2;
       if constexpr (NG == 2)
-        *(u32x2*)cp = u32x2{pk[q][0], pk[q][1]};
+        __builtin_nontemporal_store(u32x2{pk[q][0], pk[q][1]}, (u32x2*)cp);
       else
-        *(uint32_t*)cp = pk[q][0];
+        __builtin_nontemporal_store(pk[q][0], (uint32_t*)cp);
     }
     return sgn;
   };

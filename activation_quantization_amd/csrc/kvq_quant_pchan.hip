@@ -449,7 +449,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   for (int k = 0; k < (WPIECES + 63) / 64; ++k) {
     const int pc = 64 * k + lane;
     if (WPIECES % 64 == 0 || pc < WPIECES)
-      *(u32x4*)(cb + 16 * pc) = *(const u32x4*)(stage + w * (B * RB / 4) + 16 * pc);
+      __builtin_nontemporal_store(*(const u32x4*)(stage + w * (B * RB / 4) + 16 * pc), (u32x4*)(cb + 16 * pc));
   }
 }
 

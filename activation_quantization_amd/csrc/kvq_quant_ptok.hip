@@ -444,7 +444,7 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
     for (int k = 0; k < PT_ROWS / 64; ++k) {
       const int pc = 64 * k + lane;                          // piece of this wave's rows
       if ((PT_ROWS / 4) * w + pc / 4 < nvalid)
-        *(u32x4*)(cb + 16 * pc) = *(const u32x4*)(cstage + (PT_ROWS / 4) * w * RB + 16 * pc);
+        __builtin_nontemporal_store(*(const u32x4*)(cstage + (PT_ROWS / 4) * w * RB + 16 * pc), (u32x4*)(cb + 16 * pc));
     }
   } else {
     const int r = (PT_ROWS / 4) * w + (lane >> 1);          // two lanes per row
@@ -454,7 +454,7 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int piece = 2 * (lane & 1) + k;
-        *(u32x4*)(a.codes + dst * RB + 16 * piece) = *(const u32x4*)(cstage + r * RB + 16 * piece);
+        __builtin_nontemporal_store(*(const u32x4*)(cstage + r * RB + 16 * piece), (u32x4*)(a.codes + dst * RB + 16 * piece));
       }
     }
   }
