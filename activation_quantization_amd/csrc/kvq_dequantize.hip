@@ -157,10 +157,10 @@ dequant_mfma(DequantArgs a, int64_t nchunks, int lgL, int vec) {
       const uint32_t t = (uint32_t)((ch0 + i) * 64) + 16 * w;   // stream token of the wave's first row
       const unsigned char* cp = cstream + (size_t)(t + j) * cstride + LB * g;
       if constexpr (KS == 4) {
-        const u32x4 v = *(const u32x4*)cp;
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)cp);
         p.wd[0] = v.x; p.wd[1] = v.y; p.wd[2] = v.z; p.wd[3] = v.w;
       } else {
-        const u32x2 v = *(const u32x2*)cp;
+        const u32x2 v = __builtin_nontemporal_load((const u32x2*)cp);
         p.wd[0] = v.x; p.wd[1] = v.y;
       }
       if (a.nsep) {

@@ -104,6 +104,9 @@ __device__ __forceinline__ float shfl_f(float v, int src) {
 // between the load and its use)
 static __device__ const uint16_t kF16One[1] = {0x3C00u};
 // four fp16 ones, 8-byte aligned: the per-token factors of a mode that stores none
+// cache policy of an LDS-DMA load (global_load_lds) that streams data read exactly once: the
+// nontemporal bit (encoded where older targets kept SLC)
+constexpr int KVQ_LOAD_NT = 2;
 static __device__ __attribute__((aligned(8))) const uint16_t kF16Ones4[4] = {0x3C00u, 0x3C00u, 0x3C00u, 0x3C00u};
 
 // A load through a global-address-space pointer.  A pointer that may be a kernel argument or a

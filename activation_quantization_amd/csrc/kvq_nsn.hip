@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2)))
       const int p = 64 * k + lane, r = p / CPR, cc = p % CPR;
       const uint32_t off = (uint32_t)r * tok_bytes + 16u * (uint32_t)(cc ^ ((r + (B / NW) * w) % CPR));
       __builtin_amdgcn_global_load_lds((const void*)(xw + off),
-                                       (__attribute__((address_space(3))) void*)(buf + w * WSTAGE + k * 1024), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(buf + w * WSTAGE + k * 1024), 16, 0, KVQ_LOAD_NT);
     }
     uint32_t sg = 0u;
     if constexpr (LG != 0)

@@ -99,7 +99,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
       const unsigned char* base = xw + (int64_t)(RPI * k) * tok_bytes;
       const uint32_t off = lrow * (uint32_t)tok_bytes + 16u * (uint32_t)(cc ^ ((row + (B / 4) * w) % CPR));
       __builtin_amdgcn_global_load_lds((const void*)(base + off),
-                                       (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, KVQ_LOAD_NT);
     }
     if constexpr (LG != 0) {
       if (w == 0 && lane < R / 16)

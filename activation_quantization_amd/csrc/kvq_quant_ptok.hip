@@ -106,7 +106,7 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
     if (r < nvalid) {
       __builtin_amdgcn_global_load_lds((const void*)(xw + (4 * k + g) * ROWB + 16 * gc),
                                        (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0,
-                                       0);
+                                       KVQ_LOAD_NT);
       if constexpr (LG != 0) {
         const uint32_t h = a.heads > 1 ? (h0 + ((uint32_t)r >> lgL)) % (uint32_t)a.heads : 0u;
         sgn[k] = *(const u32x2*)(a.signs + (int64_t)h * a.dim + (r & (L - 1)) * R + 8 * gc);
