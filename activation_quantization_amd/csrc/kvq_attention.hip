@@ -156,7 +156,7 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     }
     u32x4 vcw[NGR];                                         // V codes: lane's 16 bytes of each KiB
 #pragma unroll
-    for (int k = 0; k < NGR; ++k) vcw[k] = ld_global((const u32x4*)(vstream + t0 * (R / 2) + k * 1024 + 16 * lane));
+    for (int k = 0; k < NGR; ++k) vcw[k] = __builtin_nontemporal_load((const u32x4*)(vstream + t0 * (R / 2) + k * 1024 + 16 * lane));
     __builtin_amdgcn_sched_barrier(0);
     float sc[KS * 8];
 #pragma unroll
