@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(256) rrs_gemm_kernel(RrsGemmArgs a, int64_t ti
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int64_t m = c0 + 64 * wc + 16 * jj + j;
-        if (t < a.n && m < a.m) yr[m] = accf[i][jj][r] * at * f16_to_f32(bh[jj]);
+        if (t < a.n && m < a.m) __builtin_nontemporal_store(accf[i][jj][r] * at * f16_to_f32(bh[jj]), yr + m);
       }
     }
 }
