@@ -74,7 +74,10 @@ def algorithmic_bytes(w, q_heads):
             "quantize_nsn": x + signs + codes + 2 * norms + 2 * scales,
             "dequantize_nsn": codes + 2 * norms + 2 * scales + signs + x,
             "score_decode_nsn": q + signs + codes + 2 * norms + 2 * scales + scores,
-            "elements": n}
+            "elements": n,
+            # the kernels' inputs alone (the "input GB/s" figure)
+            "inputs": {"quantize": x + signs, "dequantize": codes + norms + scales + signs,
+                       "score_decode": q + signs + codes + norms + scales}}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "long_context_hbm_traffic.md")
@@ -512,7 +515,8 @@ def main():
         gbs = b[n] / (per_kernel_ms[n] * 1e-3) / 1e9
         kernels[n] = {"us": round(per_kernel_ms[n] * 1e3, 2), "us_p10": round(percentile(samples[n], 10) * 1e3, 2),
                       "us_p90": round(percentile(samples[n], 90) * 1e3, 2), "bytes": b[n], "GB/s": round(gbs, 1),
-                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "input_GB/s": round(b["inputs"][n] / (per_kernel_ms[n] * 1e-3) / 1e9, 1)}
     traffic = measured_traffic("quantize")
     if attn_us is not None:
         gbs = b["attention_decode"] / (attn_us * 1e-6) / 1e9
