@@ -15,13 +15,13 @@
 // stream; every wave walks its own blocks): per block, the scores of the G query heads come from
 // the matrix cores exactly as in the decode-score kernel (query times K scales as an fp16 hi/lo
 // A operand, codes as fp16 subnormals), an online softmax keeps the running max m and sum l per
-// head, and the value sum runs on the vector units: the block's V codes are copied to LDS
-// (global_load_lds), lane 16 a + b owns channels 8 b .. 8 b + 7 of the tokens t = a (mod 4) and
-// takes them two at a time (t, t + 4) as 16-bit integer pairs against the pairs of 30-bit integer
-// weights (p' = p norm_v against the block's largest, in two 15-bit halves) of each head, in
-// exact integer dot products (v_dot2_u32_u16).  The four waves' (m, l, partial sum) are merged in LDS and the
-// workgroup writes one partial per query head to the caller's workspace.  Pass 2 merges the
-// partials of a head (log-sum-exp weights), rotates the result back and writes it.
+// head, and the value sum runs on the int8 matrix cores in exact integers: the block's V codes
+// (loaded into registers with the block's other loads, then written to LDS) are regrouped so each
+// lane holds one channel of 16 tokens as bytes c + 8, against the value weights p' = p norm_v of
+// each head as 24-bit integers (against the block's largest) split into three byte planes.  The
+// four waves' (m, l, partial sum) are merged in LDS and the workgroup writes one partial per query
+// head to the caller's workspace.  Pass 2 merges the partials of a head (log-sum-exp weights),
+// rotates the result back and writes it.
 #include <mutex>
 #include <type_traits>
 
@@ -227,11 +227,14 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     }
 
     // 3. online softmax for the row's two heads.  The value weights p' = p * norm_v become
-    //    28-bit integers W = rint(p' (2^28 - 1) / wmax) against the block's largest weight wmax of
-    //    the head (fp16 weights, 2^-12 relative, move a long, nearly cancelling value sum past 2e-3
-    //    of the output's rms), stored as four 7-bit planes: row 4 h + b of the value MFMA's A
-    //    operand.  Token t sits at K position (lane group t % 4, byte 4 ((t / 4) % 4) + (t / 16) % 4)
-    //    of K step t / 64, so this lane's four tokens of a K step fill one 32-bit word per plane.
+    //    24-bit integers W = rint(p' 2^24 / wmax) (at most 2^24 - 1) against the block's largest
+    //    weight wmax of the head (fp16 weights, 2^-12 relative, move a long, nearly cancelling value
+    //    sum past 2e-3 of the output's rms), stored as three byte planes less 128 (signed int8):
+    //    rows 4 h + b, b < 3, of the value MFMA's A operand; row 4 h + 3 is all ones, so the same
+    //    products also give each channel's code sum, which puts the 128 back.  Token t sits at K
+    //    position (lane group t % 4, byte 4 ((t / 4) % 4) + (t / 16) % 4) of K step t / 64, so this
+    //    lane's four tokens of a K step fill one 32-bit word per plane (a byte transpose of their
+    //    four weights).
     float alpha_row[2], wf_row[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
@@ -251,25 +254,31 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
         wmax = fmaxf(wmax, z[gr][q2]);
       }
       wmax = row_max16f(wmax);
-      const float wscale = wmax > 0.f ? 0x1p28f / wmax : 0.f;
+      const float wscale = wmax > 0.f ? 0x1p24f / wmax : 0.f;
       if (h < GM) {
 #pragma unroll
         for (int ks = 0; ks < NGR / 4; ++ks) {
-          uint32_t pk[4] = {0u, 0u, 0u, 0u};
+          uint32_t wq[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float wv = __builtin_rintf(z[4 * ks + r][q2] * wscale);
-            const uint32_t wq = wv < 268435455.f ? (uint32_t)wv : 268435455u;        // <= 2^28 - 1
-#pragma unroll
-            for (int b = 0; b < 4; ++b) pk[b] |= ((wq >> (7 * b)) & 127u) << (8 * r);
+            wq[r] = wv < 16777215.f ? (uint32_t)wv : 16777215u;                      // <= 2^24 - 1
           }
+          // byte b of the four tokens' weights, side by side, each less 128 (a signed int8)
+          const uint32_t l01 = __builtin_amdgcn_perm(wq[1], wq[0], 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
+          const uint32_t h01 = __builtin_amdgcn_perm(wq[3], wq[2], 0x05010400u);   // w2.0 w3.0 w2.1 w3.1
+          const uint32_t l2 = __builtin_amdgcn_perm(wq[1], wq[0], 0x06020602u);    // w0.2 w1.2 (twice)
+          const uint32_t h2 = __builtin_amdgcn_perm(wq[3], wq[2], 0x06020602u);    // w2.2 w3.2 (twice)
+          const uint32_t pk[4] = {__builtin_amdgcn_perm(h01, l01, 0x05040100u) ^ 0x80808080u,
+                                  __builtin_amdgcn_perm(h01, l01, 0x07060302u) ^ 0x80808080u,
+                                  __builtin_amdgcn_perm(h2, l2, 0x05040100u) ^ 0x80808080u, 0x01010101u};
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             *(uint32_t*)(ww + ((ks * 16 + 4 * h + b) * 64 + 16 * (j & 3) + 4 * (j >> 2))) = pk[b];
         }
       }
       ps = row_sum16f(ps);
-      wf_row[q2] = wmax * 0x1p-28f;
+      wf_row[q2] = wmax * 0x1p-24f;
       l_row[q2] = l_row[q2] * alpha_row[q2] + ps;
       m_row[q2] = mnew;
     }
@@ -325,14 +334,16 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
       acc[8] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{0x08080808, 0x08080808, 0x08080808, 0x08080808},
                                                      acc[8], 0, 0, 0);
     }
-    // lane (g, j): rows 4 g + b = the planes of head g; sum_t W (c_t) = sum_b 128^b (D_b - bias_b),
+    // lane (g, j): rows 4 g + b = the planes of head g and its row of ones; with S_b = W_b - 128,
+    // sum_t W c_t = sum_b 256^b ((D_b - bias_b) + 128 (D_1 - bias_1)), D_1 - bias_1 = sum_t c_t;
     // every difference below 2^24 (exact in fp32)
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      float v = (float)(acc[m][3] - acc[8][3]);
-      v = __builtin_fmaf(v, 128.f, (float)(acc[m][2] - acc[8][2]));
-      v = __builtin_fmaf(v, 128.f, (float)(acc[m][1] - acc[8][1]));
-      v = __builtin_fmaf(v, 128.f, (float)(acc[m][0] - acc[8][0]));
+      const float cs = (float)(acc[m][3] - acc[8][3]);          // sum_t c_t (the row of ones)
+      float v = (float)(acc[m][2] - acc[8][2]);
+      v = __builtin_fmaf(v, 256.f, (float)(acc[m][1] - acc[8][1]));
+      v = __builtin_fmaf(v, 256.f, (float)(acc[m][0] - acc[8][0]));
+      v = __builtin_fmaf(cs, 128.f * 65793.f, v);               // the 128 taken off each byte, 1 + 256 + 65536
       o[m] = o[m] * alpha_g + vs[m] * (wf_g * v);
     }
     // every lane of the wave is done with this block's LDS before the next block's copy
