@@ -296,55 +296,64 @@ attn_partial(AttnArgs a, int64_t ntiles, int64_t nchunks) {
     }
 
     // 4. value sums of the block on the matrix cores (v_mfma_i32_16x16x64_i8, exact integers):
-    //    D[4 h + b][j] of group m = sum_t W_b(t) (c_t + 8), column j = channel 8 j + m.  Lane
-    //    (kg, j) reads word j (channels 8 j .. 8 j + 7) of its 16 tokens of the K step and takes
-    //    nibble m of each as a byte; a ninth product with B = 8 gives the bias 8 sum_t W_b(t).
+    //    D[4 h + b][j] of group m = sum_t S_b(t) 16 c_t, column j = channel 8 j + m.  Lane (kg, j)
+    //    reads word j (channels 8 j .. 8 j + 7) of its 16 tokens of the K step and takes nibble m
+    //    of each as a byte.
 #pragma unroll
     for (int k = 0; k < NGR; ++k) *(u32x4*)&vbuf[w][k * 1024 + 16 * lane] = vcw[k];
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    i32x4 acc[9];
+    i32x4 acc[8];
 #pragma unroll
-    for (int m = 0; m < 9; ++m) acc[m] = i32x4{0, 0, 0, 0};
+    for (int m = 0; m < 8; ++m) acc[m] = i32x4{0, 0, 0, 0};
     const int kg = lane >> 4;
+    // bytes k of four words side by side: t[k] = (a0.k, a1.k, a2.k, a3.k)
+    auto transpose4 = [](uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t (&t)[4]) {
+      const uint32_t l01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u), h01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+      const uint32_t l23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u), h23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+      t[0] = __builtin_amdgcn_perm(l23, l01, 0x05040100u);
+      t[1] = __builtin_amdgcn_perm(l23, l01, 0x07060302u);
+      t[2] = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+      t[3] = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
+    };
 #pragma unroll
     for (int ks = 0; ks < NGR / 4; ++ks) {
+      // the lane's 16 tokens of the K step, channels 8 vb .. 8 vb + 7 as 16 c (a code nibble in the
+      // high half of a byte is 16 times its two's-complement value as an int8): even channels
+      // shifted up, odd channels masked in place
       uint32_t ev[16], od[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = 64 * ks + kg + 4 * (e >> 2) + 16 * (e & 3);
-        const uint32_t x = *(const uint32_t*)(vw + t * 64 + 4 * vb) ^ 0x88888888u;   // nibbles c + 8
-        ev[e] = x & 0x0F0F0F0Fu;                                                        // channels 8 vb + 2 k
-        od[e] = (x >> 4) & 0x0F0F0F0Fu;                                                 // channels 8 vb + 2 k + 1
+        const uint32_t x = *(const uint32_t*)(vw + t * 64 + 4 * vb);
+        ev[e] = (x << 4) & 0xF0F0F0F0u;
+        od[e] = x & 0xF0F0F0F0u;
       }
       const i32x4 av = *(const i32x4*)(ww + ((ks * 16 + (lane & 15)) * 64 + 16 * kg));
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const uint32_t* src = (m & 1) ? od : ev;
-        const int k = m >> 1;
-        const uint32_t lo_sel = 0x0C0C0400u | (uint32_t)k | ((uint32_t)k << 8);        // bytes 0, 1: byte k of src1, src0
-        const uint32_t hi_sel = 0x04000C0Cu | ((uint32_t)k << 16) | ((uint32_t)k << 24); // bytes 2, 3
-        int bq[4];
+      for (int par = 0; par < 2; ++par) {
+        const uint32_t* src = par ? od : ev;
+        uint32_t bt[4][4];                                   // [q][k]: byte k of words 4 q .. 4 q + 3
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          bq[q] = (int)(__builtin_amdgcn_perm(src[4 * q + 1], src[4 * q], lo_sel) |
-                        __builtin_amdgcn_perm(src[4 * q + 3], src[4 * q + 2], hi_sel));
-        acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{bq[0], bq[1], bq[2], bq[3]}, acc[m], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) transpose4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3], bt[q]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int m = 2 * k + par;                         // channel 8 vb + m
+          acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              av, i32x4{(int)bt[0][k], (int)bt[1][k], (int)bt[2][k], (int)bt[3][k]}, acc[m], 0, 0, 0);
+        }
       }
-      acc[8] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{0x08080808, 0x08080808, 0x08080808, 0x08080808},
-                                                     acc[8], 0, 0, 0);
     }
-    // lane (g, j): rows 4 g + b = the planes of head g and its row of ones; with S_b = W_b - 128,
-    // sum_t W c_t = sum_b 256^b ((D_b - bias_b) + 128 (D_1 - bias_1)), D_1 - bias_1 = sum_t c_t;
-    // every difference below 2^24 (exact in fp32)
+    // lane (g, j): rows 4 g + b = the planes of head g and its row of ones; with S_b = W_b - 128
+    // and B = 16 c, D_b = 16 sum_t S_b c_t and D_1 = 16 sum_t c_t, so
+    // 16 sum_t W c_t = sum_b 256^b D_b + 128 (1 + 256 + 65536) D_1; every D below 2^24 (exact in fp32)
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float cs = (float)(acc[m][3] - acc[8][3]);          // sum_t c_t (the row of ones)
-      float v = (float)(acc[m][2] - acc[8][2]);
-      v = __builtin_fmaf(v, 256.f, (float)(acc[m][1] - acc[8][1]));
-      v = __builtin_fmaf(v, 256.f, (float)(acc[m][0] - acc[8][0]));
-      v = __builtin_fmaf(cs, 128.f * 65793.f, v);               // the 128 taken off each byte, 1 + 256 + 65536
-      o[m] = o[m] * alpha_g + vs[m] * (wf_g * v);
+      float v = (float)acc[m][2];
+      v = __builtin_fmaf(v, 256.f, (float)acc[m][1]);
+      v = __builtin_fmaf(v, 256.f, (float)acc[m][0]);
+      v = __builtin_fmaf((float)acc[m][3], 128.f * 65793.f, v);
+      o[m] = o[m] * alpha_g + vs[m] * (wf_g * 0.0625f * v);
     }
     // every lane of the wave is done with this block's LDS before the next block's copy
     __builtin_amdgcn_wave_barrier();
