@@ -66,7 +66,9 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   // [token][R/2 bytes] (wave w fills bytes [(R/8) w, (R/8)(w + 1)) of every row), which are
   // then stored as one contiguous block (head-major codes)
   __shared__ __attribute__((aligned(16))) unsigned char stage[TSTAGE];
-  __shared__ __attribute__((aligned(16))) int8_t sg[R];                 // the head's random signs
+  // the head's random signs as fp16/bf16 sign-bit masks: word p holds channel 2p in bit 15 and
+  // channel 2p + 1 in bit 31
+  __shared__ __attribute__((aligned(16))) uint32_t sgm[R / 2];
   __shared__ __attribute__((aligned(16))) float ninv[16 * ST];         // [j][s]: 1 / norm of token 16 s + j
 
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
@@ -86,6 +88,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
   // 1. this wave's B / 4 rows into LDS (instruction k moves 1 KiB; the chunk that lane p fetches
   //    is XOR-swizzled with its row, so slot cc of row r holds chunk cc ^ (r % CPR) and the
   //    MFMA-layout reads below are free of bank conflicts); wave 0 also fetches the signs
+  uint32_t sg2 = 0u;                                        // wave 0: the signs of channels 2 lane, 2 lane + 1
   {
     const unsigned char* xw = (const unsigned char*)a.x + ((row0 + (B / 4) * w) * a.heads + h) * ROWB;
     const int64_t tok_bytes = a.heads * ROWB;               // x bytes from one token to the next
@@ -102,20 +105,22 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
                                        (__attribute__((address_space(3))) void*)(stage + w * WSTAGE + k * 1024), 16, 0, KVQ_LOAD_NT);
     }
     if constexpr (LG != 0) {
-      if (w == 0 && lane < R / 16)
-        __builtin_amdgcn_global_load_lds((const void*)(a.signs + h * R + 16 * lane),
-                                         (__attribute__((address_space(3))) void*)sg, 16, 0, 0);
+      if (w == 0 && lane < R / 2) sg2 = *(const uint16_t*)(a.signs + h * R + 2 * lane);
     }
   }
   // this wave's base fragments F_I (the random signs and the block signs beta(w, K) are folded
-  // in once the signs have landed), built while the rows are in flight
+  // in once the signs have landed), loaded while the rows are in flight
   u32x4 fb0[NIW];
   if constexpr (LG != 0) {
 #pragma unroll
-    for (int I = 0; I < NIW; ++I) fb0[I] = hadamard_fragment<DT, R, LG>(w, I, lane);
+    for (int I = 0; I < NIW; ++I) fb0[I] = fragment_load<DT, R, LG>(w, I, lane);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's rows (and the signs) have landed
   asm volatile("" ::: "memory");
+  if constexpr (LG != 0) {
+    // sign byte bit 7 -> bit 15 / bit 31
+    if (w == 0 && lane < R / 2) sgm[lane] = __builtin_amdgcn_perm(0u, sg2, 0x010C000Cu) & 0x80008000u;
+  }
   lds_barrier();
 
   // the NK operand chunks of tile row 16 s + j: channels 32 K + 8 g + [0, 8) (the swizzle
@@ -162,14 +167,10 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
       for (int K = 0; K < NK; ++K) {
         const int bt = frag_beta<R, LG>(W, K);
         if (bt == 0) continue;
-        const u32x2 s8 = *(const u32x2*)(sg + 32 * K + 8 * g);
-        uint32_t m[4];
+        const uint32_t bm = bt < 0 ? 0x80008000u : 0u;
+        const u32x4 m = *(const u32x4*)(sgm + 16 * K + 4 * g) ^ u32x4{bm, bm, bm, bm};   // channels 32 K + 8 g + [0, 8)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          m[q] = (__builtin_amdgcn_perm(0u, q < 2 ? s8.x : s8.y, (q & 1) ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u) ^
-                 (bt < 0 ? 0x80008000u : 0u);
-#pragma unroll
-        for (int I = 0; I < NIW; ++I) fk[K][I] = fb0[I] ^ u32x4{m[0], m[1], m[2], m[3]};
+        for (int I = 0; I < NIW; ++I) fk[K][I] = fb0[I] ^ m;
       }
     }
     auto one = [&](int s, f32x4 (&us)[NIW]) {
@@ -230,20 +231,57 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) mxf[4 * I + r] = fmaxf(mxf[4 * I + r], fabsf(u[s][I][r]));
     }
-  uint32_t mx[LCH];
-#pragma unroll
-  for (int q = 0; q < LCH; ++q) mx[q] = row_max16(__builtin_bit_cast(uint32_t, mxf[q]));   // values >= 0
-
-  // 5. scales (lane j < LCH stores channel (R/4) w + LCH g + j) and inverse scales
+  // 5. scales and inverse scales
   float iv[LCH];
-  uint32_t s16 = 0u;
+  if constexpr (LCH == 8) {
+    // the max over the 16 lanes of a row as a reduce-scatter (values >= 0, compared as bits):
+    // each exchange halves the slots a lane keeps (partner j ^ 8, then the mirror within 8
+    // lanes, then j ^ 2) and the last one (j ^ 1) completes the max, so lane j ends with slot
+    // j >> 1.  That lane computes the slot's inverse scale and stores its scale (even j); the
+    // inverse scales are then broadcast back from lanes 2 q.
+    auto dpp = [](uint32_t v, auto ctl) {
+      return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctl)::value, 0xF, 0xF, false);
+    };
+    using ROR8 = std::integral_constant<int, 0x128>;      // row_ror:8 (= lane j ^ 8)
+    using HMIR = std::integral_constant<int, 0x141>;      // row_half_mirror
+    using QX2 = std::integral_constant<int, 0x4E>;        // quad_perm [2, 3, 0, 1]
+    using QX1 = std::integral_constant<int, 0xB1>;        // quad_perm [1, 0, 3, 2]
+    const bool h8 = (j & 8) != 0, h4 = (j & 4) != 0, h2 = (j & 2) != 0;
+    uint32_t m4[4], m2[2];
 #pragma unroll
-  for (int q = 0; q < LCH; ++q) {
-    const float m = __builtin_bit_cast(float, mx[q]);
-    iv[q] = m > 0.f ? a.q * __builtin_amdgcn_rcpf(m) : 0.f;
-    if (q == j) s16 = f32_to_f16(m * a.scale_mul);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = __builtin_bit_cast(uint32_t, mxf[k]), hi = __builtin_bit_cast(uint32_t, mxf[k + 4]);
+      m4[k] = umax(h8 ? hi : lo, dpp(h8 ? lo : hi, ROR8{}));
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) m2[k] = umax(h4 ? m4[k + 2] : m4[k], dpp(h4 ? m4[k] : m4[k + 2], HMIR{}));
+    uint32_t m1 = umax(h2 ? m2[1] : m2[0], dpp(h2 ? m2[0] : m2[1], QX2{}));
+    m1 = umax(m1, dpp(m1, QX1{}));
+    const float m = __builtin_bit_cast(float, m1);
+    const float ivl = m > 0.f ? a.q * __builtin_amdgcn_rcpf(m) : 0.f;
+    if ((j & 1) == 0) a.scales[sblk * R + (R / 4) * w + LCH * g + (j >> 1)] = (uint16_t)f32_to_f16(m * a.scale_mul);
+    auto bcast = [&](auto qc) {   // row_newbcast: lane 2 q of each row to the whole row
+      return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ivl), 0x150 + 2 * decltype(qc)::value, 0xF, 0xF, true));
+    };
+    iv[0] = bcast(std::integral_constant<int, 0>{});
+    iv[1] = bcast(std::integral_constant<int, 1>{});
+    iv[2] = bcast(std::integral_constant<int, 2>{});
+    iv[3] = bcast(std::integral_constant<int, 3>{});
+    iv[4] = bcast(std::integral_constant<int, 4>{});
+    iv[5] = bcast(std::integral_constant<int, 5>{});
+    iv[6] = bcast(std::integral_constant<int, 6>{});
+    iv[7] = bcast(std::integral_constant<int, 7>{});
+  } else {
+    // (lane j < LCH stores channel (R/4) w + LCH g + j)
+    uint32_t s16 = 0u;
+#pragma unroll
+    for (int q = 0; q < LCH; ++q) {
+      const float m = __builtin_bit_cast(float, row_max16(__builtin_bit_cast(uint32_t, mxf[q])));
+      iv[q] = m > 0.f ? a.q * __builtin_amdgcn_rcpf(m) : 0.f;
+      if (q == j) s16 = f32_to_f16(m * a.scale_mul);
+    }
+    if (j < LCH) a.scales[sblk * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
   }
-  if (j < LCH) a.scales[sblk * R + (R / 4) * w + LCH * g + j] = (uint16_t)s16;
 
   // 6. codes and near-tie flags
   uint32_t pk[ST];
@@ -291,7 +329,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
         sa = __builtin_fma(xa, xa, sa);
         sb = __builtin_fma(xb, xb, sb);
         const int hv = LG == 0 ? (p == c ? 1 : 0) : hval<LG>(c, p);
-        const bool neg = (hv < 0) != (LG != 0 && sg[p] < 0);
+        const bool neg = (hv < 0) != (LG != 0 && ((sgm[p >> 1] >> (15 + 16 * (p & 1))) & 1u) != 0u);
         if (hv != 0) {
           ya += neg ? -xa : xa;
           yb += neg ? -xb : xb;
@@ -325,13 +363,9 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
         for (int K = 0; K < NK; ++K) {
           const int bt = frag_beta<R, LG>(w, K);
           if (bt == 0) continue;
-          const u32x2 s8 = *(const u32x2*)(sg + 32 * K + 8 * g);
-          uint32_t m[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            m[q] = (__builtin_amdgcn_perm(0u, q < 2 ? s8.x : s8.y, (q & 1) ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u) ^
-                   (bt < 0 ? 0x80008000u : 0u);
-          us = mfma16<DT>(fbI ^ u32x4{m[0], m[1], m[2], m[3]}, rx(K), us);
+          const uint32_t bm = bt < 0 ? 0x80008000u : 0u;
+          const u32x4 m = *(const u32x4*)(sgm + 16 * K + 4 * g) ^ u32x4{bm, bm, bm, bm};
+          us = mfma16<DT>(fbI ^ m, rx(K), us);
         }
       }
       return us * ninv[j * ST + s];
@@ -343,7 +377,7 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
       // matched to the common path's and kept live through it
       int op = 0;
       asm volatile("" : "+v"(op));
-      const u32x4 fbI = LG != 0 ? hadamard_fragment<DT, R, LG>(w, I, lane + op) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 fbI = LG != 0 ? fragment_load<DT, R, LG>(w, I, lane + op) : u32x4{0u, 0u, 0u, 0u};
       f32x4 us[ST];
 #pragma unroll
       for (int s = 0; s < ST; ++s) us[s] = rotated(s, I, fbI, op);

@@ -116,6 +116,40 @@ template <int DT, int R, int LG> __device__ __forceinline__ u32x4 hadamard_fragm
   }
   return u32x4{q4[0], q4[1], q4[2], q4[3]};
 }
+// The same fragments for every lane, computed at compile time into a read-only table, so a
+// wave loads its fragment instead of building it (R = 128: c & ~UMASK leaves no bit of w;
+// R = 64: bit 4 of c is w & 1).
+template <int LG> __host__ __device__ constexpr int hval_c(int c, int cp) {
+  if ((c >> LG) != (cp >> LG)) return 0;
+  return (__builtin_popcount(c & cp & ((1 << LG) - 1)) & 1) ? -1 : 1;
+}
+template <int DT, int R, int LG> struct alignas(16) FragTable {
+  uint32_t v[R == 128 ? 1 : 2][R / 64][64][4];   // [w class][I][lane][word]
+  constexpr FragTable() : v{} {
+    constexpr int um = R == 128 ? 0x60 : 0x20;
+    const uint32_t one = DT == DT_F16 ? 0x3C00u : 0x3F80u;
+    for (int wc = 0; wc < (R == 128 ? 1 : 2); ++wc)
+      for (int I = 0; I < R / 64; ++I)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int i = lane & 15;
+          const int c = (R == 128 ? 32 * wc + 8 * (i >> 2) + 4 * I + (i & 3) : 16 * wc + 4 * (i >> 2) + (i & 3)) & ~um;
+          for (int q = 0; q < 4; ++q) {
+            uint32_t pair = 0u;
+            for (int hh = 0; hh < 2; ++hh) {
+              const int hv = hval_c<LG>(c, (8 * (lane >> 4) + 2 * q + hh) & ~um);
+              pair |= (hv == 0 ? 0u : (one | (hv < 0 ? 0x8000u : 0u))) << (16 * hh);
+            }
+            v[wc][I][lane][q] = pair;
+          }
+        }
+  }
+};
+template <int DT, int R, int LG> __device__ constexpr FragTable<DT, R, LG> kFragTable{};
+// F_{w,I} of this lane from the table (a 16-byte global load)
+template <int DT, int R, int LG> __device__ __forceinline__ u32x4 fragment_load(int w, int I, int lane) {
+  return *(const u32x4*)kFragTable<DT, R, LG>.v[R == 128 ? 0 : (w & 1)][I][lane];
+}
+
 // beta(w, K) at run time for R = 128 (w wave-uniform): the same factor as frag_beta
 template <int LG> __device__ __forceinline__ int blk_beta(int w, int K) {
   return hval<LG>((32 * w) & 0x60, (32 * K) & 0x60);
