@@ -43,9 +43,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
+// two fp32 -> one word of two fp16 / bf16 (a low), round to nearest even: one packed
+// conversion instruction on gfx950
 template <int DT> __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (DT == DT_F16) return f32_to_f16(a) | (f32_to_f16(b) << 16);
-  else return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+  if constexpr (DT == DT_F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
+  }
 }
 
 // ------------------------------------------------------------------ launch geometry

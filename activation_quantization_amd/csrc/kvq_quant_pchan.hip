@@ -47,9 +47,24 @@ namespace {
 
 using namespace rot;
 
+// n / d for every 32-bit n as (umulhi(n, m) + n) >> l, with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1 (Granlund and Montgomery's round-up method, the sum taken in
+// 64 bits); the tile decomposition divides wave-uniform values, so this stays in scalar registers
+struct FastDiv {
+  uint32_t m, l;
+};
+FastDiv fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  return FastDiv{(uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1), l};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.l);
+}
+
 template <int DT, int R, int LG, int B>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B > 128 ? 3 : 4)))
-quant_pchan_tile(QuantArgs a, int64_t ntiles) {
+quant_pchan_tile(QuantArgs a, int64_t ntiles, FastDiv nb_div, FastDiv heads_div) {
   constexpr int NK = R / 32;            // K steps of the contraction
   constexpr int NIW = R / 64;           // output I-blocks per wave
   constexpr int LCH = 4 * NIW;          // channels per lane and token
@@ -73,13 +88,17 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
 
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
-  // tile ids fit 32 bits (a tile holds >= 8 KiB of input); 32-bit divisions are much cheaper
+  // tile ids fit 32 bits (the launcher keeps them below 2^31)
   // Tiles are numbered along the head-major output streams (block fastest), so the tiles in
   // flight on one XCD write neighbouring blocks of one stream.
-  const uint32_t tile = (uint32_t)xcd_tile(blockIdx.x, ntiles);
+  uint32_t tile;
+  {
+    const uint32_t x = blockIdx.x & 7u, k = blockIdx.x >> 3, per = (uint32_t)ntiles >> 3, rem = (uint32_t)ntiles & 7u;
+    tile = x * per + (x < rem ? x : rem) + k;                 // each XCD walks a contiguous range
+  }
   const uint32_t nb = (uint32_t)(a.tokens / B);
-  const uint32_t hs32 = tile / nb, blk = tile - hs32 * nb;              // hs = seq * heads + h
-  const uint32_t seq = hs32 / (uint32_t)a.heads, h = hs32 - seq * (uint32_t)a.heads;
+  const uint32_t hs32 = fdiv(tile, nb_div), blk = tile - hs32 * nb;     // hs = seq * heads + h
+  const uint32_t seq = fdiv(hs32, heads_div), h = hs32 - seq * (uint32_t)a.heads;
   const int64_t row0 = (int64_t)seq * a.in_seq_tokens + (int64_t)blk * B;   // x row of the tile's first token
   const int64_t hs = hs32;                                            // (sequence, head) output stream
   const int64_t tok0 = hs * a.out_tokens + a.out_tok0 + (int64_t)blk * B;   // head-major index of that token
@@ -490,7 +509,8 @@ quant_pchan_tile(QuantArgs a, int64_t ntiles) {
 template <int DT, int R, int LG>
 void launch_r(const QuantArgs& a, hipStream_t st) {
   const int64_t ntiles = a.seqs * (a.tokens / a.block) * a.heads;
-  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles); };
+  const FastDiv nbd = fast_div((uint32_t)(a.tokens / a.block)), hd = fast_div((uint32_t)a.heads);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, ntiles, nbd, hd); };
   if (a.block == 64) go(quant_pchan_tile<DT, R, LG, 64>);
   else if (a.block == 128) go(quant_pchan_tile<DT, R, LG, 128>);
   else if constexpr (R == 64) go(quant_pchan_tile<DT, R, LG, 256>);
