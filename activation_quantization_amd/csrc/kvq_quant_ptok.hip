@@ -123,7 +123,7 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
   u32x4 fb[NIW];
   if constexpr (LG != 0) {
 #pragma unroll
-    for (int I = 0; I < NIW; ++I) fb[I] = hadamard_fragment<DT, R, LG>(w, I, lane);
+    for (int I = 0; I < NIW; ++I) fb[I] = fragment_load<DT, R, LG>(w, I, lane);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's rows and sign bytes have landed
   asm volatile("" ::: "memory");
@@ -357,9 +357,11 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
     asm volatile("s_mov_b32 %0, %1" : "=s"(wr) : "s"(w));
     u32x4 fkr[NK][NIW];
     if constexpr (LG != 0) {
+      int op = 0;                                           // opaque zero: a fresh load, not the common path's
+      asm volatile("" : "+v"(op));
 #pragma unroll
       for (int I = 0; I < NIW; ++I) {
-        const u32x4 f = hadamard_fragment<DT, R, LG>(wr, I, lane);
+        const u32x4 f = fragment_load<DT, R, LG>(wr, I, lane + op);
 #pragma unroll
         for (int K = 0; K < NK; ++K) fkr[K][I] = f ^ (blk_beta<LG>(wr, K) < 0 ? 0x80008000u : 0u);
       }
