@@ -86,57 +86,33 @@ __device__ __forceinline__ double wave_sum64(double v) {
 }
 
 // entry (c, c') of blockdiag(H_n), n = 2^LG: zero unless c and c' share their n-block
-template <int LG> __device__ __forceinline__ constexpr int hval(int c, int cp) {
+template <int LG> __host__ __device__ constexpr int hval(int c, int cp) {
   if ((c >> LG) != (cp >> LG)) return 0;
   return (__builtin_popcount(c & cp & ((1 << LG) - 1)) & 1) ? -1 : 1;
 }
 
-template <int R> __device__ __forceinline__ constexpr int out_channel(int w, int I, int i) {
+template <int R> __host__ __device__ constexpr int out_channel(int w, int I, int i) {
   return R == 128 ? 32 * w + 8 * (i >> 2) + 4 * I + (i & 3) : 16 * w + 4 * (i >> 2) + (i & 3);
 }
 // bits of the channel numbers that are set by the wave index (c) and by the K step (c')
 template <int R> constexpr int UMASK = R == 128 ? 0x60 : 0x20;
 
-// F_{w,I}: this lane's 8 A-operand entries (row i = lane & 15, inputs 8 (lane >> 4) + e of K
-// step 0) over the bits of c and c' that are not both uniform
-template <int DT, int R, int LG> __device__ __forceinline__ u32x4 hadamard_fragment(int w, int I, int lane) {
-  const int c = out_channel<R>(w, I, lane & 15) & ~UMASK<R>;
-  const uint32_t one = DT == DT_F16 ? 0x3C00u : 0x3F80u;
-  uint32_t q4[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t pair = 0u;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int cp = (8 * (lane >> 4) + 2 * q + hh) & ~UMASK<R>;
-      const int v = hval<LG>(c, cp);
-      pair |= (v == 0 ? 0u : (one | (v < 0 ? 0x8000u : 0u))) << (16 * hh);
-    }
-    q4[q] = pair;
-  }
-  return u32x4{q4[0], q4[1], q4[2], q4[3]};
-}
-// The same fragments for every lane, computed at compile time into a read-only table, so a
-// wave loads its fragment instead of building it (R = 128: c & ~UMASK leaves no bit of w;
-// R = 64: bit 4 of c is w & 1).
-template <int LG> __host__ __device__ constexpr int hval_c(int c, int cp) {
-  if ((c >> LG) != (cp >> LG)) return 0;
-  return (__builtin_popcount(c & cp & ((1 << LG) - 1)) & 1) ? -1 : 1;
-}
+// F_{w,I}: a lane's 8 A-operand entries (row i = lane & 15, inputs 8 (lane >> 4) + e of K step 0)
+// over the bits of c and c' that are not both uniform, for every lane, computed at compile time
+// into a read-only table, so a wave loads its fragment instead of building it (R = 128:
+// c & ~UMASK leaves no bit of w; R = 64: bit 4 of c is w & 1).
 template <int DT, int R, int LG> struct alignas(16) FragTable {
   uint32_t v[R == 128 ? 1 : 2][R / 64][64][4];   // [w class][I][lane][word]
   constexpr FragTable() : v{} {
-    constexpr int um = R == 128 ? 0x60 : 0x20;
     const uint32_t one = DT == DT_F16 ? 0x3C00u : 0x3F80u;
     for (int wc = 0; wc < (R == 128 ? 1 : 2); ++wc)
       for (int I = 0; I < R / 64; ++I)
         for (int lane = 0; lane < 64; ++lane) {
-          const int i = lane & 15;
-          const int c = (R == 128 ? 32 * wc + 8 * (i >> 2) + 4 * I + (i & 3) : 16 * wc + 4 * (i >> 2) + (i & 3)) & ~um;
+          const int c = out_channel<R>(wc, I, lane & 15) & ~UMASK<R>;
           for (int q = 0; q < 4; ++q) {
             uint32_t pair = 0u;
             for (int hh = 0; hh < 2; ++hh) {
-              const int hv = hval_c<LG>(c, (8 * (lane >> 4) + 2 * q + hh) & ~um);
+              const int hv = hval<LG>(c, (8 * (lane >> 4) + 2 * q + hh) & ~UMASK<R>);
               pair |= (hv == 0 ? 0u : (one | (hv < 0 ? 0x8000u : 0u))) << (16 * hh);
             }
             v[wc][I][lane][q] = pair;
