@@ -65,9 +65,12 @@ __device__ __forceinline__ float group_sum(float v, int lg) {
   return v;
 }
 
-template <int DT, int LG, bool RRS>
+// LGLT: log2 of the 128-channel rows per vector when fixed at compile time (0: head_dim 128, 5: head_dim
+// 4096), so the row -> vector arithmetic and the reductions' shapes fold; -1 takes lgL_arg at run time
+template <int DT, int LG, bool RRS, int LGLT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
-quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
+quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL_arg) {
+  const int lgL = LGLT >= 0 ? LGLT : lgL_arg;
   constexpr int R = 128, NK = 4, NIW = 2, LCH = 8, ST = PT_ROWS / 16, ROWB = 2 * R, CPR = ROWB / 16, RB = R / 2;
   constexpr int WSTAGE = PT_ROWS / 4 * ROWB;                 // bytes of the rows each wave loads
   constexpr int NLD = WSTAGE / 1024;                          // load instructions per wave
@@ -465,7 +468,10 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL) {
 template <int DT, int LG, bool RRS>
 void launch_t(const QuantArgs& a, hipStream_t st, int64_t nrows, int lgL) {
   const int64_t ntiles = (nrows + PT_ROWS - 1) / PT_ROWS;
-  hipLaunchKernelGGL((quant_ptok_tile<DT, LG, RRS>), dim3((unsigned)ntiles), dim3(256), 0, st, a, nrows, ntiles, lgL);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(256), 0, st, a, nrows, ntiles, lgL); };
+  if (lgL == 5) go(quant_ptok_tile<DT, LG, RRS, 5>);
+  else if (lgL == 0) go(quant_ptok_tile<DT, LG, RRS, 0>);
+  else go(quant_ptok_tile<DT, LG, RRS, -1>);
 }
 
 template <int DT, bool RRS>
