@@ -31,6 +31,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_launch.h"
 #include "kvq_rotate.h"
 
 namespace kvq {
@@ -465,6 +466,149 @@ quant_ptok_tile(QuantArgs a, int64_t nrows, int64_t ntiles, int lgL_arg) {
   }
 }
 
+// this wave's rows of tile t into the stage st (the per-token kernel's swizzled layout), the sign
+// bytes of their chunks into sg
+template <int LG>
+__device__ __forceinline__ void colmax_issue(const QuantArgs& a, unsigned char* st, int64_t t, int64_t nrows, int L, int w,
+                                             int lane, u32x2 (&sg)[PT_ROWS * 256 / 4 / 1024]) {
+  constexpr int R = 128, ROWB = 2 * R, CPR = ROWB / 16, WSTAGE = PT_ROWS / 4 * ROWB, NLD = WSTAGE / 1024;
+  const int j = lane & 15, g = lane >> 4;
+  const int64_t row0 = t * PT_ROWS;
+  const int nvalid = (int)(nrows - row0 < PT_ROWS ? nrows - row0 : PT_ROWS);
+  const unsigned char* xw = (const unsigned char*)a.x + (row0 + (PT_ROWS / 4) * w) * ROWB;
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) {
+    const int r = (PT_ROWS / 4) * w + 4 * k + g;
+    const int gc = j ^ (r % CPR);
+    if (r < nvalid) {
+      __builtin_amdgcn_global_load_lds((const void*)(xw + (4 * k + g) * ROWB + 16 * gc),
+                                       (__attribute__((address_space(3))) void*)(st + w * WSTAGE + k * 1024), 16, 0,
+                                       KVQ_LOAD_NT);
+      if constexpr (LG != 0) sg[k] = *(const u32x2*)(a.signs + (r & (L - 1)) * R + 8 * gc);
+    }
+  }
+}
+
+// RRS smoothing scales on the matrix cores: s[g] = (1/sqrt n) max |H sigma x| over every row of
+// segment g (rows are the 128-channel segments of the [n, k] input, row r in segment r mod L).
+// Resident workgroups of four waves walk the 64-row tiles b, b + G, ...; each tile is copied into
+// one of two LDS stages while the previous one is rotated (the per-token kernel's layout: signs
+// flipped in place by the wave that loaded the rows, wave w rotating output channels
+// [32 w, 32 w + 32) of every row), and each lane keeps the max of its 8 channels per tile row
+// position.  At the end the positions are merged over the lane groups, the waves and the rows of
+// each segment (tiles start at multiples of 64 and L divides 64, so position r is segment r mod L),
+// and each segment's max enters s with an integer max on its float bits (non-negative values).
+template <int DT, int LG>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+rrs_colmax_tile(QuantArgs a, uint32_t* smax, int64_t nrows, int64_t ntiles, int lgL) {
+  constexpr int R = 128, NK = 4, NIW = 2, ST = PT_ROWS / 16, ROWB = 2 * R, CPR = ROWB / 16;
+  constexpr int WSTAGE = PT_ROWS / 4 * ROWB;                 // bytes of the rows each wave loads
+  constexpr int NLD = WSTAGE / 1024;                          // load instructions per wave
+  __shared__ __attribute__((aligned(16))) unsigned char stage[2][PT_ROWS * ROWB];
+  __shared__ __attribute__((aligned(16))) uint32_t rmax[PT_ROWS][4];   // per (row position, wave) max bits
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L = 1 << lgL;
+  const int64_t G = gridDim.x;
+
+  u32x4 fk[NK][NIW];
+  if constexpr (LG != 0) {
+#pragma unroll
+    for (int I = 0; I < NIW; ++I) {
+      const u32x4 f = fragment_load<DT, R, LG>(w, I, lane);
+#pragma unroll
+      for (int K = 0; K < NK; ++K) fk[K][I] = f ^ (blk_beta<LG>(w, K) < 0 ? 0x80008000u : 0u);
+    }
+  }
+  uint32_t acc[ST];
+#pragma unroll
+  for (int s = 0; s < ST; ++s) acc[s] = 0u;
+
+  u32x2 sgn[NLD], sgn_next[NLD];
+  int b = 0;
+  int64_t t = blockIdx.x;
+  if (t < ntiles) colmax_issue<LG>(a, stage[0], t, nrows, L, w, lane, sgn);
+  for (; t < ntiles; t += G) {
+    const int nvalid = (int)(nrows - t * PT_ROWS < PT_ROWS ? nrows - t * PT_ROWS : PT_ROWS);
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this tile's rows and sign bytes (no stores in flight)
+    asm volatile("" ::: "memory");
+    // sign bits of this wave's own rows, in place; rows past the end are zero
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int r = (PT_ROWS / 4) * w + 4 * k + g;
+      u32x4* p = (u32x4*)(stage[b] + w * WSTAGE + k * 1024 + 16 * lane);
+      if (r < nvalid) {
+        if constexpr (LG != 0) {
+          u32x4 d = *p;
+          d.x ^= __builtin_amdgcn_perm(0u, sgn[k].x, 0x010C000Cu) & 0x80008000u;
+          d.y ^= __builtin_amdgcn_perm(0u, sgn[k].x, 0x030C020Cu) & 0x80008000u;
+          d.z ^= __builtin_amdgcn_perm(0u, sgn[k].y, 0x010C000Cu) & 0x80008000u;
+          d.w ^= __builtin_amdgcn_perm(0u, sgn[k].y, 0x030C020Cu) & 0x80008000u;
+          *p = d;
+        }
+      } else {
+        *p = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    lds_barrier();   // every wave's rows are in stage b, and every wave is done with stage b ^ 1
+    if (t + G < ntiles) colmax_issue<LG>(a, stage[b ^ 1], t + G, nrows, L, w, lane, sgn_next);
+    const unsigned char* sb = stage[b];
+    auto read_x = [&](int s, int K) {
+      return *(const u32x4*)(sb + 16 * s * ROWB + (j * ROWB + 16 * ((4 * K + g) ^ (j % CPR))));
+    };
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      f32x4 u[NIW];
+      if constexpr (LG == 0) {
+        const u32x4 xr = read_x(s, w);                       // the lane's own 8 channels
+        u[0] = f32x4{lo_f32<DT>(xr.x), hi_f32<DT>(xr.x), lo_f32<DT>(xr.y), hi_f32<DT>(xr.y)};
+        u[1] = f32x4{lo_f32<DT>(xr.z), hi_f32<DT>(xr.z), lo_f32<DT>(xr.w), hi_f32<DT>(xr.w)};
+      } else {
+        u32x4 x[NK];
+#pragma unroll
+        for (int K = 0; K < NK; ++K) x[K] = read_x(s, K);
+        u[0] = u[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = 0; K < NK; ++K) {
+          if (blk_beta<LG>(w, K) == 0) continue;             // wave-uniform
+#pragma unroll
+          for (int I = 0; I < NIW; ++I) u[I] = mfma16<DT>(fk[K][I], x[K], u[I]);
+        }
+      }
+      const float m0 = __builtin_fmaxf(fmaxf(fabsf(u[0].x), fabsf(u[0].y)), fabsf(u[0].z));
+      const float m1 = __builtin_fmaxf(fmaxf(fabsf(u[0].w), fabsf(u[1].x)), fabsf(u[1].y));
+      const float m2 = __builtin_fmaxf(fmaxf(fabsf(u[1].z), fabsf(u[1].w)), m0);
+      acc[s] = umax(acc[s], __builtin_bit_cast(uint32_t, fmaxf(m1, m2)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) sgn[k] = sgn_next[k];
+    b ^= 1;
+  }
+  // position 16 s + j: over the lane groups, then the waves, then the positions of each segment
+#pragma unroll
+  for (int s = 0; s < ST; ++s) {
+    uint32_t m = acc[s];
+    m = umax(m, (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, (int)m));
+    m = umax(m, (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)m));
+    if (lane < 16) rmax[16 * s + j][w] = m;
+  }
+  lds_barrier();
+  if (w == 0) {
+    const u32x4 p = *(const u32x4*)rmax[lane];
+    float m = __builtin_bit_cast(float, umax(umax(p.x, p.y), umax(p.z, p.w)));
+    for (int o = L; o < 64; o <<= 1) m = fmaxf(m, shfl_xor_f(m, o));
+    if (lane < L) atomicMax(smax + lane, __builtin_bit_cast(uint32_t, m * a.inv_sqrt_n));
+  }
+}
+
+template <int DT, int LG>
+void launch_colmax(const QuantArgs& a, uint32_t* smax, hipStream_t st, int64_t nrows, int lgL) {
+  const int64_t ntiles = (nrows + PT_ROWS - 1) / PT_ROWS;
+  const int64_t grid = persistent_grid(rrs_colmax_tile<DT, LG>, 256, ntiles);
+  hipLaunchKernelGGL((rrs_colmax_tile<DT, LG>), dim3((unsigned)grid), dim3(256), 0, st, a, smax, nrows, ntiles, lgL);
+}
+
 template <int DT, int LG, bool RRS>
 void launch_t(const QuantArgs& a, hipStream_t st, int64_t nrows, int lgL) {
   const int64_t ntiles = (nrows + PT_ROWS - 1) / PT_ROWS;
@@ -486,6 +630,29 @@ void launch_lg(const QuantArgs& a, hipStream_t st, int64_t nrows, int lgL) {
 }
 
 }  // namespace
+
+// the RRS smoothing scales (s zero-filled by the caller): rows of 128 channels, k a power of two in
+// [128, 8192]
+hipError_t launch_rrs_colmax_mfma(const QuantArgs& a, uint32_t* smax, hipStream_t st) {
+  int lgL = 0;
+  while ((int64_t(128) << lgL) < a.dim) ++lgL;
+  if ((1 << lgL) > PT_ROWS) return hipErrorInvalidValue;   // segments must divide the tile
+  const int64_t nrows = a.seqs * a.tokens * a.heads * (a.dim / 128);
+  if (nrows == 0) return hipGetLastError();
+  auto by_lg = [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    switch (a.lg_had) {
+      case 0: launch_colmax<DT, 0>(a, smax, st, nrows, lgL); break;
+      case 4: launch_colmax<DT, 4>(a, smax, st, nrows, lgL); break;
+      case 5: launch_colmax<DT, 5>(a, smax, st, nrows, lgL); break;
+      case 6: launch_colmax<DT, 6>(a, smax, st, nrows, lgL); break;
+      default: launch_colmax<DT, 7>(a, smax, st, nrows, lgL); break;
+    }
+  };
+  if (a.dtype == DT_F16) by_lg(std::integral_constant<int, DT_F16>{});
+  else by_lg(std::integral_constant<int, DT_BF16>{});
+  return hipGetLastError();
+}
 
 // head_dim a power of two in [128, 8192]
 hipError_t launch_quantize_ptok_mfma(const QuantArgs& a, hipStream_t st) {

@@ -523,6 +523,7 @@ hipError_t launch_rrs_colmax(const QuantArgs& a, float* s, hipStream_t st) {
   uint32_t* smax = reinterpret_cast<uint32_t*>(s);
   hipLaunchKernelGGL(rrs_fill_zero, dim3(1), dim3(64), 0, st, smax, (int)(a.dim / 128));
   if (nseg > 0) {
+    if (!rotation_butterfly()) return launch_rrs_colmax_mfma(a, smax, st);   // the matrix-core kernel
     if (a.dtype == DT_F16) colmax_dt<DT_F16>(a, smax, st, nseg, lgL); else colmax_dt<DT_BF16>(a, smax, st, nseg, lgL);
   }
   return hipGetLastError();
