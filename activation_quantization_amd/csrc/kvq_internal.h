@@ -126,9 +126,6 @@ bool rotation_butterfly();
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_quantize_pchan(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_ptok(const QuantArgs& a, hipStream_t stream);
-// the RRS smoothing scales on the matrix cores (smax zero-filled beforehand); launch_rrs_colmax
-// dispatches to it unless the butterfly kernels are selected
-hipError_t launch_rrs_colmax_mfma(const QuantArgs& a, uint32_t* smax, hipStream_t stream);
 // the matrix-core per-token kernel (head_dim a power of two in [128, 8192]); launch_quantize_ptok
 // dispatches to it
 hipError_t launch_quantize_ptok_mfma(const QuantArgs& a, hipStream_t stream);

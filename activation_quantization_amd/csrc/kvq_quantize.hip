@@ -516,6 +516,9 @@ static void colmax_dt(const QuantArgs& a, uint32_t* smax, hipStream_t st, int64_
   }
 }
 
+// the RRS smoothing scales on the matrix cores (kvq_quant_ptok.hip; smax zero-filled beforehand)
+hipError_t launch_rrs_colmax_mfma(const QuantArgs& a, uint32_t* smax, hipStream_t st);
+
 hipError_t launch_rrs_colmax(const QuantArgs& a, float* s, hipStream_t st) {
   int lgL = 0;
   while ((128 << lgL) < a.dim) ++lgL;
