@@ -95,6 +95,20 @@ def test_rrs_parity(n, m, k, had, dtype, bits):
     _check_y(y.numpy(), y_chain, "end to end", rel=1e-3)
 
 
+@pytest.mark.parametrize("n,k,had,dtype", [
+    (2048 * 64 + 37, 128, 128, torch.bfloat16),   # 2049 tiles of 64 rows: several per resident workgroup, the last ragged
+    (1030 * 32 + 5, 256, 64, torch.float16),      # two segments per token, an odd tail of rows
+])
+def test_rrs_smooth_scales_many_tiles(n, k, had, dtype):
+    # the smoothing scales alone, over more 64-row tiles than the GPU holds workgroups at once
+    x = _acts(n + 7, n, k, dtype)
+    sg = _signs(k + 1, k)
+    s = kvq.rrs_smooth_scales(x.to(DEV), sg.to(DEV), had)
+    torch.cuda.synchronize()
+    s_ref = oracle.rrs_smooth_scales(x.double().numpy(), sg.numpy(), had)
+    np.testing.assert_allclose(s.cpu().numpy(), s_ref, rtol=REL_S)
+
+
 def test_rrs_zero_rows_and_groups():
     # a zero activation row (a_t = 0, codes 0, y row 0) and a channel group that is zero in every
     # token (s_g = 0: its columns quantize to 0)
