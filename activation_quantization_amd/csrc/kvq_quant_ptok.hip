@@ -497,7 +497,8 @@ __device__ __forceinline__ void colmax_issue(const QuantArgs& a, unsigned char* 
 // [32 w, 32 w + 32) of every row), and each lane keeps the max of its 8 channels per tile row
 // position.  At the end the positions are merged over the lane groups, the waves and the rows of
 // each segment (tiles start at multiples of 64 and L divides 64, so position r is segment r mod L),
-// and each segment's max enters s with an integer max on its float bits (non-negative values).
+// and each segment's max enters s with an integer max on its float bits (non-negative values), skipped
+// when the value already there is not smaller.
 template <int DT, int LG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 rrs_colmax_tile(QuantArgs a, uint32_t* smax, int64_t nrows, int64_t ntiles, int lgL) {
@@ -598,7 +599,11 @@ rrs_colmax_tile(QuantArgs a, uint32_t* smax, int64_t nrows, int64_t ntiles, int 
     const u32x4 p = *(const u32x4*)rmax[lane];
     float m = __builtin_bit_cast(float, umax(umax(p.x, p.y), umax(p.z, p.w)));
     for (int o = L; o < 64; o <<= 1) m = fmaxf(m, shfl_xor_f(m, o));
-    if (lane < L) atomicMax(smax + lane, __builtin_bit_cast(uint32_t, m * a.inv_sqrt_n));
+    // the maxima only grow, so a value not above the one already there (read without ordering: a
+    // stale read is at most the current value, and then the atomic is merely not skipped) needs no
+    // atomic; the workgroups' atomics on this one line would otherwise serialize
+    const uint32_t mb = __builtin_bit_cast(uint32_t, m * a.inv_sqrt_n);
+    if (lane < L && mb > ld_global(smax + lane)) atomicMax(smax + lane, mb);
   }
 }
 
